@@ -1,0 +1,426 @@
+"""CPU oracle of one Mixture-of-Experts feed-forward layer, in float64.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
+GPU library is checked against.  Only the test suite, the package smoke check
+and the benchmark's CPU-baseline leg may import or run it; the library itself
+never does, and this module imports nothing from the library.
+
+Sources (cited by page title and section; the pages are web pages about the
+MoE layers of GPT-OSS and GLM4-MoE-Lite):
+
+  [GPTOSS]  "Implementation:Ollama Ollama Imagegen GPT OSS" -- Description and
+            Signature (clipped SwiGLU, alpha = 1.702, Config fields).
+  [GGUF]    "GPT-OSS 20B GGUF with MoE CPU Offloading Support" -- Key Features
+            and Model Specifications (32 experts / 4 active, MXFP4 experts).
+  [MAXTEXT] MaxText "weight_mapping/gpt_oss" module -- the "MoE Router" and
+            "MOE EXPERTS" blocks of to_hf_mapping (router kernel + bias,
+            gate_proj / up_proj kernels + biases, mlp2 weight + bias).
+  [GLM]     "x/models/glm4_moe_lite/glm4_moe_lite.go" -- Config, DenseMLP,
+            MoEGate.Forward, SwitchMLP.Forward, SharedExperts.Forward,
+            MoE.Forward.
+  [OCP-MX]  OCP Microscaling Formats (MX) v1.0 specification (not on the
+            pages; it defines the e2m1 element and e8m0 scale the MXFP4 name
+            on [GGUF] refers to).
+
+Readings taken where the pages are silent or disagree (each is listed with its
+reason in the design notes of this repository):
+  * GPT-OSS routing: top-k of the raw router logits, weights = softmax over the
+    k selected logits ([MAXTEXT] shows only an affine router; [GPTOSS] does
+    not describe it).
+  * Ordering and ties: experts ordered by (score descending, index ascending);
+    an exact tie goes to the lower index.
+  * Clipped SwiGLU: g' = clip(g, 0, limit), u' = clip(u, -limit, limit),
+    h = g' * sigmoid(alpha * g') * u'  ([GPTOSS] Description, taken literally).
+  * Biases are added by each Linear before the activation; the down bias is
+    inside each expert's output, before the routing weight.
+  * GLM grouped routing: scores s = softmax(logits) over all experts (or
+    sigmoid, as [GLM] MoEGate.Forward computes); the group score is the
+    largest selection score in each contiguous group of E/n_group experts;
+    topk_group groups are kept (ties to the lower group index); top-k is taken
+    among the kept experts on the selection score (score + correction bias);
+    weights are the unbiased scores of the chosen experts, renormalised when
+    k > 1 and norm_topk_prob, then multiplied by routed_scaling_factor.
+  * The shared expert is a SiLU-gated MLP without bias, weight 1, added after
+    the routed sum ([GLM] SharedExperts.Forward, MoE.Forward).
+  * Permutation: pairs p = t*k + j sorted by (expert, p) (a stable sort).
+"""
+from __future__ import annotations
+
+import itertools
+from typing import Optional
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Decoding of stored inputs into float64.
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64.  bf16 is the top half of an
+    IEEE binary32, so widening is exact."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def to_f64(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    """Stored array (bf16 bits or float32) -> float64; None stays None."""
+    if a is None:
+        return None
+    if dtype == "bf16":
+        return bf16_to_f64(a)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# [OCP-MX] FP4 E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit.
+# Magnitudes of codes 0..7; codes 8..15 are the same with the sign bit set.
+E2M1_MAGNITUDE = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    """Value of a 4-bit e2m1 code ([OCP-MX] FP4 element)."""
+    code = np.asarray(code, dtype=np.uint8)
+    mag = E2M1_MAGNITUDE[code & 7]
+    return np.where(code & 8, -mag, mag)
+
+
+def e8m0_value(scale: np.ndarray) -> np.ndarray:
+    """Value of an e8m0 block scale: 2**(byte - 127); byte 255 is NaN ([OCP-MX])."""
+    s = np.asarray(scale, dtype=np.int64)
+    v = np.ldexp(1.0, (s - 127).astype(np.int32))
+    return np.where(s == 255, np.nan, v)
+
+
+def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decode one MXFP4 matrix: codes uint8 [rows, cols/2] (element 2i in the
+    low nibble, 2i+1 in the high nibble), scales uint8 [rows, cols/32], one per
+    32 consecutive elements of a row.  Returns float64 [rows, cols]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    cols = 2 * half
+    elem = np.empty((rows, cols), dtype=np.uint8)
+    elem[:, 0::2] = codes & 0x0F
+    elem[:, 1::2] = codes >> 4
+    blk_scale = np.repeat(e8m0_value(scales), 32, axis=1)
+    assert blk_scale.shape == (rows, cols)
+    return e2m1_value(elem) * blk_scale
+
+
+# ----------------------------------------------------------------------------
+# Router.
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, b_router: Optional[np.ndarray]) -> np.ndarray:
+    """l[t, e] = sum_i x[t, i] * Wr[e, i] + br[e]  -- the router is an affine map
+    from the hidden size to one logit per expert ([MAXTEXT] "MoE Router": a
+    kernel and a bias; [GLM] MoEGate.Forward: Gate Linear)."""
+    l = x @ w_router.T
+    if b_router is not None:
+        l = l + b_router[None, :]
+    return l
+
+
+def order_desc(v: np.ndarray) -> np.ndarray:
+    """Indices of each row of v ordered by (value descending, index ascending)."""
+    return np.argsort(-v, axis=-1, kind="stable")
+
+
+def gptoss_route(logits: np.ndarray, k: int):
+    """Top-k experts of each token and their weights.
+
+    Selection: the k largest logits (ties to the lower expert index).
+    Weights: softmax over the k selected logits.
+    Returns idx int64 [T, k] in selection order, w float64 [T, k]."""
+    idx = order_desc(logits)[:, :k]
+    sel = np.take_along_axis(logits, idx, axis=1)
+    m = sel[:, :1]
+    ex = np.exp(sel - m)
+    w = ex / ex.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic function 1 / (1 + exp(-z)), evaluated without overflow."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis (max-subtracted)."""
+    m = z.max(axis=-1, keepdims=True)
+    ex = np.exp(z - m)
+    return ex / ex.sum(axis=-1, keepdims=True)
+
+
+def grouped_route(logits: np.ndarray, k: int, n_group: int, topk_group: int,
+                  norm_topk_prob: bool, routed_scaling_factor: float,
+                  score: str = "softmax", e_score_bias: Optional[np.ndarray] = None):
+    """Group-limited routing of GLM4-MoE style ([GLM] Config fields n_group /
+    topk_group / norm_topk_prob / routed_scaling_factor; [GLM] MoEGate.Forward).
+
+    1. s = softmax(l) over all experts, or sigmoid(l) ([GLM] MoEGate.Forward).
+    2. s' = s + e_score_bias when a correction bias is given (selection only).
+    3. Experts form n_group contiguous groups of E/n_group; group score =
+       max of s' over the group; keep the topk_group best groups.
+    4. idx = the k best experts by s' among the kept groups.
+    5. w = s[idx]; if k > 1 and norm_topk_prob: w /= sum(w); w *= rsf.
+    Returns idx int64 [T, k], w float64 [T, k]."""
+    T, E = logits.shape
+    assert E % n_group == 0 and 1 <= topk_group <= n_group
+    s = softmax(logits) if score == "softmax" else sigmoid(logits)
+    s_sel = s + e_score_bias[None, :] if e_score_bias is not None else s
+    gsize = E // n_group
+    group_score = s_sel.reshape(T, n_group, gsize).max(axis=2)
+    kept_groups = order_desc(group_score)[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, kept_groups, True, axis=1)
+    allowed_e = np.repeat(allowed, gsize, axis=1)
+    cand = np.where(allowed_e, s_sel, -np.inf)
+    idx = order_desc(cand)[:, :k]
+    assert np.all(np.take_along_axis(allowed_e, idx, axis=1)), "k exceeds the kept experts"
+    w = np.take_along_axis(s, idx, axis=1)
+    if k > 1 and norm_topk_prob:
+        w = w / w.sum(axis=1, keepdims=True)
+    w = w * routed_scaling_factor
+    return idx, w
+
+
+# ----------------------------------------------------------------------------
+# Expert MLP.
+
+
+def clipped_swiglu(g: np.ndarray, u: np.ndarray, alpha: float, limit: float) -> np.ndarray:
+    """GPT-OSS activation ([GPTOSS] Description): gate clipped to [0, limit],
+    up clipped to [-limit, limit], sigmoid scaled by alpha:
+        h = g' * sigmoid(alpha * g') * u'."""
+    gc = np.minimum(np.maximum(g, 0.0), limit)
+    uc = np.minimum(np.maximum(u, -limit), limit)
+    return gc * sigmoid(alpha * gc) * uc
+
+
+def silu_glu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """SiLU-gated product ([GLM] DenseMLP / SwitchMLP / SharedExperts):
+        h = silu(g) * u = g * sigmoid(g) * u."""
+    return g * sigmoid(g) * u
+
+
+def activation(g, u, act: str, alpha: float, limit: float):
+    if act == "clipped_swiglu":
+        return clipped_swiglu(g, u, alpha, limit)
+    if act == "silu":
+        return silu_glu(g, u)
+    raise ValueError(act)
+
+
+def expert_mlp(X: np.ndarray, Wg, bg, Wu, bu, Wd, bd, act: str, alpha: float, limit: float) -> np.ndarray:
+    """One expert on the rows of X [n, d]:
+        g = X Wg^T + bg ; u = X Wu^T + bu ; h = act(g, u) ; y = h Wd^T + bd
+    ([MAXTEXT] "MOE EXPERTS": separate gate_proj / up_proj kernels and biases,
+    mlp2 weight and bias; [GLM] SwitchMLP.Forward: gate, up, activation, down)."""
+    g = X @ Wg.T
+    u = X @ Wu.T
+    if bg is not None:
+        g = g + bg[None, :]
+    if bu is not None:
+        u = u + bu[None, :]
+    h = activation(g, u, act, alpha, limit)
+    y = h @ Wd.T
+    if bd is not None:
+        y = y + bd[None, :]
+    return y
+
+
+class ExpertWeights:
+    """Access to one layer's stacked expert weights, decoded to float64 per expert.
+
+    `arrays` holds the stored inputs: w_gate/w_up/w_down (bf16 bits or f32) or
+    their MXFP4 (codes, scales) pairs, and b_gate/b_up/b_down (or None)."""
+
+    def __init__(self, arrays: dict, dtype: str, weights: str):
+        self.a = arrays
+        self.dtype = dtype
+        self.weights = weights
+
+    def _mat(self, name: str, e: int) -> np.ndarray:
+        if self.weights == "mxfp4":
+            return mxfp4_decode(self.a[name + "_codes"][e], self.a[name + "_scales"][e])
+        return to_f64(self.a[name][e], self.dtype)
+
+    def _vec(self, name: str, e: int):
+        b = self.a.get(name)
+        return None if b is None else to_f64(b[e], self.dtype)
+
+    def expert(self, e: int):
+        return (self._mat("w_gate", e), self._vec("b_gate", e),
+                self._mat("w_up", e), self._vec("b_up", e),
+                self._mat("w_down", e), self._vec("b_down", e))
+
+    def shared(self):
+        if self.a.get("shared_w_gate") is None:
+            return None
+        return (to_f64(self.a["shared_w_gate"], self.dtype), None,
+                to_f64(self.a["shared_w_up"], self.dtype), None,
+                to_f64(self.a["shared_w_down"], self.dtype), None)
+
+
+# ----------------------------------------------------------------------------
+# Routing of a whole layer, permutation, and the layer forward.
+
+
+def route(arrays: dict, cfg: dict, tokens: Optional[np.ndarray] = None):
+    """Router logits and (idx, w) for the given tokens (all tokens if None).
+
+    cfg keys: dtype, k, routing ("gptoss" | "grouped"); for grouped routing
+    also n_group, topk_group, norm_topk_prob, routed_scaling_factor, score;
+    optional e_score_bias (float array [E])."""
+    dt = cfg["dtype"]
+    x = to_f64(arrays["x"], dt)
+    if tokens is not None:
+        x = x[tokens]
+    l = router_logits(x, to_f64(arrays["router_w"], dt), to_f64(arrays.get("router_b"), dt))
+    if cfg.get("routing", "gptoss") == "gptoss":
+        idx, w = gptoss_route(l, cfg["k"])
+    else:
+        eb = cfg.get("e_score_bias")
+        idx, w = grouped_route(l, cfg["k"], cfg["n_group"], cfg["topk_group"],
+                               bool(cfg["norm_topk_prob"]), float(cfg["routed_scaling_factor"]),
+                               cfg.get("score", "softmax"),
+                               None if eb is None else np.asarray(eb, dtype=np.float64))
+    return l, idx, w
+
+
+def permutation(idx: np.ndarray, E: int):
+    """Order in which the (token, slot) pairs visit the experts ([GLM]
+    SwitchMLP.Forward: flatten the [T, k] indices, argsort, and the inverse
+    argsort to restore token order).
+
+    Pair p = t*k + j.  sorted_pair lists the pairs of expert 0 in increasing p,
+    then those of expert 1, and so on; pos is its inverse (pos[sorted_pair[r]] = r).
+    counts[e] = pairs routed to e; offsets = exclusive prefix sum (E+1 entries)."""
+    flat = np.asarray(idx).reshape(-1)
+    counts = np.zeros(E, dtype=np.int64)
+    sorted_pair = []
+    for e in range(E):
+        members = np.nonzero(flat == e)[0]       # increasing p
+        counts[e] = members.size
+        sorted_pair.append(members)
+    sorted_pair = np.concatenate(sorted_pair) if sorted_pair else np.zeros(0, np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    pos = np.empty_like(sorted_pair)
+    pos[sorted_pair] = np.arange(sorted_pair.size)
+    return counts, offsets, sorted_pair, pos
+
+
+def experts_forward(arrays: dict, cfg: dict, idx: np.ndarray, w: np.ndarray,
+                    tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """Routed experts and combine for the given tokens with the given routing:
+
+        out[t] = sum_{j = 0..k-1} w[t, j] * FFN_{idx[t, j]}(x_t)   (+ shared(x_t))
+
+    ([GLM] MoE.Forward: sum over the k expert outputs weighted by the gate
+    scores, then the shared experts added).  idx/w are [len(tokens), k]."""
+    dt = cfg["dtype"]
+    x = to_f64(arrays["x"], dt)
+    if tokens is not None:
+        x = x[tokens]
+    n, k = idx.shape
+    W = ExpertWeights(arrays, dt, cfg.get("weights", "dense"))
+    act, alpha, limit = cfg.get("act", "clipped_swiglu"), cfg.get("alpha", 1.702), cfg.get("limit", 7.0)
+    y = np.zeros((n, k, x.shape[1]), dtype=np.float64)
+    for e in np.unique(idx):
+        t_sel, j_sel = np.nonzero(idx == e)
+        y[t_sel, j_sel] = expert_mlp(x[t_sel], *W.expert(int(e)), act, alpha, limit)
+    out = np.zeros((n, x.shape[1]), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * y[:, j]
+    sh = W.shared()
+    if sh is not None:
+        out += expert_mlp(x, *sh, "silu", 0.0, 0.0)
+    return out
+
+
+def moe_layer(arrays: dict, cfg: dict, tokens: Optional[np.ndarray] = None) -> dict:
+    """Whole MoE-FFN layer for the given tokens: routing, experts, combine.
+    Returns dict(out, logits, idx, w), all float64 / int64."""
+    l, idx, w = route(arrays, cfg, tokens)
+    out = experts_forward(arrays, cfg, idx, w, tokens)
+    return {"out": out, "logits": l, "idx": idx, "w": w}
+
+
+def forced_weights(logits: np.ndarray, idx: np.ndarray, cfg: dict) -> np.ndarray:
+    """Routing weights of a given expert choice (used for tokens whose choice is
+    a near-tie, so that the output can be checked for the choice actually made)."""
+    l = np.asarray(logits, dtype=np.float64)
+    if cfg.get("routing", "gptoss") == "gptoss":
+        sel = np.take_along_axis(l, idx, axis=1)
+        ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+        return ex / ex.sum(axis=1, keepdims=True)
+    s = softmax(l) if cfg.get("score", "softmax") == "softmax" else sigmoid(l)
+    w = np.take_along_axis(s, idx, axis=1)
+    if idx.shape[1] > 1 and cfg["norm_topk_prob"]:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w * float(cfg["routed_scaling_factor"])
+
+
+# ----------------------------------------------------------------------------
+# Decision margins (how close a token's expert choice is to a tie).
+
+
+def route_margins(logits: np.ndarray, cfg: dict):
+    """Per-token margins of the routing decision in the space where it is made.
+
+    Returns (boundary, inner): boundary = gap between the last selected and the
+    best unselected candidate (for grouped routing also the gap at the group
+    boundary, whichever is smaller); inner = smallest gap between consecutive
+    selected experts (decides their order only).  Gaps are measured in logit
+    space (softmax and sigmoid are monotone in the logit), or in score space
+    when a correction bias is in use."""
+    l = np.asarray(logits, dtype=np.float64)
+    T, E = l.shape
+    k = cfg["k"]
+    if cfg.get("routing", "gptoss") == "grouped":
+        eb = cfg.get("e_score_bias")
+        if eb is not None:
+            s = softmax(l) if cfg.get("score", "softmax") == "softmax" else sigmoid(l)
+            l = s + np.asarray(eb, dtype=np.float64)[None, :]
+        ng, tg = cfg["n_group"], cfg["topk_group"]
+        gs = E // ng
+        G = l.reshape(T, ng, gs).max(axis=2)
+        Gs = -np.sort(-G, axis=1)
+        gmargin = Gs[:, tg - 1] - Gs[:, tg] if tg < ng else np.full(T, np.inf)
+        kept = order_desc(G)[:, :tg]
+        allowed = np.zeros((T, ng), dtype=bool)
+        np.put_along_axis(allowed, kept, True, axis=1)
+        cand = np.where(np.repeat(allowed, gs, axis=1), l, -np.inf)
+    else:
+        gmargin = np.full(T, np.inf)
+        cand = l
+    srt = -np.sort(-cand, axis=1)
+    boundary = srt[:, k - 1] - srt[:, k] if k < E else np.full(T, np.inf)
+    boundary = np.where(np.isfinite(boundary), boundary, np.inf)
+    boundary = np.minimum(boundary, gmargin)
+    inner = np.min(srt[:, :k - 1] - srt[:, 1:k], axis=1) if k > 1 else np.full(T, np.inf)
+    return boundary, inner
+
+
+# ----------------------------------------------------------------------------
+# Brute-force forms used to pin the oracle on tiny inputs.
+
+
+def topk_bruteforce(logits_row: np.ndarray, k: int) -> tuple:
+    """The k-subset of experts with the largest logit sum (exhaustive)."""
+    E = logits_row.shape[0]
+    best, best_set = -np.inf, None
+    for sub in itertools.combinations(range(E), k):
+        s = float(np.sum(logits_row[list(sub)]))
+        if s > best:
+            best, best_set = s, sub
+    return best_set
