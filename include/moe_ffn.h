@@ -1,0 +1,206 @@
+/*
+ * moe_ffn.h -- C ABI of an MI355X (gfx950) Mixture-of-Experts feed-forward layer.
+ *
+ * One call runs one MoE-FFN layer forward for T tokens on the caller's HIP
+ * stream:
+ *
+ *   1. router logits   l[t,e] = x[t,:] . router_w[e,:] + router_b[e]     (fp32)
+ *   2. routing         top-k experts per token and their weights
+ *   3. permutation     (token, slot) pairs sorted by expert, stably
+ *   4. gate|up         g = x W_gate[e]^T + b_gate[e], u = x W_up[e]^T + b_up[e],
+ *                      h = act(g, u)
+ *   5. down            y = h W_down[e]^T + b_down[e]
+ *   6. combine         out[t] = sum_j w[t,j] * y[t,j]  (+ shared expert(x_t))
+ *
+ * Sources (web pages on the MoE layers of GPT-OSS and GLM4-MoE-Lite):
+ *   - "Implementation:Ollama Ollama Imagegen GPT OSS", Description / Signature:
+ *     clipped SwiGLU (gate clipped to [0, limit], up to [-limit, limit], fixed
+ *     sigmoid scaling alpha = 1.702), num_local_experts, num_experts_per_tok,
+ *     swiglu_limit.
+ *   - MaxText GPT-OSS weight mapping, "MoE Router" and "MOE EXPERTS" blocks:
+ *     router kernel + bias; separate gate_proj / up_proj kernels and biases;
+ *     down projection (mlp2) weight and bias.
+ *   - glm4_moe_lite.go: MoEGate.Forward (sigmoid scores, correction bias used
+ *     for selection only, top-k, renormalisation when k > 1 and
+ *     norm_topk_prob, routed_scaling_factor), SwitchMLP.Forward (stacked
+ *     [E, out, in] expert weights, sort of the flattened expert indices and
+ *     its inverse), SharedExperts.Forward and MoE.Forward (weighted sum, then
+ *     shared experts added), Config (n_group, topk_group).
+ *   - "GPT-OSS 20B GGUF with MoE CPU Offloading Support", Model
+ *     Specifications: MXFP4 expert weights.  The MXFP4 bit layout is the OCP
+ *     Microscaling (MX) v1.0 one (e2m1 elements, one e8m0 scale per 32).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array pointer is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or synchronises device memory, keeps
+ *   no state between calls (except the opt-in profiler below) and is
+ *   reentrant.  Concurrent calls need distinct workspaces.  `out` must not
+ *   overlap any input or the workspace.
+ * Layouts.  Row-major and contiguous:
+ *   x [T, d]; router_w [E, d]; router_b [E];
+ *   w_gate, w_up [E, d_ff, d]; b_gate, b_up [E, d_ff];
+ *   w_down [E, d, d_ff]; b_down [E, d]; out [T, d].
+ *   Weights use the [out, in] convention: the reduction dimension is the
+ *   contiguous one.
+ * Element type.  `dt` gives the type of x, the router weight and bias, the
+ *   dense expert weights, all expert biases and out (MOE_F32 or MOE_BF16).
+ *   Router logits, routing weights, accumulation and the activation are fp32;
+ *   with MOE_BF16 the hidden activation h and the expert outputs y are stored
+ *   as bf16 between kernels.
+ * Routing outputs.  `routing` may be NULL; each of its fields may be NULL.
+ *   Non-NULL fields are filled (device pointers, caller-owned).
+ * Workspace.  `workspace` is device memory of at least
+ *   moe_ffn_workspace_bytes(...) bytes, 256-byte aligned; its contents on
+ *   entry do not matter and are clobbered.
+ * Stream.  All work is enqueued on `stream` (0 = the null stream).  The call
+ *   returns without waiting for the GPU.
+ * Errors.  Every argument is checked on the host before anything is
+ *   enqueued.  On an error nothing is launched, `out` and the workspace are
+ *   untouched and a non-zero status is returned; moe_last_error_detail()
+ *   then describes it.  T == 0 is a valid no-op.  A launch failure returns
+ *   MOE_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *   synchronisation.
+ * Limits.  1 <= E <= 256, 1 <= k <= min(E, 16), d and d_ff multiples of 8
+ *   (of 32 for MXFP4 weights), T * k < 2^26.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* NULL required pointer, out-of-range size or parameter */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid layer outside the limits listed above */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Activation of the expert MLP.
+ *   MOE_ACT_CLIPPED_SWIGLU: g' = min(max(g, 0), limit), u' = min(max(u, -limit), limit),
+ *                           h = g' * sigmoid(alpha * g') * u'   (GPT-OSS page, Description)
+ *   MOE_ACT_SILU:           h = g * sigmoid(g) * u             (glm4_moe_lite.go, SwitchMLP) */
+typedef enum { MOE_ACT_CLIPPED_SWIGLU = 0, MOE_ACT_SILU = 1 } moe_act;
+
+/* Expert score of grouped routing: softmax over all E logits, or the
+ * element-wise sigmoid that glm4_moe_lite.go's MoEGate.Forward applies. */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+typedef struct {
+  int32_t* topk_idx;       /* [T, k]: chosen experts, best first (ties: lower index first) */
+  float* topk_w;           /* [T, k]: routing weight of each chosen expert */
+  int32_t* expert_offsets; /* [E + 1]: exclusive prefix sum of pairs per routed expert */
+  int32_t* sorted_pair;    /* [T * k]: pair ids p = t*k + j sorted by (expert, p) */
+} moe_routing_out;
+
+/* Bytes of workspace a call with these sizes needs (pure host function).
+ * d_ff_shared = 0 when there is no shared expert.  Returns 0 for T == 0 and
+ * (size_t)-1 for sizes outside the limits. */
+size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int d_ff_shared);
+
+/* GPT-OSS-style layer.
+ * Routing: the k largest router logits per token (ties to the lower expert
+ * index), weights = softmax over the k selected logits.  Activation: clipped
+ * SwiGLU with `alpha` and `limit` (limit > 0).  router_b, b_gate, b_up,
+ * b_down may be NULL (no bias); x, router_w, w_gate, w_up, w_down and out are
+ * required when T > 0. */
+moe_status moe_ffn_forward(const void* x, const void* router_w, const void* router_b,
+                           const void* w_gate, const void* b_gate,
+                           const void* w_up, const void* b_up,
+                           const void* w_down, const void* b_down,
+                           int T, int d, int d_ff, int E, int k, float alpha, float limit,
+                           void* out, moe_dtype dt, void* workspace, size_t workspace_bytes,
+                           moe_routing_out* routing, hipStream_t stream);
+
+/* GPT-OSS-style layer with MXFP4 expert weights ("F16 base + MXFP4 expert
+ * weights", GGUF page, Model Specifications).  Same as moe_ffn_forward with
+ * dt = MOE_BF16, except that each expert weight is a pair:
+ *   *_codes  uint8 [E, rows, cols/2]: e2m1 codes (bit 3 = sign), element 2i of
+ *            a row in the low nibble, element 2i+1 in the high nibble;
+ *   *_scales uint8 [E, rows, cols/32]: e8m0 scale 2^(byte-127) of each block of
+ *            32 consecutive elements along cols (the input dimension).
+ * (rows, cols) = (d_ff, d) for gate and up, (d, d_ff) for down.  x, router
+ * weight and bias, expert biases and out are bf16.  d and d_ff must be
+ * multiples of 32.  A scale byte of 255 (NaN) yields NaN outputs. */
+moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void* router_b,
+                                 const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                 const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                 const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                 int T, int d, int d_ff, int E, int k, float alpha, float limit,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 moe_routing_out* routing, hipStream_t stream);
+
+/* GLM4-MoE-style layer with group-limited routing and optional shared expert
+ * (glm4_moe_lite.go: Config, MoEGate.Forward, SharedExperts.Forward, MoE.Forward).
+ * Routing per token:
+ *   s  = softmax(l) over all E (score = MOE_SCORE_SOFTMAX) or sigmoid(l);
+ *   s' = s + e_score_bias (fp32 [E], NULL = none; used for selection only);
+ *   the E experts form n_group contiguous groups of E/n_group; a group's
+ *   score is the largest s' in it; the topk_group best groups are kept (ties
+ *   to the lower group index); the k best experts by s' among the kept
+ *   groups are chosen (ties to the lower index);
+ *   w = s[chosen]; if k > 1 and norm_topk_prob, w /= sum(w); w *= routed_scaling_factor.
+ * Requirements: E % n_group == 0, 1 <= n_group <= 64, 1 <= topk_group <= n_group,
+ * k <= topk_group * E / n_group.
+ * Experts use `act` (with alpha/limit for MOE_ACT_CLIPPED_SWIGLU).  Biases may be NULL.
+ * Shared expert: when shared_w_gate != NULL, shared_w_gate/shared_w_up
+ * [d_ff_shared, d] and shared_w_down [d, d_ff_shared] (same dt, no bias)
+ * form a SiLU-gated MLP applied to every token with weight 1 and added after
+ * the routed sum; d_ff_shared must then be >= 1 and a multiple of 8. */
+moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const void* router_b,
+                                   const float* e_score_bias,
+                                   const void* w_gate, const void* b_gate,
+                                   const void* w_up, const void* b_up,
+                                   const void* w_down, const void* b_down,
+                                   const void* shared_w_gate, const void* shared_w_up,
+                                   const void* shared_w_down, int d_ff_shared,
+                                   int T, int d, int d_ff, int E, int k,
+                                   int n_group, int topk_group, int norm_topk_prob,
+                                   float routed_scaling_factor, moe_score score,
+                                   moe_act act, float alpha, float limit,
+                                   void* out, moe_dtype dt, void* workspace, size_t workspace_bytes,
+                                   moe_routing_out* routing, hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Description of the last error returned on the calling thread (static,
+ * thread-local storage; empty after a successful call). */
+const char* moe_last_error_detail(void);
+
+/* ---- Opt-in stage timing -------------------------------------------------
+ * Stages of one call, in launch order. */
+typedef enum {
+  MOE_STAGE_ROUTE = 0,    /* router logits + top-k + weights */
+  MOE_STAGE_PERMUTE = 1,  /* per-expert counts, prefix sums, stable scatter */
+  MOE_STAGE_GATE_UP = 2,  /* grouped gate|up GEMM + bias + activation */
+  MOE_STAGE_DOWN = 3,     /* grouped down GEMM + bias */
+  MOE_STAGE_COMBINE = 4,  /* weighted gather-reduce back to token order */
+  MOE_NUM_STAGES = 5
+} moe_stage;
+
+/* Enable (stage_mask != 0) or disable (0) timing of the stages whose bit
+ * (1 << moe_stage) is set.  While enabled, every forward call records a HIP
+ * event before and after each selected stage on its stream.  Events are
+ * created here (not in the forward calls).  Process-wide; not thread-safe. */
+moe_status moe_ffn_profile_enable(unsigned stage_mask);
+
+/* Wait for the recorded events, then write, per stage, the summed duration
+ * in milliseconds and the number of timed launches since the last read (or
+ * enable), and reset the sums.  ms and launches have n_stages entries. */
+moe_status moe_ffn_profile_read(double* ms, int* launches, int n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

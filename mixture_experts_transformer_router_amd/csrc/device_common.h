@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels: element loads/stores, the two
+// expert activations and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p, size_t i);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+template <typename T> __device__ __forceinline__ void store_f32(T* p, size_t i, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, size_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Expert activation.  act 0: clipped SwiGLU (gate clipped to [0, limit], up to
+// [-limit, limit], h = g' * sigmoid(alpha g') * u').  act 1: h = g sigmoid(g) u.
+__device__ __forceinline__ float expert_act(int act, float g, float u, float alpha, float limit) {
+  if (act == 0) {
+    float gc = fminf(fmaxf(g, 0.f), limit);
+    float uc = fminf(fmaxf(u, -limit), limit);
+    return gc * sigmoidf_(alpha * gc) * uc;
+  }
+  return g * sigmoidf_(g) * u;
+}
+
+// Wave64 reductions (all lanes receive the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// Index of an empty arg-max candidate.
+constexpr int kNoIndex = 0x7fffffff;
+
+// (v1, i1) precedes (v2, i2) in the order (value descending, index
+// ascending); an empty candidate (index kNoIndex) follows everything.  Values
+// must not be NaN (callers map NaN to -inf), so the order is total.
+__device__ __forceinline__ bool precedes(float v1, int i1, float v2, int i2) {
+  if (i1 == kNoIndex) return false;
+  if (i2 == kNoIndex) return true;
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Arg-max over the wave in that order; every lane receives the same result.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, 64);
+    int oi = __shfl_xor(i, o, 64);
+    if (precedes(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+}
+
+}  // namespace moe

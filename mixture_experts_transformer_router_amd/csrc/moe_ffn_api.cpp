@@ -1,0 +1,309 @@
+// Host side of the C ABI declared in moe_ffn.h: argument checks, workspace
+// layout, and the launch sequence route -> permute -> gate|up -> down ->
+// combine on the caller's stream.  Nothing here allocates device memory or
+// synchronises, except the opt-in stage timer (moe_ffn_profile_*).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+thread_local char g_detail[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// ---- opt-in stage timer ----------------------------------------------------
+struct Profiler {
+  std::mutex mu;
+  unsigned mask = 0;
+  std::vector<hipEvent_t> begin, end;
+  std::vector<int> stage_of;  // stage of each used pair
+  size_t used = 0;
+} g_prof;
+
+constexpr size_t kProfPairs = 8192;
+
+struct StageTimer {
+  hipStream_t s;
+  int stage;
+  long slot = -1;
+  StageTimer(hipStream_t s_, int stage_) : s(s_), stage(stage_) {
+    if (!(g_prof.mask & (1u << stage))) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.used >= g_prof.begin.size()) return;
+    slot = static_cast<long>(g_prof.used++);
+    g_prof.stage_of[slot] = stage;
+    hipEventRecord(g_prof.begin[slot], s);
+  }
+  ~StageTimer() {
+    if (slot >= 0) hipEventRecord(g_prof.end[slot], s);
+  }
+};
+
+// ---- checks ----------------------------------------------------------------
+moe_status check_common(const Layer& L) {
+  if (L.T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", L.T);
+  if (L.d < 1 || L.F < 1) return fail(MOE_ERR_INVALID_ARG, "d = %d, d_ff = %d must be >= 1", L.d, L.F);
+  if (L.E < 1) return fail(MOE_ERR_INVALID_ARG, "E = %d must be >= 1", L.E);
+  if (L.k < 1 || L.k > L.E) return fail(MOE_ERR_INVALID_ARG, "k = %d must be in [1, E = %d]", L.k, L.E);
+  if (L.E > 256) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 256", L.E);
+  if (L.k > 16) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 16", L.k);
+  if ((long long)L.T * L.k >= (1ll << 26)) return fail(MOE_ERR_UNSUPPORTED, "T * k = %lld >= 2^26", (long long)L.T * L.k);
+  if (L.dt != MOE_F32 && L.dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", L.dt);
+  const int q = L.wfmt == WF_MXFP4 ? 32 : 8;
+  if (L.d % q || L.F % q) return fail(MOE_ERR_UNSUPPORTED, "d = %d and d_ff = %d must be multiples of %d", L.d, L.F, q);
+  if (L.act != MOE_ACT_CLIPPED_SWIGLU && L.act != MOE_ACT_SILU) return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", L.act);
+  if (L.act == MOE_ACT_CLIPPED_SWIGLU) {
+    if (!(L.limit > 0.f) || !std::isfinite(L.limit)) return fail(MOE_ERR_INVALID_ARG, "limit = %g must be finite and > 0", (double)L.limit);
+    if (!std::isfinite(L.alpha)) return fail(MOE_ERR_INVALID_ARG, "alpha must be finite");
+  }
+  if (L.grouped) {
+    if (L.n_group < 1 || L.E % L.n_group) return fail(MOE_ERR_INVALID_ARG, "n_group = %d must divide E = %d", L.n_group, L.E);
+    if (L.n_group > 64) return fail(MOE_ERR_UNSUPPORTED, "n_group = %d > 64", L.n_group);
+    if (L.topk_group < 1 || L.topk_group > L.n_group)
+      return fail(MOE_ERR_INVALID_ARG, "topk_group = %d must be in [1, n_group = %d]", L.topk_group, L.n_group);
+    if (L.k > L.topk_group * (L.E / L.n_group))
+      return fail(MOE_ERR_INVALID_ARG, "k = %d exceeds the %d experts of topk_group groups", L.k, L.topk_group * (L.E / L.n_group));
+    if (!std::isfinite(L.rsf)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor must be finite");
+    if (L.score != MOE_SCORE_SOFTMAX && L.score != MOE_SCORE_SIGMOID) return fail(MOE_ERR_INVALID_ARG, "unknown score %d", L.score);
+  }
+  if (L.has_shared()) {
+    if (!L.sh_wu || !L.sh_wd) return fail(MOE_ERR_INVALID_ARG, "shared_w_up and shared_w_down are required with shared_w_gate");
+    if (L.F_sh < 1 || L.F_sh % 8) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared = %d must be >= 1 and a multiple of 8", L.F_sh);
+  }
+  if (L.T == 0) return MOE_OK;
+  if (!L.x || !L.router_w || !L.out) return fail(MOE_ERR_INVALID_ARG, "x, router_w and out are required");
+  if (L.wfmt == WF_MXFP4) {
+    if (!L.wg_codes || !L.wg_scales || !L.wu_codes || !L.wu_scales || !L.wd_codes || !L.wd_scales)
+      return fail(MOE_ERR_INVALID_ARG, "all MXFP4 codes and scales are required");
+  } else if (!L.wg || !L.wu || !L.wd) {
+    return fail(MOE_ERR_INVALID_ARG, "w_gate, w_up and w_down are required");
+  }
+  const size_t xbytes = (size_t)L.T * L.d * L.elt();
+  if (overlaps(L.out, xbytes, L.x, xbytes)) return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
+  return MOE_OK;
+}
+
+moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
+  g_detail[0] = '\0';
+  moe_status st = check_common(L);
+  if (st != MOE_OK || L.T == 0) return st;
+  Work W;
+  const size_t need = carve_workspace(L, nullptr, &W);
+  if (need == (size_t)-1) return fail(MOE_ERR_UNSUPPORTED, "workspace size overflows");
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (overlaps(L.out, (size_t)L.T * L.d * L.elt(), ws, need)) return fail(MOE_ERR_INVALID_ARG, "out overlaps the workspace");
+  carve_workspace(L, ws, &W);
+
+  hipError_t e;
+  {
+    StageTimer tm(s, MOE_STAGE_ROUTE);
+    e = launch_route(L, W, s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "route launch: %s", hipGetErrorString(e));
+  {
+    StageTimer tm(s, MOE_STAGE_PERMUTE);
+    e = launch_permute(L, W, s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
+  {
+    StageTimer tm(s, MOE_STAGE_GATE_UP);
+    e = launch_gate_up(L, W, s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
+  {
+    StageTimer tm(s, MOE_STAGE_DOWN);
+    e = launch_down(L, W, s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
+  {
+    StageTimer tm(s, MOE_STAGE_COMBINE);
+    e = launch_combine(L, W, s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+}  // namespace
+
+size_t carve_workspace(const Layer& L, void* ws, Work* W) {
+  const size_t P = (size_t)L.T * L.k;
+  const size_t rows = (size_t)L.rows_all();
+  const size_t nblk = ((size_t)L.T + kRouteTokens - 1) / kRouteTokens;
+  const size_t Eall = (size_t)L.n_experts_all();
+  size_t off = 0;
+  char* base = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  W->idx = static_cast<int32_t*>(take(P * 4));
+  W->w = static_cast<float*>(take(P * 4));
+  W->hist = static_cast<int32_t*>(take(nblk * L.E * 4));
+  W->offsets = static_cast<int32_t*>(take((Eall + 1) * 4));
+  W->tile_prefix = static_cast<int32_t*>(take((Eall + 1) * 4));
+  W->sorted_pair = static_cast<int32_t*>(take(rows * 4));
+  W->row_token = static_cast<int32_t*>(take(rows * 4));
+  W->pos = static_cast<int32_t*>(take(P * 4));
+  W->h = take(rows * (size_t)L.F_max() * L.elt());
+  W->y = take(rows * (size_t)L.d * L.elt());
+  return off;
+}
+
+}  // namespace moe
+
+using moe::Layer;
+
+extern "C" {
+
+size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int d_ff_shared) {
+  if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E || d_ff_shared < 0) return (size_t)-1;
+  if ((long long)T * k >= (1ll << 26)) return (size_t)-1;
+  if (T == 0) return 0;
+  Layer L;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k; L.dt = dt;
+  L.F_sh = d_ff_shared;
+  static const char dummy = 0;
+  if (d_ff_shared > 0) L.sh_wg = &dummy;
+  moe::Work W;
+  return moe::carve_workspace(L, nullptr, &W);
+}
+
+moe_status moe_ffn_forward(const void* x, const void* router_w, const void* router_b,
+                           const void* w_gate, const void* b_gate, const void* w_up, const void* b_up,
+                           const void* w_down, const void* b_down, int T, int d, int d_ff, int E, int k,
+                           float alpha, float limit, void* out, moe_dtype dt, void* workspace,
+                           size_t workspace_bytes, moe_routing_out* routing, hipStream_t stream) {
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b;
+  L.wg = w_gate; L.bg = b_gate; L.wu = w_up; L.bu = b_up; L.wd = w_down; L.bd = b_down;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
+  L.dt = dt; L.wfmt = dt == MOE_F32 ? moe::WF_F32 : moe::WF_BF16;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void* router_b,
+                                 const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                 const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                 const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                 int T, int d, int d_ff, int E, int k, float alpha, float limit, void* out,
+                                 void* workspace, size_t workspace_bytes, moe_routing_out* routing,
+                                 hipStream_t stream) {
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b;
+  L.wg_codes = w_gate_codes; L.wg_scales = w_gate_scales; L.bg = b_gate;
+  L.wu_codes = w_up_codes; L.wu_scales = w_up_scales; L.bu = b_up;
+  L.wd_codes = w_down_codes; L.wd_scales = w_down_scales; L.bd = b_down;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
+  L.dt = MOE_BF16; L.wfmt = moe::WF_MXFP4;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const void* router_b,
+                                   const float* e_score_bias, const void* w_gate, const void* b_gate,
+                                   const void* w_up, const void* b_up, const void* w_down, const void* b_down,
+                                   const void* shared_w_gate, const void* shared_w_up, const void* shared_w_down,
+                                   int d_ff_shared, int T, int d, int d_ff, int E, int k, int n_group,
+                                   int topk_group, int norm_topk_prob, float routed_scaling_factor,
+                                   moe_score score, moe_act act, float alpha, float limit, void* out,
+                                   moe_dtype dt, void* workspace, size_t workspace_bytes,
+                                   moe_routing_out* routing, hipStream_t stream) {
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b; L.e_bias = e_score_bias;
+  L.wg = w_gate; L.bg = b_gate; L.wu = w_up; L.bu = b_up; L.wd = w_down; L.bd = b_down;
+  L.sh_wg = shared_w_gate; L.sh_wu = shared_w_up; L.sh_wd = shared_w_down;
+  L.F_sh = shared_w_gate ? d_ff_shared : 0;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.grouped = 1; L.n_group = n_group; L.topk_group = topk_group; L.norm = norm_topk_prob ? 1 : 0;
+  L.rsf = routed_scaling_factor; L.score = score;
+  L.act = act; L.alpha = alpha; L.limit = limit;
+  L.dt = dt; L.wfmt = dt == MOE_F32 ? moe::WF_F32 : moe::WF_BF16;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_UNKNOWN_STATUS";
+}
+
+const char* moe_last_error_detail(void) { return moe::g_detail; }
+
+moe_status moe_ffn_profile_enable(unsigned stage_mask) {
+  using moe::g_prof;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (stage_mask && g_prof.begin.empty()) {
+    g_prof.begin.resize(moe::kProfPairs);
+    g_prof.end.resize(moe::kProfPairs);
+    g_prof.stage_of.assign(moe::kProfPairs, -1);
+    for (size_t i = 0; i < moe::kProfPairs; ++i) {
+      if (hipEventCreate(&g_prof.begin[i]) != hipSuccess || hipEventCreate(&g_prof.end[i]) != hipSuccess)
+        return moe::fail(MOE_ERR_HIP, "hipEventCreate failed");
+    }
+  }
+  g_prof.mask = stage_mask;
+  g_prof.used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_ffn_profile_read(double* ms, int* launches, int n_stages) {
+  using moe::g_prof;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int i = 0; i < n_stages; ++i) {
+    if (ms) ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    const int st = g_prof.stage_of[i];
+    if (hipEventSynchronize(g_prof.end[i]) != hipSuccess) return moe::fail(MOE_ERR_HIP, "hipEventSynchronize failed");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_prof.begin[i], g_prof.end[i]) != hipSuccess)
+      return moe::fail(MOE_ERR_HIP, "hipEventElapsedTime failed");
+    if (st >= 0 && st < n_stages) {
+      if (ms) ms[st] += t;
+      if (launches) launches[st] += 1;
+    }
+  }
+  g_prof.used = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

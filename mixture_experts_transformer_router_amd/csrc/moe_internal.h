@@ -1,0 +1,87 @@
+// Internal declarations shared by the host dispatcher and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_ffn.h"
+
+namespace moe {
+
+// Storage format of the expert weights.
+enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2 };
+
+// Tokens handled by one block of the route and permute kernels.
+constexpr int kRouteTokens = 64;
+// Rows per M-tile of the tiled grouped GEMMs (the permute kernel writes the
+// per-expert tile prefix for this size).
+constexpr int kTileM = 64;
+
+// One call's arguments after validation.
+struct Layer {
+  const void* x = nullptr;
+  const void* router_w = nullptr;
+  const void* router_b = nullptr;
+  const float* e_bias = nullptr;
+  const void* wg = nullptr;
+  const void* bg = nullptr;
+  const void* wu = nullptr;
+  const void* bu = nullptr;
+  const void* wd = nullptr;
+  const void* bd = nullptr;
+  const uint8_t* wg_codes = nullptr;
+  const uint8_t* wg_scales = nullptr;
+  const uint8_t* wu_codes = nullptr;
+  const uint8_t* wu_scales = nullptr;
+  const uint8_t* wd_codes = nullptr;
+  const uint8_t* wd_scales = nullptr;
+  const void* sh_wg = nullptr;
+  const void* sh_wu = nullptr;
+  const void* sh_wd = nullptr;
+  int F_sh = 0;
+  int T = 0, d = 0, F = 0, E = 0, k = 0;
+  int grouped = 0, n_group = 1, topk_group = 1, norm = 0;
+  float rsf = 1.f;
+  int score = MOE_SCORE_SOFTMAX;
+  int act = MOE_ACT_CLIPPED_SWIGLU;
+  float alpha = 1.702f, limit = 7.f;
+  int dt = MOE_BF16;
+  int wfmt = WF_BF16;
+  void* out = nullptr;
+  moe_routing_out routing{nullptr, nullptr, nullptr, nullptr};
+
+  bool has_shared() const { return sh_wg != nullptr; }
+  int n_experts_all() const { return E + (has_shared() ? 1 : 0); }
+  int pairs() const { return T * k; }
+  int rows_all() const { return T * k + (has_shared() ? T : 0); }
+  int F_max() const { return F_sh > F ? F_sh : F; }
+  size_t elt() const { return dt == MOE_F32 ? 4 : 2; }
+};
+
+// Device buffers carved out of the caller's workspace.
+struct Work {
+  int32_t* idx = nullptr;          // [T*k] chosen experts
+  float* w = nullptr;              // [T*k] routing weights
+  int32_t* hist = nullptr;         // [n_route_blocks * E] per-block expert counts
+  int32_t* offsets = nullptr;      // [E_all + 1] row offsets of each expert (shared last)
+  int32_t* tile_prefix = nullptr;  // [E_all + 1] first M-tile of each expert
+  int32_t* sorted_pair = nullptr;  // [rows_all] pair id of each sorted row (shared rows: -1)
+  int32_t* row_token = nullptr;    // [rows_all] token of each sorted row
+  int32_t* pos = nullptr;          // [T*k] sorted row of each pair
+  void* h = nullptr;               // [rows_all, F_max] hidden activation (dt)
+  void* y = nullptr;               // [rows_all, d] expert outputs (dt)
+};
+
+// Byte size of the workspace and the layout of its buffers (ws == nullptr:
+// size only).  Returns (size_t)-1 for sizes it cannot represent.
+size_t carve_workspace(const Layer& L, void* ws, Work* W);
+
+// Kernel launchers (each enqueues one kernel on `s`).
+hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_gate_up(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
+
+}  // namespace moe

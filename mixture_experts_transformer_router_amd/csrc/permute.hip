@@ -1,0 +1,154 @@
+// Permutation of the (token, slot) pairs into expert order.
+//
+// Pair p = t*k + j is routed to expert idx[p].  Rows of the grouped GEMMs are
+// the pairs sorted by (expert, p) -- the stable sort of the flattened expert
+// indices that glm4_moe_lite.go's SwitchMLP.Forward performs, with its
+// inverse (pos) used to return to token order.  With a shared expert, its T
+// rows (one per token, in token order) follow all routed rows.
+//
+// One block per route block (64 tokens, 64*k pairs).  Each block
+//   1. sums the per-block expert counts written by the router: totals give the
+//      expert offsets (exclusive prefix sum), the counts of earlier blocks give
+//      this block's first row inside each expert;
+//   2. ranks its own pairs stably: per wavefront, the lanes routed to the same
+//      expert are found with 9 ballots over the expert id bits; earlier
+//      wavefronts and rounds are added through small LDS counters;
+//   3. writes sorted_pair, row_token and pos.
+// Block 0 also writes the expert offsets and the M-tile prefix used by the
+// grouped GEMMs.  No atomics touch global memory: the result is unique.
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxE = 257;  // 256 routed experts + shared
+
+struct PermuteArgs {
+  const int32_t* idx;
+  const int32_t* hist;
+  int T, k, E, nblk, shared;
+  int tile_m;
+  int32_t* offsets;
+  int32_t* tile_prefix;
+  int32_t* sorted_pair;
+  int32_t* row_token;
+  int32_t* pos;
+  int32_t* user_offsets;
+  int32_t* user_sorted;
+};
+
+__global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
+  __shared__ int total[kMaxE];
+  __shared__ int before[kMaxE];
+  __shared__ int off[kMaxE + 1];
+  __shared__ int running[kMaxE];
+  __shared__ int wcnt[4][kMaxE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x;
+  const int E = a.E;
+
+  for (int e = tid; e < E; e += kThreads) {
+    int tot = 0, bef = 0;
+    for (int i = 0; i < a.nblk; ++i) {
+      int c = a.hist[(size_t)i * E + e];
+      tot += c;
+      if (i < b) bef += c;
+    }
+    total[e] = tot;
+    before[e] = bef;
+    running[e] = 0;
+  }
+  for (int i = tid; i < 4 * kMaxE; i += kThreads) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) { off[e] = acc; acc += total[e]; }
+    off[E] = acc;
+  }
+  __syncthreads();
+
+  if (b == 0) {
+    const int Eall = E + (a.shared ? 1 : 0);
+    for (int e = tid; e <= E; e += kThreads) {
+      a.offsets[e] = off[e];
+      if (a.user_offsets) a.user_offsets[e] = off[e];
+    }
+    if (a.shared && tid == 0) a.offsets[E + 1] = off[E] + a.T;
+    if (tid == 0) {
+      int acc = 0;
+      for (int e = 0; e < Eall; ++e) {
+        a.tile_prefix[e] = acc;
+        int c = e < E ? total[e] : a.T;
+        acc += (c + a.tile_m - 1) / a.tile_m;
+      }
+      a.tile_prefix[Eall] = acc;
+    }
+  }
+
+  const int t_begin = b * kRouteTokens;
+  const int t_end = min(a.T, t_begin + kRouteTokens);
+  const int p_begin = t_begin * a.k;
+  const int n = (t_end - t_begin) * a.k;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int r0 = 0; r0 < n; r0 += kThreads) {
+    const int pl = r0 + tid;
+    const bool valid = pl < n;
+    const int e = valid ? a.idx[p_begin + pl] : 0;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bm = __ballot(on);
+      m &= on ? bm : ~bm;
+    }
+    const int rank = __popcll(m & lt_mask);
+    if (valid && rank == 0) wcnt[wv][e] = __popcll(m);
+    __syncthreads();
+    if (valid) {
+      int pre = running[e];
+      for (int w2 = 0; w2 < wv; ++w2) pre += wcnt[w2][e];
+      const int dest = off[e] + before[e] + pre + rank;
+      const int p = p_begin + pl;
+      a.sorted_pair[dest] = p;
+      a.row_token[dest] = p / a.k;
+      a.pos[p] = dest;
+      if (a.user_sorted) a.user_sorted[dest] = p;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kThreads) {
+      running[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
+      wcnt[0][ee] = wcnt[1][ee] = wcnt[2][ee] = wcnt[3][ee] = 0;
+    }
+    __syncthreads();
+  }
+
+  if (a.shared) {
+    const int P = a.T * a.k;
+    for (int t = t_begin + tid; t < t_end; t += kThreads) {
+      a.sorted_pair[P + t] = -1;
+      a.row_token[P + t] = t;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s) {
+  PermuteArgs a;
+  a.idx = W.idx; a.hist = W.hist;
+  a.T = L.T; a.k = L.k; a.E = L.E;
+  a.nblk = (L.T + kRouteTokens - 1) / kRouteTokens;
+  a.shared = L.has_shared() ? 1 : 0;
+  a.tile_m = kTileM;
+  a.offsets = W.offsets; a.tile_prefix = W.tile_prefix;
+  a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
+  a.user_offsets = L.routing.expert_offsets; a.user_sorted = L.routing.sorted_pair;
+  permute_kernel<<<a.nblk, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

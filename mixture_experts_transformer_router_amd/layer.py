@@ -1,0 +1,54 @@
+"""Run a described workload through the C ABI: move generated arrays to the
+device as torch tensors and call the matching entry point (marshalling only)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import moe_ffn
+from .workloads import Workload
+
+
+def to_device(arrays: dict, device="cuda") -> dict:
+    """numpy arrays (bf16 as uint16 bits) -> device tensors (bf16 / f32 / uint8)."""
+    out = {}
+    for key, a in arrays.items():
+        if a is None:
+            out[key] = None
+        elif a.dtype == np.uint16:
+            out[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        else:
+            out[key] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return out
+
+
+def workspace_for(w: Workload, device="cuda") -> torch.Tensor:
+    dt = moe_ffn.MOE_F32 if w.dtype == "f32" else moe_ffn.MOE_BF16
+    n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared)
+    return moe_ffn.alloc_workspace(n, device)
+
+
+def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=None,
+        e_score_bias=None):
+    """One layer forward of workload `w` on device tensors `t`."""
+    if w.routing == "grouped":
+        return moe_ffn.forward_grouped(
+            t["x"], t["router_w"], t.get("router_b"), t.get("w_gate"), t.get("b_gate"), t.get("w_up"),
+            t.get("b_up"), t.get("w_down"), t.get("b_down"), w.k, w.n_group, w.topk_group,
+            w.norm_topk_prob, w.routed_scaling_factor,
+            score=moe_ffn.MOE_SCORE_SOFTMAX if w.score == "softmax" else moe_ffn.MOE_SCORE_SIGMOID,
+            act=moe_ffn.MOE_ACT_SILU if w.act == "silu" else moe_ffn.MOE_ACT_CLIPPED_SWIGLU,
+            alpha=w.alpha, limit=w.limit, e_score_bias=e_score_bias,
+            shared_w_gate=t.get("shared_w_gate"), shared_w_up=t.get("shared_w_up"),
+            shared_w_down=t.get("shared_w_down"), out=out, workspace=workspace, routing=routing,
+            stream=stream)
+    if w.weights == "mxfp4":
+        return moe_ffn.forward_mxfp4(
+            t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),
+            t["w_up_codes"], t["w_up_scales"], t.get("b_up"), t["w_down_codes"], t["w_down_scales"],
+            t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
+            routing=routing, stream=stream)
+    return moe_ffn.forward(
+        t["x"], t["router_w"], t.get("router_b"), t["w_gate"], t.get("b_gate"), t["w_up"], t.get("b_up"),
+        t["w_down"], t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
+        routing=routing, stream=stream)

@@ -1,0 +1,143 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/moe_ffn.h declares, and rejects every invalid argument before any HIP
+call (the device pointers below are never dereferenced).  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_transformer_router_amd import moe_ffn as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+FAKE = 0x7f0000000000  # 256-aligned, never dereferenced
+FAKE2 = 0x7f1000000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.lib_path()):
+        from mixture_experts_transformer_router_amd import build
+        build.build()
+    return M.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert len(declared) >= 8, declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in moe_ffn.h but not exported"
+    assert sorted(declared) == sorted(M.EXPORTED)
+
+
+def test_status_strings(lib):
+    for s, n in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARG"), (2, "MOE_ERR_UNSUPPORTED"),
+                 (3, "MOE_ERR_WORKSPACE"), (4, "MOE_ERR_HIP")]:
+        assert lib.moe_status_string(s).decode() == n
+
+
+def test_workspace_bytes(lib):
+    n = lib.moe_ffn_workspace_bytes
+    assert n(0, 2880, 2880, 32, 4, M.MOE_BF16, 0) == 0
+    big = n(8192, 2880, 2880, 32, 4, M.MOE_BF16, 0)
+    P = 8192 * 4
+    assert big >= 2 * P * 2880 * 2          # hidden activations + expert outputs (bf16)
+    assert big < 2 * P * 2880 * 2 + (8 << 20)
+    assert n(16, 64, 64, 8, 2, M.MOE_F32, 0) > n(16, 64, 64, 8, 2, M.MOE_BF16, 0)
+    assert n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 1536) > n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 0)
+    bad = ctypes.c_size_t(-1).value
+    assert n(8, 64, 64, 300, 2, M.MOE_BF16, 0) == bad
+    assert n(8, 64, 64, 8, 9, M.MOE_BF16, 0) == bad
+    assert n(-1, 64, 64, 8, 2, M.MOE_BF16, 0) == bad
+
+
+def _fwd(lib, T=16, d=64, F=64, E=8, k=2, alpha=1.702, limit=7.0, dt=M.MOE_BF16, x=FAKE, wr=FAKE,
+         wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE2, ws=None, wsb=None):
+    need = lib.moe_ffn_workspace_bytes(max(T, 0), d, F, E, min(k, 16) if k > 0 else 1, dt, 0)
+    if ws is None:
+        ws = FAKE + (1 << 36)
+    if wsb is None:
+        wsb = need if need != ctypes.c_size_t(-1).value else 0
+    return lib.moe_ffn_forward(x, wr, None, wg, None, wu, None, wd, None, T, d, F, E, k, alpha, limit,
+                               out, dt, ws, wsb, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9), M.MOE_ERR_INVALID_ARG),
+    (dict(k=0), M.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(d=0), M.MOE_ERR_INVALID_ARG),
+    (dict(E=0, k=1), M.MOE_ERR_INVALID_ARG),
+    (dict(E=300, k=2), M.MOE_ERR_UNSUPPORTED),
+    (dict(E=32, k=17), M.MOE_ERR_UNSUPPORTED),
+    (dict(d=100), M.MOE_ERR_UNSUPPORTED),
+    (dict(F=36), M.MOE_ERR_UNSUPPORTED),
+    (dict(limit=0.0), M.MOE_ERR_INVALID_ARG),
+    (dict(limit=float("nan")), M.MOE_ERR_INVALID_ARG),
+    (dict(alpha=float("inf")), M.MOE_ERR_INVALID_ARG),
+    (dict(x=None), M.MOE_ERR_INVALID_ARG),
+    (dict(wr=None), M.MOE_ERR_INVALID_ARG),
+    (dict(wg=None), M.MOE_ERR_INVALID_ARG),
+    (dict(wd=None), M.MOE_ERR_INVALID_ARG),
+    (dict(out=None), M.MOE_ERR_INVALID_ARG),
+    (dict(dt=7), M.MOE_ERR_INVALID_ARG),
+    (dict(out=FAKE), M.MOE_ERR_INVALID_ARG),                       # out aliases x
+    (dict(ws=0), M.MOE_ERR_WORKSPACE),
+    (dict(wsb=1024), M.MOE_ERR_WORKSPACE),
+    (dict(ws=FAKE + (1 << 36) + 64), M.MOE_ERR_WORKSPACE),          # misaligned
+    (dict(out=FAKE + (1 << 36) + 512), M.MOE_ERR_INVALID_ARG),      # out inside the workspace
+    (dict(T=0), M.MOE_OK),
+    (dict(T=0, x=None, out=None, ws=0, wsb=0), M.MOE_OK),
+])
+def test_forward_argument_checks(lib, kw, status):
+    st = _fwd(lib, **kw)
+    assert st == status, (st, lib.moe_last_error_detail().decode())
+    if status != M.MOE_OK:
+        assert len(lib.moe_last_error_detail()) > 0
+    else:
+        assert lib.moe_last_error_detail() == b""
+
+
+def _grouped(lib, E=64, k=6, ng=8, tg=4, shared=(None, None, None), Fs=0, score=0, act=1, T=16, d=64, F=64):
+    need = lib.moe_ffn_workspace_bytes(T, d, F, E, min(k, 16), M.MOE_BF16, Fs)
+    return lib.moe_ffn_forward_grouped(FAKE, FAKE, None, None, FAKE, None, FAKE, None, FAKE, None,
+                                       shared[0], shared[1], shared[2], Fs, T, d, F, E, k, ng, tg, 1, 1.8,
+                                       score, act, 1.702, 7.0, FAKE2, M.MOE_BF16, FAKE + (1 << 36), need,
+                                       None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ng=7), M.MOE_ERR_INVALID_ARG),                  # E % n_group != 0
+    (dict(ng=0), M.MOE_ERR_INVALID_ARG),
+    (dict(tg=9), M.MOE_ERR_INVALID_ARG),                  # topk_group > n_group
+    (dict(tg=0), M.MOE_ERR_INVALID_ARG),
+    (dict(tg=1, k=9), M.MOE_ERR_INVALID_ARG),             # k > topk_group * E / n_group
+    (dict(E=256, ng=128, tg=4, k=6), M.MOE_ERR_UNSUPPORTED),
+    (dict(score=5), M.MOE_ERR_INVALID_ARG),
+    (dict(act=3), M.MOE_ERR_INVALID_ARG),
+    (dict(shared=(FAKE, None, FAKE), Fs=64), M.MOE_ERR_INVALID_ARG),
+    (dict(shared=(FAKE, FAKE, FAKE), Fs=12), M.MOE_ERR_INVALID_ARG),
+    (dict(shared=(FAKE, FAKE, FAKE), Fs=0), M.MOE_ERR_INVALID_ARG),
+])
+def test_grouped_argument_checks(lib, kw, status):
+    st = _grouped(lib, **kw)
+    assert st == status, (st, lib.moe_last_error_detail().decode())
+
+
+def test_mxfp4_argument_checks(lib):
+    def call(d=64, F=64, codes=FAKE):
+        need = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0)
+        return lib.moe_ffn_forward_mxfp4(FAKE, FAKE, None, codes, FAKE, None, FAKE, FAKE, None, FAKE, FAKE,
+                                         None, 16, d, F, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36), need,
+                                         None, None)
+    assert call(d=48) == M.MOE_ERR_UNSUPPORTED
+    assert call(F=40) == M.MOE_ERR_UNSUPPORTED
+    assert call(codes=None) == M.MOE_ERR_INVALID_ARG
