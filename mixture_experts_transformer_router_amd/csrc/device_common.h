@@ -78,3 +78,31 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// ---- gfx950 MFMA operands -------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D = A (16 x 32) * B (32 x 16) + C, bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l % 16), k = 8 (l / 16) .. +7 and B column (l % 16),
+// the same k; it receives D rows 4 (l / 16) .. +3 of column (l % 16).
+__device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+// Streaming (read-once) variant: non-temporal hint so weights do not evict
+// reusable lines from the caches.
+__device__ __forceinline__ bf16x8_t load_bf16x8_stream(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+__device__ __forceinline__ bf16x8_t zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+}
+
+}  // namespace moe

@@ -130,14 +130,17 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
     e = launch_permute(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
+  // Expert stages: weight streaming on MFMA for a few tokens (every expert
+  // then holds at most kDecodeMaxTokens rows), tiled GEMMs otherwise.
+  const bool decode = L.dt == MOE_BF16 && L.wfmt == WF_BF16 && L.T <= kDecodeMaxTokens;
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
-    e = launch_gate_up(L, W, s);
+    e = decode ? launch_gate_up_decode(L, W, s) : launch_gate_up(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
     StageTimer tm(s, MOE_STAGE_DOWN);
-    e = launch_down(L, W, s);
+    e = decode ? launch_down_decode(L, W, s) : launch_down(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
   {
@@ -153,7 +156,7 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
 size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   const size_t P = (size_t)L.T * L.k;
   const size_t rows = (size_t)L.rows_all();
-  const size_t nblk = ((size_t)L.T + kRouteTokens - 1) / kRouteTokens;
+  const size_t nblk = ((size_t)L.T + kMinRouteTokens - 1) / kMinRouteTokens;
   const size_t Eall = (size_t)L.n_experts_all();
   size_t off = 0;
   char* base = static_cast<char*>(ws);

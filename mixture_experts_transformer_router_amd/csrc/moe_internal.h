@@ -12,8 +12,14 @@ namespace moe {
 // Storage format of the expert weights.
 enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2 };
 
-// Tokens handled by one block of the route and permute kernels.
-constexpr int kRouteTokens = 64;
+// Tokens handled by one block of the permute kernel.  Router blocks cover
+// route_block_tokens() tokens, a divisor of this.
+constexpr int kPermuteTokens = 64;
+// Smallest router block (rows of the per-block expert count table).
+constexpr int kMinRouteTokens = 16;
+// Largest token count that takes the weight-streaming (decode) expert path:
+// an expert then has at most this many rows, one MFMA column tile.
+constexpr int kDecodeMaxTokens = 16;
 // Rows per M-tile of the tiled grouped GEMMs (the permute kernel writes the
 // per-expert tile prefix for this size).
 constexpr int kTileM = 64;
@@ -77,11 +83,15 @@ struct Work {
 // size only).  Returns (size_t)-1 for sizes it cannot represent.
 size_t carve_workspace(const Layer& L, void* ws, Work* W);
 
+int route_block_tokens(const Layer& L);
+
 // Kernel launchers (each enqueues one kernel on `s`).
 hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_gate_up(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
 
 }  // namespace moe

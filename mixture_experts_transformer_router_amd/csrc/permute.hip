@@ -6,10 +6,10 @@
 // inverse (pos) used to return to token order.  With a shared expert, its T
 // rows (one per token, in token order) follow all routed rows.
 //
-// One block per route block (64 tokens, 64*k pairs).  Each block
-//   1. sums the per-block expert counts written by the router: totals give the
-//      expert offsets (exclusive prefix sum), the counts of earlier blocks give
-//      this block's first row inside each expert;
+// One block per 64 tokens (64*k pairs).  Each block
+//   1. sums the per-router-block expert counts: totals give the expert
+//      offsets (exclusive prefix sum), the counts of earlier tokens give this
+//      block's first row inside each expert;
 //   2. ranks its own pairs stably: per wavefront, the lanes routed to the same
 //      expert are found with 9 ballots over the expert id bits; earlier
 //      wavefronts and rounds are added through small LDS counters;
@@ -27,8 +27,10 @@ constexpr int kMaxE = 257;  // 256 routed experts + shared
 
 struct PermuteArgs {
   const int32_t* idx;
-  const int32_t* hist;
-  int T, k, E, nblk, shared;
+  const int32_t* hist;  // [n_hist, E] expert counts per router block
+  int n_hist;           // router blocks
+  int hist_per_block;   // router blocks per permute block (64 / router block tokens)
+  int T, k, E, shared;
   int tile_m;
   int32_t* offsets;
   int32_t* tile_prefix;
@@ -52,10 +54,11 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
 
   for (int e = tid; e < E; e += kThreads) {
     int tot = 0, bef = 0;
-    for (int i = 0; i < a.nblk; ++i) {
+    const int first_own = b * a.hist_per_block;
+    for (int i = 0; i < a.n_hist; ++i) {
       int c = a.hist[(size_t)i * E + e];
       tot += c;
-      if (i < b) bef += c;
+      if (i < first_own) bef += c;
     }
     total[e] = tot;
     before[e] = bef;
@@ -88,8 +91,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
     }
   }
 
-  const int t_begin = b * kRouteTokens;
-  const int t_end = min(a.T, t_begin + kRouteTokens);
+  const int t_begin = b * kPermuteTokens;
+  const int t_end = min(a.T, t_begin + kPermuteTokens);
   const int p_begin = t_begin * a.k;
   const int n = (t_end - t_begin) * a.k;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -141,13 +144,16 @@ hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s) {
   PermuteArgs a;
   a.idx = W.idx; a.hist = W.hist;
   a.T = L.T; a.k = L.k; a.E = L.E;
-  a.nblk = (L.T + kRouteTokens - 1) / kRouteTokens;
+  const int rb = route_block_tokens(L);
+  a.n_hist = (L.T + rb - 1) / rb;
+  a.hist_per_block = kPermuteTokens / rb;
+  const int nblk = (L.T + kPermuteTokens - 1) / kPermuteTokens;
   a.shared = L.has_shared() ? 1 : 0;
   a.tile_m = kTileM;
   a.offsets = W.offsets; a.tile_prefix = W.tile_prefix;
   a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
   a.user_offsets = L.routing.expert_offsets; a.user_sorted = L.routing.sorted_pair;
-  permute_kernel<<<a.nblk, kThreads, 0, s>>>(a);
+  permute_kernel<<<nblk, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -1,15 +1,18 @@
 // Router: logits, expert choice and routing weights, plus per-block expert
 // counts for the permutation.
 //
-// Logits l[t,e] = sum_i x[t,i] Wr[e,i] + br[e] are accumulated in fp32 over i
-// in increasing order (router kernel and bias: MaxText GPT-OSS weight mapping,
-// "MoE Router"; glm4_moe_lite.go, MoEGate.Forward).  Each block owns 64
-// tokens; its 256 threads hold a [64 tokens x E] tile of logits in registers
-// while the input dimension streams through LDS in chunks of 32.
+// Logits l[t,e] = sum_i x[t,i] Wr[e,i] + br[e], accumulated in fp32 (router
+// kernel and bias: MaxText GPT-OSS weight mapping, "MoE Router";
+// glm4_moe_lite.go, MoEGate.Forward).
+//   bf16: a [16 tokens x 16 experts] tile per MFMA; the block's 8 wavefronts
+//         split the input dimension and their partial tiles are added in
+//         wavefront order (deterministic).
+//   fp32: 64 tokens per block on the vector ALUs, the input dimension
+//         streaming through LDS in chunks of 32.
 //
-// Choice: one wavefront per token at a time; lane l holds the scores of
-// experts l, l+64, ...; k rounds of a wave arg-max by (score desc, index asc)
-// pick the experts best first.
+// Choice: one wavefront per token; lane l holds the scores of experts l,
+// l+64, ...; k rounds of a wave arg-max by (score desc, index asc) pick the
+// experts best first.
 //   GPT-OSS:  score = logit, w = softmax over the k chosen logits.
 //   grouped:  s = softmax(l) over E (or sigmoid(l)), s' = s + correction bias,
 //             group score = max s' in each of n_group contiguous groups, the
@@ -21,9 +24,6 @@
 
 namespace moe {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kChunk = 32;
 
 struct RouteArgs {
   const void* x;
@@ -40,42 +40,222 @@ struct RouteArgs {
   float* user_w;
 };
 
-// EPT = experts per thread (E <= 4 * EPT); TIn = float or uint16_t (bf16).
-template <typename TIn, int EPT>
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
-  __shared__ float xs[kRouteTokens][kChunk + 1];
+// Choose the experts of token t from its logits row `lg` (LDS, E entries;
+// overwritten with selection scores on the grouped path) with one wavefront.
+// VPL = experts per lane (E <= 64 * VPL).  Adds the chosen experts to `cnt`.
+template <int VPL>
+__device__ void choose_experts(const RouteArgs& a, float* lg, int t, int lane, int* cnt) {
+  const int E = a.E;
+  float sc[VPL];    // selection score
+  float base[VPL];  // weight source (logit for GPT-OSS, s for grouped)
+  bool allowed[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane + 64 * v;
+    const float l = e < E ? lg[e] : -INFINITY;
+    sc[v] = l != l ? -INFINITY : l;  // NaN never outranks a number
+    allowed[v] = e < E;
+  }
+
+  if (a.grouped) {
+    if (a.score == MOE_SCORE_SOFTMAX) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) m = fmaxf(m, sc[v]);
+      m = wave_max(m);
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        base[v] = allowed[v] ? expf(sc[v] - m) : 0.f;
+        s += base[v];
+      }
+      s = wave_sum(s);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) base[v] = base[v] / s;
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) base[v] = allowed[v] ? 1.0f / (1.0f + expf(-sc[v])) : 0.f;
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + 64 * v;
+      const float sel = base[v] + ((a.e_bias != nullptr && e < E) ? a.e_bias[e] : 0.f);
+      sc[v] = (allowed[v] && sel == sel) ? sel : -INFINITY;
+      if (e < E) lg[e] = sc[v];  // read back per group below (same wavefront)
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // group scores: lane g < n_group takes the max over its contiguous group
+    const int gsz = E / a.n_group;
+    float gscore = -INFINITY;
+    int gidx = kNoIndex;
+    if (lane < a.n_group) {
+      for (int i = 0; i < gsz; ++i) gscore = fmaxf(gscore, lg[lane * gsz + i]);
+      gidx = lane;
+    }
+    uint64_t kept = 0;
+    for (int j = 0; j < a.topk_group; ++j) {
+      float bv = gscore;
+      int bi = gidx;
+      wave_argmax(bv, bi);
+      kept |= 1ull << bi;
+      if (lane == bi) { gscore = -INFINITY; gidx = kNoIndex; }
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + 64 * v;
+      if (e < E && !((kept >> (e / gsz)) & 1ull)) allowed[v] = false;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) base[v] = sc[v];
+  }
+
+  // k rounds of arg-max over the allowed experts; the host guarantees at
+  // least k allowed experts, so every round finds one (bi < E).
+  int my_e = -1;
+  float my_base = 0.f, first_base = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = kNoIndex;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + 64 * v;
+      if (allowed[v] && precedes(sc[v], e, bv, bi)) { bv = sc[v]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    float bb = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      if (lane + 64 * v == bi) { allowed[v] = false; bb = base[v]; }
+    }
+    bb = __shfl(bb, bi & 63, 64);
+    if (j == 0) first_base = bb;
+    if (lane == j) { my_e = bi; my_base = bb; }
+  }
+  float wt;
+  if (!a.grouped) {
+    const float ex = lane < a.k ? expf(my_base - first_base) : 0.f;
+    wt = ex / wave_sum(ex);
+  } else {
+    wt = lane < a.k ? my_base : 0.f;
+    if (a.k > 1 && a.norm) wt = wt / wave_sum(wt);
+    wt *= a.rsf;
+  }
+  if (lane < a.k) {
+    const size_t o = (size_t)t * a.k + lane;
+    a.idx[o] = my_e;
+    a.w[o] = wt;
+    if (a.user_idx) a.user_idx[o] = my_e;
+    if (a.user_w) a.user_w[o] = wt;
+    atomicAdd(&cnt[my_e], 1);
+  }
+}
+
+// ---- bf16: MFMA logits -----------------------------------------------------
+constexpr int kMfmaTokens = 16;
+constexpr int kMfmaWaves = 8;
+
+// EG = groups of 16 experts (E <= 16 * EG).
+template <int EG>
+__global__ __launch_bounds__(64 * kMfmaWaves) void route_mfma_kernel(RouteArgs a) {
+  constexpr int EP = 16 * EG;
+  __shared__ float lg[kMfmaTokens][EP + 1];
+  __shared__ int cnt[EP];
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int t0 = blockIdx.x * kMfmaTokens;
+  const int E = a.E, d = a.d;
+  for (int e = tid; e < EP; e += 64 * kMfmaWaves) cnt[e] = 0;
+
+  const int tok = t0 + (lane & 15);
+  const int kg = lane >> 4;
+  const bool tok_ok = tok < a.T;
+  const uint16_t* xr = x + (size_t)(tok_ok ? tok : 0) * d;
+  f32x4_t acc[EG];
+#pragma unroll
+  for (int g = 0; g < EG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int steps = (d + 31) / 32;
+#pragma unroll 2
+  for (int s = wv; s < steps; s += kMfmaWaves) {
+    const int k = 32 * s + 8 * kg;
+    const bool k_ok = k < d;  // d % 8 == 0: a lane's 8 elements are all in or all out
+    const bf16x8_t av = (tok_ok && k_ok) ? load_bf16x8(xr + k) : zero_bf16x8();
+#pragma unroll
+    for (int g = 0; g < EG; ++g) {
+      const int e = 16 * g + (lane & 15);
+      const bf16x8_t bv = (e < E && k_ok) ? load_bf16x8(wr + (size_t)e * d + k) : zero_bf16x8();
+      acc[g] = mfma_16x16x32(av, bv, acc[g]);
+    }
+  }
+  // partial tiles added in wavefront order
+  for (int w = 0; w < kMfmaWaves; ++w) {
+    if (wv == w) {
+#pragma unroll
+      for (int g = 0; g < EG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * kg + r, col = 16 * g + (lane & 15);
+          lg[row][col] = (w == 0) ? acc[g][r] : lg[row][col] + acc[g][r];
+        }
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < kMfmaTokens * E; i += 64 * kMfmaWaves) {
+    const int r = i / E, e = i % E;
+    if (a.br) lg[r][e] += bf16_to_f32(static_cast<const uint16_t*>(a.br)[e]);
+  }
+  __syncthreads();
+  constexpr int VPL = (EP + 63) / 64;
+  for (int r = wv; r < kMfmaTokens; r += kMfmaWaves) {
+    const int t = t0 + r;
+    if (t < a.T) choose_experts<VPL>(a, lg[r], t, lane, cnt);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 64 * kMfmaWaves) a.hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// ---- fp32: vector-ALU logits -------------------------------------------------
+constexpr int kValuTokens = 64;
+constexpr int kValuThreads = 256;
+constexpr int kChunk = 32;
+
+// EPT = experts per thread (E <= 4 * EPT).
+template <int EPT>
+__global__ __launch_bounds__(kValuThreads) void route_valu_kernel(RouteArgs a) {
+  __shared__ float xs[kValuTokens][kChunk + 1];
   __shared__ float ws[4 * EPT][kChunk + 1];
-  __shared__ float lg[kRouteTokens][4 * EPT + 1];
+  __shared__ float lg[kValuTokens][4 * EPT + 1];
   __shared__ int cnt[4 * EPT];
 
-  const TIn* x = static_cast<const TIn*>(a.x);
-  const TIn* wr = static_cast<const TIn*>(a.wr);
+  const float* x = static_cast<const float*>(a.x);
+  const float* wr = static_cast<const float*>(a.wr);
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kRouteTokens;
+  const int t0 = blockIdx.x * kValuTokens;
   const int my_tok = tid & 63;
   const int egrp = tid >> 6;  // experts egrp, egrp + 4, ...
   const int E = a.E, d = a.d;
 
-  for (int e = tid; e < 4 * EPT; e += kThreads) cnt[e] = 0;
-
+  for (int e = tid; e < 4 * EPT; e += kValuThreads) cnt[e] = 0;
   float acc[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) acc[j] = 0.f;
 
   for (int c0 = 0; c0 < d; c0 += kChunk) {
-    for (int i = tid; i < kRouteTokens * kChunk; i += kThreads) {
-      int r = i / kChunk, c = i % kChunk;
-      int t = t0 + r;
-      xs[r][c] = (t < a.T && c0 + c < d) ? load_f32(x, (size_t)t * d + c0 + c) : 0.f;
+    for (int i = tid; i < kValuTokens * kChunk; i += kValuThreads) {
+      const int r = i / kChunk, c = i % kChunk, t = t0 + r;
+      xs[r][c] = (t < a.T && c0 + c < d) ? x[(size_t)t * d + c0 + c] : 0.f;
     }
-    for (int i = tid; i < 4 * EPT * kChunk; i += kThreads) {
-      int e = i / kChunk, c = i % kChunk;
-      ws[e][c] = (e < E && c0 + c < d) ? load_f32(wr, (size_t)e * d + c0 + c) : 0.f;
+    for (int i = tid; i < 4 * EPT * kChunk; i += kValuThreads) {
+      const int e = i / kChunk, c = i % kChunk;
+      ws[e][c] = (e < E && c0 + c < d) ? wr[(size_t)e * d + c0 + c] : 0.f;
     }
     __syncthreads();
 #pragma unroll 4
     for (int c = 0; c < kChunk; ++c) {
-      float xv = xs[my_tok][c];
+      const float xv = xs[my_tok][c];
 #pragma unroll
       for (int j = 0; j < EPT; ++j) acc[j] = fmaf(xv, ws[egrp + 4 * j][c], acc[j]);
     }
@@ -83,146 +263,24 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
-    int e = egrp + 4 * j;
-    float b = (a.br != nullptr && e < E) ? load_f32(static_cast<const TIn*>(a.br), e) : 0.f;
+    const int e = egrp + 4 * j;
+    const float b = (a.br != nullptr && e < E) ? static_cast<const float*>(a.br)[e] : 0.f;
     lg[my_tok][e] = acc[j] + b;
   }
   __syncthreads();
-
-  // ---- choice: wave `wv` handles tokens wv, wv+4, ...
   const int lane = tid & 63, wv = tid >> 6;
-  constexpr int VPL = (4 * EPT + 63) / 64;  // values per lane
-  for (int r = wv; r < kRouteTokens; r += 4) {
+  constexpr int VPL = (4 * EPT + 63) / 64;
+  for (int r = wv; r < kValuTokens; r += 4) {
     const int t = t0 + r;
-    if (t >= a.T) break;
-    float sc[VPL];     // selection score
-    float base[VPL];   // weight source (logit for GPT-OSS, s for grouped)
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      int e = lane + 64 * v;
-      const float l = e < E ? lg[r][e] : -INFINITY;
-      sc[v] = l != l ? -INFINITY : l;  // NaN never outranks a number
-    }
-    bool allowed[VPL];
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) allowed[v] = (lane + 64 * v) < E;
-
-    if (a.grouped) {
-      // scores
-      if (a.score == MOE_SCORE_SOFTMAX) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) m = fmaxf(m, sc[v]);
-        m = wave_max(m);
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          base[v] = allowed[v] ? expf(sc[v] - m) : 0.f;
-          s += base[v];
-        }
-        s = wave_sum(s);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) base[v] = base[v] / s;
-      } else {
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) base[v] = allowed[v] ? 1.0f / (1.0f + expf(-sc[v])) : 0.f;
-      }
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        int e = lane + 64 * v;
-        float sel = base[v] + ((a.e_bias != nullptr && e < E) ? a.e_bias[e] : 0.f);
-        sc[v] = (allowed[v] && sel == sel) ? sel : -INFINITY;
-        if (e < E) lg[r][e] = sc[v];  // selection scores, read back per group below
-      }
-      // group scores: lane g < n_group takes the max over its contiguous group
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      const int gsz = E / a.n_group;
-      float gscore = -INFINITY;
-      int gidx = kNoIndex;
-      if (lane < a.n_group) {
-        for (int i = 0; i < gsz; ++i) gscore = fmaxf(gscore, lg[r][lane * gsz + i]);
-        gidx = lane;
-      }
-      uint64_t kept = 0;
-      for (int j = 0; j < a.topk_group; ++j) {
-        float bv = gscore;
-        int bi = gidx;
-        wave_argmax(bv, bi);
-        kept |= 1ull << bi;
-        if (lane == bi) { gscore = -INFINITY; gidx = kNoIndex; }
-      }
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        int e = lane + 64 * v;
-        if (e < E && !((kept >> (e / gsz)) & 1ull)) allowed[v] = false;
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) base[v] = sc[v];
-    }
-
-    // k rounds of arg-max over the allowed experts
-    int my_e = -1;
-    float my_base = 0.f, first_base = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      float bv = -INFINITY;
-      int bi = kNoIndex;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        int e = lane + 64 * v;
-        if (allowed[v] && precedes(sc[v], e, bv, bi)) { bv = sc[v]; bi = e; }
-      }
-      wave_argmax(bv, bi);
-      // the host guarantees at least k allowed experts, so bi < E here
-      // owner lane of expert bi retires it and broadcasts its weight source
-      float bb = 0.f;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        if (lane + 64 * v == bi) { allowed[v] = false; bb = base[v]; }
-      }
-      bb = __shfl(bb, bi & 63, 64);
-      if (j == 0) first_base = bb;
-      if (lane == j) { my_e = bi; my_base = bb; }
-    }
-    // weights
-    float wv_ = 0.f;
-    if (!a.grouped) {
-      float ex = lane < a.k ? expf(my_base - first_base) : 0.f;
-      float s = wave_sum(ex);
-      wv_ = ex / s;
-    } else {
-      wv_ = lane < a.k ? my_base : 0.f;
-      if (a.k > 1 && a.norm) {
-        float s = wave_sum(wv_);
-        wv_ = wv_ / s;
-      }
-      wv_ *= a.rsf;
-    }
-    if (lane < a.k) {
-      size_t o = (size_t)t * a.k + lane;
-      a.idx[o] = my_e;
-      a.w[o] = wv_;
-      if (a.user_idx) a.user_idx[o] = my_e;
-      if (a.user_w) a.user_w[o] = wv_;
-      atomicAdd(&cnt[my_e], 1);
-    }
+    if (t < a.T) choose_experts<VPL>(a, lg[r], t, lane, cnt);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads) a.hist[(size_t)blockIdx.x * E + e] = cnt[e];
-}
-
-template <typename TIn>
-hipError_t launch_t(const RouteArgs& a, int nblk, hipStream_t s) {
-  if (a.E <= 8) route_kernel<TIn, 2><<<nblk, kThreads, 0, s>>>(a);
-  else if (a.E <= 16) route_kernel<TIn, 4><<<nblk, kThreads, 0, s>>>(a);
-  else if (a.E <= 32) route_kernel<TIn, 8><<<nblk, kThreads, 0, s>>>(a);
-  else if (a.E <= 64) route_kernel<TIn, 16><<<nblk, kThreads, 0, s>>>(a);
-  else route_kernel<TIn, 64><<<nblk, kThreads, 0, s>>>(a);
-  return hipGetLastError();
+  for (int e = tid; e < E; e += kValuThreads) a.hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
 }  // namespace
+
+int route_block_tokens(const Layer& L) { return L.dt == MOE_F32 ? kValuTokens : kMfmaTokens; }
 
 hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
   RouteArgs a;
@@ -232,8 +290,23 @@ hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
   a.norm = L.norm; a.score = L.score; a.rsf = L.rsf;
   a.idx = W.idx; a.w = W.w; a.hist = W.hist;
   a.user_idx = L.routing.topk_idx; a.user_w = L.routing.topk_w;
-  int nblk = (L.T + kRouteTokens - 1) / kRouteTokens;
-  return L.dt == MOE_F32 ? launch_t<float>(a, nblk, s) : launch_t<uint16_t>(a, nblk, s);
+  const int tb = route_block_tokens(L);
+  const int nblk = (L.T + tb - 1) / tb;
+  if (L.dt == MOE_F32) {
+    if (L.E <= 8) route_valu_kernel<2><<<nblk, kValuThreads, 0, s>>>(a);
+    else if (L.E <= 16) route_valu_kernel<4><<<nblk, kValuThreads, 0, s>>>(a);
+    else if (L.E <= 32) route_valu_kernel<8><<<nblk, kValuThreads, 0, s>>>(a);
+    else if (L.E <= 64) route_valu_kernel<16><<<nblk, kValuThreads, 0, s>>>(a);
+    else route_valu_kernel<64><<<nblk, kValuThreads, 0, s>>>(a);
+  } else {
+    const dim3 blk(64 * kMfmaWaves);
+    if (L.E <= 16) route_mfma_kernel<1><<<nblk, blk, 0, s>>>(a);
+    else if (L.E <= 32) route_mfma_kernel<2><<<nblk, blk, 0, s>>>(a);
+    else if (L.E <= 64) route_mfma_kernel<4><<<nblk, blk, 0, s>>>(a);
+    else if (L.E <= 128) route_mfma_kernel<8><<<nblk, blk, 0, s>>>(a);
+    else route_mfma_kernel<16><<<nblk, blk, 0, s>>>(a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -127,9 +127,10 @@ def test_zero_tokens_is_noop_and_errors_leave_out_untouched():
     _say("[case] errors")
     t = LY.to_device(I.make_inputs(w), DEV)
     out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device=DEV)
+    ws = LY.workspace_for(w, DEV)
     with pytest.raises(moe_ffn.MoeError) as ei:
         moe_ffn.forward(t["x"], t["router_w"], t["router_b"], t["w_gate"], t["b_gate"], t["w_up"],
-                        t["b_up"], t["w_down"], t["b_down"], k=5, out=out)
+                        t["b_up"], t["w_down"], t["b_down"], k=5, out=out, workspace=ws)
     assert ei.value.status == moe_ffn.MOE_ERR_INVALID_ARG
     small_ws = torch.empty(256, dtype=torch.uint8, device=DEV)
     with pytest.raises(moe_ffn.MoeError) as ei:
