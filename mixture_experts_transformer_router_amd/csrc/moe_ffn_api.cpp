@@ -131,16 +131,22 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
   // Expert stages: weight streaming on MFMA for a few tokens (every expert
-  // then holds at most kDecodeMaxTokens rows), tiled GEMMs otherwise.
-  const bool decode = L.dt == MOE_BF16 && L.wfmt == WF_BF16 && L.T <= kDecodeMaxTokens;
+  // then holds at most kDecodeMaxTokens rows), grouped MFMA GEMMs for bf16 /
+  // MXFP4 otherwise, vector-ALU tiles for fp32.
+  enum { kDecode, kMfma, kTiled } path;
+  if (L.dt == MOE_F32) path = kTiled;
+  else if (L.wfmt == WF_BF16 && L.T <= kDecodeMaxTokens) path = kDecode;
+  else path = kMfma;
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
-    e = decode ? launch_gate_up_decode(L, W, s) : launch_gate_up(L, W, s);
+    e = path == kDecode ? launch_gate_up_decode(L, W, s)
+        : path == kMfma ? launch_gate_up_mfma(L, W, s) : launch_gate_up(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
     StageTimer tm(s, MOE_STAGE_DOWN);
-    e = decode ? launch_down_decode(L, W, s) : launch_down(L, W, s);
+    e = path == kDecode ? launch_down_decode(L, W, s)
+        : path == kMfma ? launch_down_mfma(L, W, s) : launch_down(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
   {
@@ -170,6 +176,7 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   W->hist = static_cast<int32_t*>(take(nblk * L.E * 4));
   W->offsets = static_cast<int32_t*>(take((Eall + 1) * 4));
   W->tile_prefix = static_cast<int32_t*>(take((Eall + 1) * 4));
+  W->tile_prefix_big = static_cast<int32_t*>(take((Eall + 1) * 4));
   W->sorted_pair = static_cast<int32_t*>(take(rows * 4));
   W->row_token = static_cast<int32_t*>(take(rows * 4));
   W->pos = static_cast<int32_t*>(take(P * 4));

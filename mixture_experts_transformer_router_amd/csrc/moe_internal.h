@@ -23,6 +23,8 @@ constexpr int kDecodeMaxTokens = 16;
 // Rows per M-tile of the tiled grouped GEMMs (the permute kernel writes the
 // per-expert tile prefix for this size).
 constexpr int kTileM = 64;
+// Rows per M-tile of the MFMA grouped GEMMs.
+constexpr int kTileMBig = 256;
 
 // One call's arguments after validation.
 struct Layer {
@@ -71,7 +73,8 @@ struct Work {
   float* w = nullptr;              // [T*k] routing weights
   int32_t* hist = nullptr;         // [n_route_blocks * E] per-block expert counts
   int32_t* offsets = nullptr;      // [E_all + 1] row offsets of each expert (shared last)
-  int32_t* tile_prefix = nullptr;  // [E_all + 1] first M-tile of each expert
+  int32_t* tile_prefix = nullptr;  // [E_all + 1] first 64-row M-tile of each expert
+  int32_t* tile_prefix_big = nullptr;  // [E_all + 1] first 256-row M-tile of each expert
   int32_t* sorted_pair = nullptr;  // [rows_all] pair id of each sorted row (shared rows: -1)
   int32_t* row_token = nullptr;    // [rows_all] token of each sorted row
   int32_t* pos = nullptr;          // [T*k] sorted row of each pair
@@ -92,6 +95,8 @@ hipError_t launch_gate_up(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
 
 }  // namespace moe

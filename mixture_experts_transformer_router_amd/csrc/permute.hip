@@ -31,9 +31,10 @@ struct PermuteArgs {
   int n_hist;           // router blocks
   int hist_per_block;   // router blocks per permute block (64 / router block tokens)
   int T, k, E, shared;
-  int tile_m;
+  int tile_m, tile_m_big;
   int32_t* offsets;
   int32_t* tile_prefix;
+  int32_t* tile_prefix_big;
   int32_t* sorted_pair;
   int32_t* row_token;
   int32_t* pos;
@@ -81,13 +82,16 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
     }
     if (a.shared && tid == 0) a.offsets[E + 1] = off[E] + a.T;
     if (tid == 0) {
-      int acc = 0;
+      int acc = 0, acc_big = 0;
       for (int e = 0; e < Eall; ++e) {
         a.tile_prefix[e] = acc;
-        int c = e < E ? total[e] : a.T;
+        a.tile_prefix_big[e] = acc_big;
+        const int c = e < E ? total[e] : a.T;
         acc += (c + a.tile_m - 1) / a.tile_m;
+        acc_big += (c + a.tile_m_big - 1) / a.tile_m_big;
       }
       a.tile_prefix[Eall] = acc;
+      a.tile_prefix_big[Eall] = acc_big;
     }
   }
 
@@ -150,7 +154,8 @@ hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s) {
   const int nblk = (L.T + kPermuteTokens - 1) / kPermuteTokens;
   a.shared = L.has_shared() ? 1 : 0;
   a.tile_m = kTileM;
-  a.offsets = W.offsets; a.tile_prefix = W.tile_prefix;
+  a.tile_m_big = kTileMBig;
+  a.offsets = W.offsets; a.tile_prefix = W.tile_prefix; a.tile_prefix_big = W.tile_prefix_big;
   a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
   a.user_offsets = L.routing.expert_offsets; a.user_sorted = L.routing.sorted_pair;
   permute_kernel<<<nblk, kThreads, 0, s>>>(a);
