@@ -74,6 +74,22 @@ def algorithmic_gate_up(w, counts):
     return nbytes, flops, len(active)
 
 
+def recorded_traffic(w, workload_name):
+    """HBM bytes per launch of the gate|up kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs recorded in profiles/traffic.json
+    (calibrated on a plain copy); None when none was recorded for this
+    workload or the kernel's sources changed since."""
+    import json
+    from mixture_experts_transformer_router_amd import prof_summary as PS
+    path = PS.TRAFFIC_JSON
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload_name)
+    if not rec or rec.get("source_sha256") != PS.source_digest(rec["kernel"]):
+        return None
+    return rec["bytes"]
+
+
 def cpu_baseline(w, a, budget_s):
     """Time the float64 oracle on a bounded sample of the workload."""
     import numpy as np
@@ -165,7 +181,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": flops / gu_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(w, args.workload)
     roof["kernel"] = "gate_up"
     roof["kernel_avg_us"] = gu_avg_s * 1e6
 

@@ -8,13 +8,15 @@
 // SwitchMLP.Forward: per-expert gathered products, activation, down product;
 // SharedExperts.Forward for the shared expert, handled as expert E.)
 //
-// Block tile 256 rows x 256 columns, K staged 64 at a time through two LDS
-// buffers: the copies of tile k+1 (global -> LDS directly, no registers) are
-// in flight while tile k is multiplied.
-// 4 wavefronts, each owning a 128 x 128 sub-tile as 4 x 4 results of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulators).  LDS rows are 128 bytes (64
-// bf16); the 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the
-// 16-byte fragment reads of 8 consecutive rows hit 8 different bank groups.
+// Block tile 256 rows x (64 NJ) columns; K is staged BK at a time through NS
+// LDS buffers.  Global -> LDS copies go straight into LDS (no registers) and
+// run NS - 1 tiles ahead of the multiply, so the latency of a copy is covered
+// by NS - 1 tiles of MFMA work.
+// 4 wavefronts, each owning a 128 x (32 NJ) sub-tile as 4 x NJ results of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators).  An LDS row holds BK bf16;
+// its 16-byte chunks are stored XOR-swizzled by the row's position within a
+// 128-byte line group, so the 16-byte fragment reads of 8 consecutive rows
+// hit 8 different bank groups.
 //
 // gate|up: the block's 256 columns are 128 gate and the same 128 up rows of
 // the expert, interleaved by 32 (gate, up, gate, up within each wavefront), so
@@ -22,6 +24,8 @@
 // in registers.  Token rows are gathered while loading (no permuted copy of
 // x).  MXFP4 weights: the loader decodes e2m1 codes with their e8m0 block
 // scale to bf16 in LDS (exact: every value is a bf16 number).
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -29,9 +33,21 @@ namespace moe {
 namespace {
 
 constexpr int BM = kTileMBig;  // 256
-constexpr int BN = 256;
-constexpr int BK = 64;
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;       // MI355X: workgroup i runs on XCD i % 8
+// Tuning knobs (compile-time; -D overrides for sweeps).
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 4
+#endif
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 5
+#endif
+constexpr int kGroupM = MOE_GEMM_GROUP_M;  // row tiles walked together within an XCD
+constexpr int kBK = MOE_GEMM_BK;           // K elements per LDS stage
+constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages (5 x 32 KB = the whole 160 KB)
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -67,7 +83,39 @@ struct MfmaArgs {
   float alpha, limit;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// Element offset of 16-byte chunk `chunk` of LDS row `row` (rows of BK bf16).
+// The chunk is XOR-ed with a row hash chosen so that the 16-byte reads of
+// any 8 consecutive rows (same logical chunk) fall in 8 distinct 16-byte
+// slots of a 128-byte bank window, and those of any 16 consecutive rows
+// (32-aligned groups, as the fragment reads use) in 16 distinct slots of a
+// 256-byte window: conflict-free whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per clock.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  constexpr int CPR = BK / 8;  // chunks per row: 4 (BK 32) or 8 (BK 64)
+  int h;
+  if constexpr (CPR == 4) h = ((row >> 1) ^ (row >> 3)) & 3;
+  else h = (row ^ (row >> 3)) & 7;
+  return row * BK + ((chunk ^ h) << 3);
+}
+
+// Workgroup barrier for the copy pipeline.  __syncthreads() would also drain
+// every outstanding global -> LDS copy (its release fence covers them), which
+// would serialise the pipeline; here each wavefront first waits for its own
+// LDS stores and for the copies it needs (wait_vmcnt), then meets the others.
+// The asm's memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most n vector-memory operations of this wavefront are
+// outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // 8 e2m1 codes (one 32-bit word, element 0 in the low nibble) times the block
 // scale 2^(s - 127) -> 8 bf16.
@@ -87,13 +135,39 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, uint32_t s) {
   return u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
-template <int WF, bool GATED>
+// NJ = 32-column result tiles per wavefront (block columns BN = 64 NJ).
+// NJ = 32-column result tiles per wavefront (block columns BN = 64 NJ);
+// BK = K elements per stage; NS = LDS stages.
+template <int WF, bool GATED, int NJ, int BK, int NS>
 __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
-  __shared__ uint16_t lds[2][2][BM * BK];  // [stage][A | B] -- 128 KB
+  constexpr int BN = 64 * NJ;
+  constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
+  constexpr int SEG_ROWS = 1024 / (2 * BK);  // rows per 1 KB copy segment
+  constexpr int RA = BM * CPR / kThreads; // copy rounds per stage, A
+  constexpr int RB = BN * CPR / kThreads; // copy rounds per stage, B (dense)
+  constexpr int R = RA + (WF == WF_MXFP4 ? 0 : RB);
+  static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
+  // the copies of tile kt+1 must be in flight before tile kt's last step
+  static_assert(NS >= 3, "the pipeline needs at least 3 LDS stages");
+  static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "copy rounds");
+  __shared__ uint16_t lds[NS][2][BM * BK];  // [stage][A | B]
 
-  const int m_tile = blockIdx.x / a.n_tiles;
-  const int n_tile = blockIdx.x % a.n_tiles;
-  if (m_tile >= a.tile_prefix[a.E_all]) return;
+  // Tile order.  The real number of row tiles is known only on the device;
+  // every block reads it and the blocks of XCD x take the x-th contiguous
+  // share of the tiles, walked kGroupM row tiles at a time, so the blocks
+  // resident on one XCD reuse each other's A and B tiles through its L2.
+  const int total_m = a.tile_prefix[a.E_all];
+  const int total = total_m * a.n_tiles;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int share = (total + kXcds - 1) / kXcds;
+  const int L = xcd * share + j;
+  if (j >= share || L >= total) return;
+  const int group = L / (kGroupM * a.n_tiles);
+  const int first_m = group * kGroupM;
+  const int gm = min(kGroupM, total_m - first_m);
+  const int rr = L - group * kGroupM * a.n_tiles;
+  const int m_tile = first_m + rr % gm;
+  const int n_tile = rr / gm;
   int lo = 0, hi = a.E_all - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -111,44 +185,47 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
 
-  // ---- loaders.  Global -> LDS copies go straight into LDS (16 bytes per
-  // lane): in round i, wavefront wv fills LDS rows 8 (4 i + wv) .. +7, lane l
-  // the 16-byte slot l of that 1 KB segment, i.e. row 8 (4 i + wv) + (l >> 3),
-  // stored chunk l & 7, which holds logical chunk (l & 7) ^ (row & 7).
-  // Rows past the expert's last row (A) or past N (B) load a valid row
-  // instead: they only feed outputs that the epilogue drops.  Chunks past K
-  // are zero-filled with an ordinary LDS store.
-  const int ld_sub = lane >> 3;                          // row within the segment
-  const int ld_chunk = (lane & 7) ^ (ld_sub & 7);        // logical chunk loaded
-  int a_row[8];
-  int b_row[8];
+  // ---- copy coordinates.  In round i, wavefront wv fills the 1 KB LDS
+  // segment 4 i + wv: lane l writes 16-byte slot l, i.e. row
+  // SEG_ROWS (4 i + wv) + l / CPR, stored chunk l % CPR, which holds the
+  // logical chunk that swz() maps there.  Rows past the expert's last row (A)
+  // or past N (B) copy a valid row instead: they only feed outputs that the
+  // epilogue drops.
+  const int ld_sub = lane / CPR;
+  const int ld_phys = lane % CPR;
+  // The hash of swz() depends on row bits 1..4 (BK 32) or 0..5 (BK 64);
+  // segments start at multiples of SEG_ROWS (16 or 8 rows), so the hash of a
+  // copied row also depends on its segment: computed per round below.
+  int a_row[RA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (4 * i + wv) + ld_sub;
+  for (int i = 0; i < RA; ++i) {
+    const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
     const int gr = r0 + r < r_end ? r0 + r : r0;
     a_row[i] = a.row_token ? a.row_token[gr] : gr;
-    if constexpr (WF != WF_MXFP4) {
-      // B row r of the tile -> weight row of the expert (-1: the up matrix, encoded below)
-      int wrow, up = 0;
-      if constexpr (GATED) {
-        const int q = r >> 6, sub = r & 63;
-        wrow = n0 + 32 * q + (sub & 31);
-        up = sub >= 32;
-      } else {
-        wrow = n0 + r;
-      }
-      if (wrow >= N) wrow = n0;
-      b_row[i] = (wrow << 1) | up;
+  }
+  int b_row[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
+    int wrow, up = 0;
+    if constexpr (GATED) {
+      const int q = r >> 6, sub = r & 63;
+      wrow = n0 + 32 * q + (sub & 31);
+      up = sub >= 32;
+    } else {
+      wrow = n0 + r;
     }
+    if (wrow >= N) wrow = n0;
+    b_row[i] = (wrow << 1) | up;
   }
   const uint16_t* w_gate = shared ? a.sh_w0 : a.w0 + (size_t)e * a.N * K;
   const uint16_t* w_up = GATED ? (shared ? a.sh_w1 : a.w1 + (size_t)e * a.N * K) : nullptr;
 
-  // MXFP4: thread t decodes B row t (64 elements per K tile) through registers
+  // MXFP4: thread t < BN decodes B row t through registers
   const uint8_t* mx_codes = nullptr;
   const uint8_t* mx_scales = nullptr;
   if constexpr (WF == WF_MXFP4) {
-    const int r = tid;
+    const int r = tid < BN ? tid : BN - 1;
     int wrow;
     bool up = false;
     if constexpr (GATED) {
@@ -164,95 +241,169 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       mx_scales = (up ? a.s1 : a.s0) + row * (K / 32);
     }
   }
-  u32x4_t mxr[3];
+  u32x4_t mxr[2];   // codes of BK elements (BK / 2 bytes)
+  uint32_t mxs[2];  // their scale bytes (one per 32 elements)
 
-  // full K tiles (tail == false) need no bounds checks
-  auto issue_tile = [&](int k0, int stage, bool tail) {
-    const int k = k0 + 8 * ld_chunk;
-    const bool k_ok = !tail || k < K;
+  // Every tile issues exactly R copy instructions per wavefront (the K tail
+  // copies clamped, valid addresses and is zeroed after it lands), so the
+  // counted waits below are exact.
+  // logical chunk that lane slot ld_phys of round i holds (inverse of swz)
+  auto ld_chunk_of = [&](int i) {
+    const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
+    return (swz<BK>(row, ld_phys) - row * BK) >> 3;  // XOR is an involution
+  };
+  auto issue_tile = [&](int kt) {
+    const int stage = kt % NS;
     uint16_t* As = lds[stage][0];
     uint16_t* Bs = lds[stage][1];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t* seg = As + (4 * i + wv) * 512;  // 1 KB segment (512 bf16)
-      if (k_ok) {
-        __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, seg, 16, 0, 0);
-      } else {
-        *reinterpret_cast<u32x4_t*>(seg + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < RA; ++i) {
+      const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
+      __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (4 * i + wv) * 512, 16, 0, 0);
     }
     if constexpr (WF == WF_MXFP4) {
-      const bool ok0 = mx_codes && k0 < K, ok1 = mx_codes && k0 + 32 < K;
-      mxr[0] = ok0 ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2) : u32x4_t{0u, 0u, 0u, 0u};
-      mxr[1] = ok1 ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2 + 16) : u32x4_t{0u, 0u, 0u, 0u};
-      mxr[2] = u32x4_t{ok0 ? (uint32_t)mx_scales[k0 / 32] : 127u, ok1 ? (uint32_t)mx_scales[k0 / 32 + 1] : 127u, 0u, 0u};
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int h = 0; h < BK / 32; ++h) {
+        const bool ok = mx_codes && k0 + 32 * h < K;
+        mxr[h] = ok ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2 + 16 * h) : u32x4_t{0u, 0u, 0u, 0u};
+        mxs[h] = ok ? (uint32_t)mx_scales[k0 / 32 + h] : 127u;
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint16_t* seg = Bs + (4 * i + wv) * 512;
-        if (k_ok) {
-          const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
-          __builtin_amdgcn_global_load_lds(wsrc + (size_t)(b_row[i] >> 1) * K + k, seg, 16, 0, 0);
-        } else {
-          *reinterpret_cast<u32x4_t*>(seg + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
-        }
+      for (int i = 0; i < RB; ++i) {
+        const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
+        const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
+        __builtin_amdgcn_global_load_lds(wsrc + (size_t)(b_row[i] >> 1) * K + k, Bs + (4 * i + wv) * 512, 16, 0, 0);
       }
     }
   };
-  // MXFP4 only: decode the staged codes of row tid into LDS
-  auto finish_tile = [&](int stage) {
+  // MXFP4 only: decode the staged codes of row tid into the tile's stage
+  auto finish_tile = [&](int kt) {
     if constexpr (WF == WF_MXFP4) {
-      uint16_t* Bs = lds[stage][1];
+      uint16_t* Bs = lds[kt % NS][1];
+      if (tid < BN) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<u32x4_t*>(Bs + swz(tid, c)) = decode_e2m1x8(mxr[c >> 2][c & 3], mxr[2][c >> 2]);
+        for (int c = 0; c < CPR; ++c)
+          *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, c)) = decode_e2m1x8(mxr[c / 4][c % 4], mxs[c / 4]);
+      }
+    }
+  };
+  // zero the chunks of the tile past K (the last tile only)
+  auto zero_tail = [&](int kt) {
+    uint16_t* As = lds[kt % NS][0];
+    uint16_t* Bs = lds[kt % NS][1];
+#pragma unroll
+    for (int i = 0; i < RA; ++i)
+      if (kt * BK + 8 * ld_chunk_of(i) >= K)
+        *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (WF != WF_MXFP4) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        if (kt * BK + 8 * ld_chunk_of(i) >= K)
+          *reinterpret_cast<u32x4_t*>(Bs + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+  // ---- pipeline.  Tile t's copies are issued NS - 1 tiles ahead.  The
+  // fragments of the next 16-wide K step are read from LDS while the MFMAs of
+  // the current step run (two register sets).  Before the last step of tile
+  // kt the block waits for tile kt+1 and meets at a barrier; after it, the
+  // copies of tile kt+NS-1 go into the stage tile kt-1 used, and the first
+  // fragments of tile kt+1 load under the last MFMAs of tile kt.
+  constexpr int KK = BK / 16;
+  static_assert(KK % 2 == 0, "fragment double buffering needs an even step count");
   const int ktiles = (K + BK - 1) / BK;
-  const int full_tiles = K / BK;  // tiles with no element past K
-  issue_tile(0, 0, full_tiles == 0);
-  finish_tile(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const int tail_tile = (K % BK) != 0 ? ktiles - 1 : -1;
   const int fr = lane & 31, fk = lane >> 5;
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < full_tiles) issue_tile((kt + 1) * BK, st ^ 1, false);
-    else if (kt + 1 < ktiles) issue_tile((kt + 1) * BK, st ^ 1, true);
-    const uint16_t* As = lds[st][0];
-    const uint16_t* Bs = lds[st][1];
+
+  bf16x8_t fa[2][4], fb[2][NJ];
+  auto load_frags = [&](int stage, int kk, int buf) {
+    const uint16_t* As = lds[stage][0];
+    const uint16_t* Bs = lds[stage][1];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
+      fa[buf][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(As + swz<BK>(wm * 128 + 32 * i + fr, 2 * kk + fk)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(As + swz(wm * 128 + 32 * i + fr, 2 * kk + fk)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Bs + swz(wn * 128 + 32 * j + fr, 2 * kk + fk)));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+    for (int j = 0; j < NJ; ++j)
+      fb[buf][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Bs + swz<BK>(wn * 32 * NJ + 32 * j + fr, 2 * kk + fk)));
+  };
+  // wait until tile t has landed, given the tiles issued so far (up to `last`)
+  auto wait_tile = [&](int t, int last) {
+    const int after = last - t;  // tiles issued after t
+    if constexpr (WF == WF_MXFP4) {
+      wait_vmcnt<0>();
+    } else {
+      if (NS >= 5 && after >= 3) wait_vmcnt<(NS >= 5 ? 3 * R : 0)>();
+      else if (NS >= 4 && after >= 2) wait_vmcnt<(NS >= 4 ? 2 * R : 0)>();
+      else if (NS >= 3 && after >= 1) wait_vmcnt<(NS >= 3 ? R : 0)>();
+      else wait_vmcnt<0>();
     }
-    if (kt + 1 < ktiles) finish_tile(st ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's LDS copies have landed
-    __syncthreads();
+  };
+
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) {
+    if (t < ktiles) {
+      issue_tile(t);
+      finish_tile(t);
+    }
   }
+  wait_tile(0, min(NS - 2, ktiles - 1));
+  barrier_lds();
+  if (tail_tile == 0) {
+    zero_tail(0);
+    barrier_lds();
+  }
+  load_frags(0, 0, 0);
+  // One K tile.  STEADY: the next tile exists, its copies and those of tile
+  // kt+NS-1 are issued unconditionally (no branches, so the compiler's wait
+  // counting stays exact and the fragment reads overlap the MFMAs).
+  auto tile_step = [&](int kt, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const int st = kt % NS;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KK) {
+        load_frags(st, kk + 1, cur ^ 1);
+      } else if (STEADY || kt + 1 < ktiles) {
+        if (STEADY) wait_tile(kt + 1, kt + NS - 2);
+        else wait_tile(kt + 1, min(kt + NS - 2, ktiles - 1));
+        barrier_lds();  // tile kt+1 is in LDS; every wavefront is past tile kt-1
+        if (!STEADY && kt + 1 == tail_tile) {
+          zero_tail(kt + 1);
+          barrier_lds();
+        }
+        if (STEADY || kt + NS - 1 < ktiles) issue_tile(kt + NS - 1);
+        load_frags((kt + 1) % NS, 0, cur ^ 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+    }
+    if (STEADY || kt + NS - 1 < ktiles) finish_tile(kt + NS - 1);
+  };
+  int kt = 0;
+  // steady state needs tile kt+NS-1 < ktiles and no tail tile at kt+1
+  const int steady_end = ktiles - NS + 1 - (tail_tile >= 0 ? 1 : 0);
+  for (; kt < steady_end; ++kt) tile_step(kt, std::true_type{});
+  for (; kt < ktiles; ++kt) tile_step(kt, std::false_type{});
+  wait_vmcnt<0>();
+  barrier_lds();  // every wavefront is done with the stages before they are reused
 
   // ---- epilogue: bias (+ activation) in registers, bf16 tile staged in LDS,
   // then written out as 16-byte row chunks.
   constexpr int OC = GATED ? BN / 2 : BN;     // output columns of the tile
-  constexpr int OLD = GATED ? OC + 8 : OC;    // LDS row pitch (bf16); padded where it fits
+  constexpr int OLD = BM * (OC + 8) * 2 <= (int)sizeof(lds) ? OC + 8 : OC;  // LDS row pitch (bf16)
   static_assert(BM * OLD * 2 <= (int)sizeof(lds), "output tile exceeds the LDS buffers");
   uint16_t* ot = &lds[0][0][0];
   const uint16_t* bias0 = shared ? nullptr : a.bias0;
@@ -278,10 +429,10 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         }
       }
   } else {
-    float bv[4];
+    float bv[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + 32 * j + fr;
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn * 32 * NJ + 32 * j + fr;
       bv[j] = (bias0 && n < N) ? bf16_to_f32(bias0[(size_t)e * N + n]) : 0.f;
     }
 #pragma unroll
@@ -290,15 +441,15 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       for (int q = 0; q < 16; ++q) {
         const int row = wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fk + (q & 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ot[row * OLD + wn * 128 + 32 * j + fr] = f32_to_bf16(acc[i][j][q] + bv[j]);
+        for (int j = 0; j < NJ; ++j) ot[row * OLD + wn * 32 * NJ + 32 * j + fr] = f32_to_bf16(acc[i][j][q] + bv[j]);
       }
   }
   __syncthreads();
-  constexpr int CPR = OC / 8;  // 16-byte chunks per row
+  constexpr int OCPR = OC / 8;  // 16-byte chunks per output row
   const int rows = min(BM, r_end - r0);
   const int cols = min(OC, N - n0);  // multiple of 8
-  for (int c = tid; c < BM * CPR; c += kThreads) {
-    const int row = c / CPR, ch = c % CPR;
+  for (int c = tid; c < BM * OCPR; c += kThreads) {
+    const int row = c / OCPR, ch = c % OCPR;
     if (row < rows && 8 * ch < cols) {
       u32x4_t v;
       const uint32_t* src = reinterpret_cast<const uint32_t*>(ot + row * OLD + 8 * ch);
@@ -321,6 +472,7 @@ MfmaArgs base_args(const Layer& L, const Work& W) {
 }
 
 int max_row_tiles(const Layer& L) { return (L.rows_all() + BM - 1) / BM + L.n_experts_all(); }
+int grid_for(int tiles) { return (tiles + kXcds - 1) / kXcds * kXcds; }
 
 }  // namespace
 
@@ -339,10 +491,10 @@ hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.N = L.F; m.K = L.d; m.N_sh = L.F_sh; m.K_sh = L.d;
   m.out = static_cast<uint16_t*>(W.h);
   m.ldo = L.F_max();
-  m.n_tiles = (L.F_max() + BN / 2 - 1) / (BN / 2);
-  const dim3 grid(max_row_tiles(L) * m.n_tiles);
-  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, true><<<grid, kThreads, 0, s>>>(m);
-  else mfma_gemm_kernel<WF_BF16, true><<<grid, kThreads, 0, s>>>(m);
+  m.n_tiles = (L.F_max() + 127) / 128;
+  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, true, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+  else mfma_gemm_kernel<WF_BF16, true, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
 
@@ -358,10 +510,18 @@ hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.N = L.d; m.K = L.F; m.N_sh = L.d; m.K_sh = L.F_sh;
   m.out = static_cast<uint16_t*>(W.y);
   m.ldo = L.d;
-  m.n_tiles = (L.d + BN - 1) / BN;
-  const dim3 grid(max_row_tiles(L) * m.n_tiles);
-  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, false><<<grid, kThreads, 0, s>>>(m);
-  else mfma_gemm_kernel<WF_BF16, false><<<grid, kThreads, 0, s>>>(m);
+  // 192-column tiles when they waste fewer columns than 256-column ones
+  const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
+  const bool narrow = t192 * 192 < t256 * 256;
+  m.n_tiles = narrow ? t192 : t256;
+  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  if (L.wfmt == WF_MXFP4) {
+    if (narrow) mfma_gemm_kernel<WF_MXFP4, false, 3, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+    else mfma_gemm_kernel<WF_MXFP4, false, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+  } else {
+    if (narrow) mfma_gemm_kernel<WF_BF16, false, 3, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+    else mfma_gemm_kernel<WF_BF16, false, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+  }
   return hipGetLastError();
 }
 

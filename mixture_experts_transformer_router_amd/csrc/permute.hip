@@ -53,17 +53,37 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   const int b = blockIdx.x;
   const int E = a.E;
 
-  for (int e = tid; e < E; e += kThreads) {
-    int tot = 0, bef = 0;
+  // Column sums of the count table, split over all threads: thread
+  // (part, e) adds rows part, part + parts, ... of expert e.
+  {
+    int* part_tot = &wcnt[0][0];           // scratch, cleared again below
+    int* part_bef = &wcnt[2][0];
+    const int parts = E >= kThreads ? 1 : kThreads / E;
     const int first_own = b * a.hist_per_block;
-    for (int i = 0; i < a.n_hist; ++i) {
-      int c = a.hist[(size_t)i * E + e];
-      tot += c;
-      if (i < first_own) bef += c;
+    for (int t = tid; t < parts * E; t += kThreads) {
+      const int e = t % E, part = t / E;
+      int tot = 0, bef = 0;
+#pragma unroll 4
+      for (int i = part; i < a.n_hist; i += parts) {
+        const int c = a.hist[(size_t)i * E + e];
+        tot += c;
+        bef += i < first_own ? c : 0;
+      }
+      part_tot[t] = tot;
+      part_bef[t] = bef;
     }
-    total[e] = tot;
-    before[e] = bef;
-    running[e] = 0;
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) {
+      int tot = 0, bef = 0;
+      for (int p = 0; p < parts; ++p) {
+        tot += part_tot[p * E + e];
+        bef += part_bef[p * E + e];
+      }
+      total[e] = tot;
+      before[e] = bef;
+      running[e] = 0;
+    }
+    __syncthreads();
   }
   for (int i = tid; i < 4 * kMaxE; i += kThreads) (&wcnt[0][0])[i] = 0;
   __syncthreads();
