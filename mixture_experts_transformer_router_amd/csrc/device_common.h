@@ -11,12 +11,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN); the
+// conversion is gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// two floats -> packed bf16 pair (a in the low half)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
 template <typename T> __device__ __forceinline__ float load_f32(const T* p, size_t i);
@@ -31,7 +33,8 @@ template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, siz
   p[i] = f32_to_bf16(v);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic function with the hardware exp2 and reciprocal (about 2 ulp).
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Expert activation.  act 0: clipped SwiGLU (gate clipped to [0, limit], up to
 // [-limit, limit], h = g' * sigmoid(alpha g') * u').  act 1: h = g sigmoid(g) u.

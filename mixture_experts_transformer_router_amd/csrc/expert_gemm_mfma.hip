@@ -43,11 +43,17 @@ constexpr int kXcds = 8;       // MI355X: workgroup i runs on XCD i % 8
 #define MOE_GEMM_BK 32
 #endif
 #ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 5
+#define MOE_GEMM_STAGES 4
+#endif
+#ifndef MOE_GEMM_COPY_VIA_REGS
+#define MOE_GEMM_COPY_VIA_REGS 0
 #endif
 constexpr int kGroupM = MOE_GEMM_GROUP_M;  // row tiles walked together within an XCD
+// 0: global -> LDS copies (global_load_lds); 1: global -> registers at the
+// start of a tile, registers -> LDS after its last barrier.
+constexpr bool kCopyViaRegs = MOE_GEMM_COPY_VIA_REGS != 0;
 constexpr int kBK = MOE_GEMM_BK;           // K elements per LDS stage
-constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages (5 x 32 KB = the whole 160 KB)
+constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages (copies run this many tiles ahead)
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -76,6 +82,7 @@ struct MfmaArgs {
   int E, E_all;
   const int32_t* offsets;     // [E_all + 1]
   const int32_t* tile_prefix; // [E_all + 1], 256-row tiles
+  const int32_t* tile_desc;   // [tiles][4]: expert, first row, end row
   int n_tiles;                // column tiles per row tile
   uint16_t* out;
   int ldo;
@@ -105,8 +112,14 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // LDS stores and for the copies it needs (wait_vmcnt), then meets the others.
 // The asm's memory clobber keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // the wait is a builtin so that the compiler's own wait counting sees it
+  __builtin_amdgcn_s_waitcnt((15 << 14) | 15 | (7 << 4));  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
 }
+
+// Wait for this wavefront's outstanding LDS operations only (vmcnt and
+// expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt((15 << 14) | 15 | (7 << 4)); }
 
 // Wait until at most n vector-memory operations of this wavefront are
 // outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and
@@ -115,6 +128,14 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Value of lane l ^ 1 / l ^ 2 within each lane quad (DPP quad_perm [1,0,3,2] / [2,3,0,1]).
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
 }
 
 // 8 e2m1 codes (one 32-bit word, element 0 in the low nibble) times the block
@@ -147,8 +168,8 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int RB = BN * CPR / kThreads; // copy rounds per stage, B (dense)
   constexpr int R = RA + (WF == WF_MXFP4 ? 0 : RB);
   static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
-  // the copies of tile kt+1 must be in flight before tile kt's last step
-  static_assert(NS >= 3, "the pipeline needs at least 3 LDS stages");
+  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  constexpr bool REGS = kCopyViaRegs && WF != WF_MXFP4;  // MXFP4 B goes through registers anyway
   static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "copy rounds");
   __shared__ uint16_t lds[NS][2][BM * BK];  // [stage][A | B]
 
@@ -168,19 +189,15 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   const int rr = L - group * kGroupM * a.n_tiles;
   const int m_tile = first_m + rr % gm;
   const int n_tile = rr / gm;
-  int lo = 0, hi = a.E_all - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.tile_prefix[mid] <= m_tile) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
+  const int4 desc = reinterpret_cast<const int4*>(a.tile_desc)[m_tile];
+  const int e = desc.x;
   const bool shared = e >= a.E;
   const int N = shared ? a.N_sh : a.N;
   const int K = shared ? a.K_sh : a.K;
   const int n0 = n_tile * (GATED ? BN / 2 : BN);
   if (n0 >= N) return;
-  const int r0 = a.offsets[e] + (m_tile - a.tile_prefix[e]) * BM;
-  const int r_end = a.offsets[e + 1];
+  const int r0 = desc.y;
+  const int r_end = desc.z;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
@@ -252,10 +269,46 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
     return (swz<BK>(row, ld_phys) - row * BK) >> 3;  // XOR is an involution
   };
+  u32x4_t stage_a[REGS ? RA : 1], stage_b[REGS ? RB : 1];
+  // register path: fetch tile kt into registers
+  auto fetch_regs = [&](int kt) {
+    if constexpr (REGS) {
+#pragma unroll
+      for (int i = 0; i < RA; ++i) {
+        const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
+        stage_a[i] = *reinterpret_cast<const u32x4_t*>(a.a + (size_t)a_row[i] * a.lda + k);
+      }
+      if constexpr (WF != WF_MXFP4) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
+          const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
+          stage_b[i] = *reinterpret_cast<const u32x4_t*>(wsrc + (size_t)(b_row[i] >> 1) * K + k);
+        }
+      }
+    }
+  };
+  // register path: store the fetched tile into its stage
+  auto land_regs = [&](int kt) {
+    if constexpr (REGS) {
+      uint16_t* As = lds[kt % NS][0];
+      uint16_t* Bs = lds[kt % NS][1];
+#pragma unroll
+      for (int i = 0; i < RA; ++i) *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = stage_a[i];
+      if constexpr (WF != WF_MXFP4) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) *reinterpret_cast<u32x4_t*>(Bs + (4 * i + wv) * 512 + 8 * lane) = stage_b[i];
+      }
+    }
+  };
   auto issue_tile = [&](int kt) {
     const int stage = kt % NS;
     uint16_t* As = lds[stage][0];
     uint16_t* Bs = lds[stage][1];
+    if constexpr (REGS) {
+      (void)As; (void)Bs;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
@@ -313,12 +366,15 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // ---- pipeline.  Tile t's copies are issued NS - 1 tiles ahead.  The
-  // fragments of the next 16-wide K step are read from LDS while the MFMAs of
-  // the current step run (two register sets).  Before the last step of tile
-  // kt the block waits for tile kt+1 and meets at a barrier; after it, the
-  // copies of tile kt+NS-1 go into the stage tile kt-1 used, and the first
-  // fragments of tile kt+1 load under the last MFMAs of tile kt.
+  // ---- pipeline.  The copies of tile t are issued NS tiles ahead: the
+  // prologue issues tiles 0 .. NS-1 into all stages; in the last 16-wide K
+  // step of tile kt the block waits for tile kt+1, meets at a barrier (after
+  // which nobody reads tile kt from LDS: its last fragments are in
+  // registers), issues tile kt+NS into tile kt's stage and reads the first
+  // fragments of tile kt+1, all before the last MFMAs of tile kt.  Within a
+  // tile the fragments of step kk+1 are read while step kk multiplies (two
+  // register sets).  sched_barrier(0) keeps the compiler from sinking those
+  // reads below the MFMAs they are meant to overlap.
   constexpr int KK = BK / 16;
   static_assert(KK % 2 == 0, "fragment double buffering needs an even step count");
   const int ktiles = (K + BK - 1) / BK;
@@ -336,125 +392,136 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     for (int j = 0; j < NJ; ++j)
       fb[buf][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Bs + swz<BK>(wn * 32 * NJ + 32 * j + fr, 2 * kk + fk)));
   };
-  // wait until tile t has landed, given the tiles issued so far (up to `last`)
+  // wait until tile t has landed, given that tiles up to `last` are issued
   auto wait_tile = [&](int t, int last) {
     const int after = last - t;  // tiles issued after t
     if constexpr (WF == WF_MXFP4) {
       wait_vmcnt<0>();
     } else {
-      if (NS >= 5 && after >= 3) wait_vmcnt<(NS >= 5 ? 3 * R : 0)>();
-      else if (NS >= 4 && after >= 2) wait_vmcnt<(NS >= 4 ? 2 * R : 0)>();
-      else if (NS >= 3 && after >= 1) wait_vmcnt<(NS >= 3 ? R : 0)>();
+      if (NS >= 4 && after >= 3) wait_vmcnt<(NS >= 4 ? 3 * R : 0)>();
+      else if (NS >= 3 && after >= 2) wait_vmcnt<(NS >= 3 ? 2 * R : 0)>();
+      else if (NS >= 2 && after >= 1) wait_vmcnt<(NS >= 2 ? R : 0)>();
       else wait_vmcnt<0>();
     }
   };
 
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t) {
+  for (int t = 0; t < NS; ++t) {
     if (t < ktiles) {
       issue_tile(t);
       finish_tile(t);
+      fetch_regs(t);
+      land_regs(t);
     }
   }
-  wait_tile(0, min(NS - 2, ktiles - 1));
+  if constexpr (REGS) wait_vmcnt<0>();
+  else wait_tile(0, min(NS - 1, ktiles - 1));
   barrier_lds();
   if (tail_tile == 0) {
     zero_tail(0);
     barrier_lds();
   }
   load_frags(0, 0, 0);
-  // One K tile.  STEADY: the next tile exists, its copies and those of tile
-  // kt+NS-1 are issued unconditionally (no branches, so the compiler's wait
-  // counting stays exact and the fragment reads overlap the MFMAs).
+  // One K tile.  STEADY: tiles kt+1 and kt+NS exist and kt+1 is no tail, so
+  // the step runs without branches (and the compiler's wait counting stays exact).
   auto tile_step = [&](int kt, auto steady_tag) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     const int st = kt % NS;
+    if (REGS && (STEADY || kt + NS < ktiles)) fetch_regs(kt + NS);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
       if (kk + 1 < KK) {
+        // this step's fragments were read a whole MFMA run ago; waiting for
+        // them here keeps the wait from also covering the reads issued next
+        wait_lgkmcnt0();
         load_frags(st, kk + 1, cur ^ 1);
       } else if (STEADY || kt + 1 < ktiles) {
-        if (STEADY) wait_tile(kt + 1, kt + NS - 2);
-        else wait_tile(kt + 1, min(kt + NS - 2, ktiles - 1));
-        barrier_lds();  // tile kt+1 is in LDS; every wavefront is past tile kt-1
+        if constexpr (REGS) wait_vmcnt<0>();  // the registers of tile kt+NS
+        else if (STEADY) wait_tile(kt + 1, kt + NS - 1);
+        else wait_tile(kt + 1, min(kt + NS - 1, ktiles - 1));
+        barrier_lds();  // tile kt+1 is in LDS; every wavefront is done reading tile kt
         if (!STEADY && kt + 1 == tail_tile) {
           zero_tail(kt + 1);
           barrier_lds();
         }
-        if (STEADY || kt + NS - 1 < ktiles) issue_tile(kt + NS - 1);
+        if (STEADY || kt + NS < ktiles) {
+          issue_tile(kt + NS);
+          land_regs(kt + NS);
+        }
         load_frags((kt + 1) % NS, 0, cur ^ 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (STEADY || kt + NS - 1 < ktiles) finish_tile(kt + NS - 1);
+    if (STEADY || kt + NS < ktiles) finish_tile(kt + NS);
   };
   int kt = 0;
-  // steady state needs tile kt+NS-1 < ktiles and no tail tile at kt+1
-  const int steady_end = ktiles - NS + 1 - (tail_tile >= 0 ? 1 : 0);
+  // steady state needs tile kt+NS < ktiles and no tail tile at kt+1
+  const int steady_end = ktiles - NS - (tail_tile >= 0 ? 1 : 0);
   for (; kt < steady_end; ++kt) tile_step(kt, std::true_type{});
   for (; kt < ktiles; ++kt) tile_step(kt, std::false_type{});
   wait_vmcnt<0>();
   barrier_lds();  // every wavefront is done with the stages before they are reused
 
-  // ---- epilogue: bias (+ activation) in registers, bf16 tile staged in LDS,
-  // then written out as 16-byte row chunks.
-  constexpr int OC = GATED ? BN / 2 : BN;     // output columns of the tile
-  constexpr int OLD = BM * (OC + 8) * 2 <= (int)sizeof(lds) ? OC + 8 : OC;  // LDS row pitch (bf16)
-  static_assert(BM * OLD * 2 <= (int)sizeof(lds), "output tile exceeds the LDS buffers");
-  uint16_t* ot = &lds[0][0][0];
+  // ---- epilogue.  Bias (+ activation) in registers.  A lane holds one
+  // column for 16 rows of each 32 x 32 result; a 4 x 4 transpose across each
+  // lane quad (two xor shuffles) gives it 4 consecutive columns of one row,
+  // stored as 8 bytes straight to HBM (8 lanes write a 64-byte row piece).
   const uint16_t* bias0 = shared ? nullptr : a.bias0;
   const uint16_t* bias1 = shared ? nullptr : a.bias1;
   const int act = shared ? 1 : a.act;
-  if constexpr (GATED) {
-    float bg[2], bu[2];
+  const int c4 = fr & 3;            // position in the lane quad
+  constexpr int OJ = GATED ? NJ / 2 : NJ;  // output column tiles per wavefront
+  float bv0[OJ], bv1[OJ];
+  int colj[OJ];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int f = n0 + 32 * (2 * wn + jj) + fr;
-      bg[jj] = (bias0 && f < N) ? bf16_to_f32(bias0[(size_t)e * N + f]) : 0.f;
-      bu[jj] = (bias1 && f < N) ? bf16_to_f32(bias1[(size_t)e * N + f]) : 0.f;
-    }
+  for (int j = 0; j < OJ; ++j) {
+    colj[j] = GATED ? n0 + 32 * (2 * wn + j) : n0 + wn * 32 * NJ + 32 * j;
+    const int c = colj[j] + fr;
+    bv0[j] = (bias0 && c < N) ? bf16_to_f32(bias0[(size_t)e * N + c]) : 0.f;
+    bv1[j] = (GATED && bias1 && c < N) ? bf16_to_f32(bias1[(size_t)e * N + c]) : 0.f;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fk + (q & 3);
+    for (int g = 0; g < 4; ++g) {      // groups of 4 consecutive rows (q = 4 g .. 4 g + 3)
+      const int row_base = wm * 128 + 32 * i + 8 * g + 4 * fk;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const float h = expert_act(act, acc[i][2 * jj][q] + bg[jj], acc[i][2 * jj + 1][q] + bu[jj], a.alpha, a.limit);
-          ot[row * OLD + 32 * (2 * wn + jj) + fr] = f32_to_bf16(h);
+      for (int j = 0; j < OJ; ++j) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = 4 * g + r;
+          if constexpr (GATED) v[r] = expert_act(act, acc[i][2 * j][q] + bv0[j], acc[i][2 * j + 1][q] + bv1[j], a.alpha, a.limit);
+          else v[r] = acc[i][j][q] + bv0[j];
+        }
+        // transpose within the lane quad: afterwards lane c4 holds row
+        // row_base + c4, columns (fr & ~3) .. +3
+        {
+          const bool odd = c4 & 1;
+          const float s0 = odd ? v[0] : v[1], s1 = odd ? v[2] : v[3];
+          const float r0_ = quad_xor1(s0), r1_ = quad_xor1(s1);
+          if (odd) { v[0] = r0_; v[2] = r1_; } else { v[1] = r0_; v[3] = r1_; }
+          // lane even: v = [row 0 c, row 0 c+1, row 2 c, row 2 c+1]; odd: rows 1 and 3
+        }
+        {
+          const bool hi = c4 & 2;
+          const float s0 = hi ? v[0] : v[2], s1 = hi ? v[1] : v[3];
+          const float r0_ = quad_xor2(s0), r1_ = quad_xor2(s1);
+          if (hi) { v[0] = r0_; v[1] = r1_; } else { v[2] = r0_; v[3] = r1_; }
+        }
+        const int row = r0 + row_base + c4;
+        const int col = colj[j] + (fr & ~3);
+        if (row < r_end && col < N) {
+          *reinterpret_cast<uint2*>(a.out + (size_t)row * a.ldo + col) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
-  } else {
-    float bv[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + wn * 32 * NJ + 32 * j + fr;
-      bv[j] = (bias0 && n < N) ? bf16_to_f32(bias0[(size_t)e * N + n]) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fk + (q & 3);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) ot[row * OLD + wn * 32 * NJ + 32 * j + fr] = f32_to_bf16(acc[i][j][q] + bv[j]);
-      }
-  }
-  __syncthreads();
-  constexpr int OCPR = OC / 8;  // 16-byte chunks per output row
-  const int rows = min(BM, r_end - r0);
-  const int cols = min(OC, N - n0);  // multiple of 8
-  for (int c = tid; c < BM * OCPR; c += kThreads) {
-    const int row = c / OCPR, ch = c % OCPR;
-    if (row < rows && 8 * ch < cols) {
-      u32x4_t v;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(ot + row * OLD + 8 * ch);
-      v[0] = src[0]; v[1] = src[1]; v[2] = src[2]; v[3] = src[3];
-      *reinterpret_cast<u32x4_t*>(a.out + (size_t)(r0 + row) * a.ldo + n0 + 8 * ch) = v;
     }
   }
 }
@@ -465,6 +532,7 @@ MfmaArgs base_args(const Layer& L, const Work& W) {
   m.E_all = L.n_experts_all();
   m.offsets = W.offsets;
   m.tile_prefix = W.tile_prefix_big;
+  m.tile_desc = W.tile_desc;
   m.act = L.act;
   m.alpha = L.alpha;
   m.limit = L.limit;

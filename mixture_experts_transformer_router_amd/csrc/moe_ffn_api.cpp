@@ -177,6 +177,7 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   W->offsets = static_cast<int32_t*>(take((Eall + 1) * 4));
   W->tile_prefix = static_cast<int32_t*>(take((Eall + 1) * 4));
   W->tile_prefix_big = static_cast<int32_t*>(take((Eall + 1) * 4));
+  W->tile_desc = static_cast<int32_t*>(take((size_t)max_big_tiles((int)rows, (int)Eall) * 16));
   W->sorted_pair = static_cast<int32_t*>(take(rows * 4));
   W->row_token = static_cast<int32_t*>(take(rows * 4));
   W->pos = static_cast<int32_t*>(take(P * 4));

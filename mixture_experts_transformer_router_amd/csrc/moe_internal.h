@@ -25,6 +25,8 @@ constexpr int kDecodeMaxTokens = 16;
 constexpr int kTileM = 64;
 // Rows per M-tile of the MFMA grouped GEMMs.
 constexpr int kTileMBig = 256;
+// Upper bound on the number of 256-row tiles of a call.
+inline int max_big_tiles(int rows_all, int E_all) { return (rows_all + kTileMBig - 1) / kTileMBig + E_all; }
 
 // One call's arguments after validation.
 struct Layer {
@@ -75,6 +77,7 @@ struct Work {
   int32_t* offsets = nullptr;      // [E_all + 1] row offsets of each expert (shared last)
   int32_t* tile_prefix = nullptr;  // [E_all + 1] first 64-row M-tile of each expert
   int32_t* tile_prefix_big = nullptr;  // [E_all + 1] first 256-row M-tile of each expert
+  int32_t* tile_desc = nullptr;    // [max 256-row tiles][4]: expert, first row, end row, 0
   int32_t* sorted_pair = nullptr;  // [rows_all] pair id of each sorted row (shared rows: -1)
   int32_t* row_token = nullptr;    // [rows_all] token of each sorted row
   int32_t* pos = nullptr;          // [T*k] sorted row of each pair

@@ -35,6 +35,7 @@ struct PermuteArgs {
   int32_t* offsets;
   int32_t* tile_prefix;
   int32_t* tile_prefix_big;
+  int32_t* tile_desc;
   int32_t* sorted_pair;
   int32_t* row_token;
   int32_t* pos;
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   __shared__ int off[kMaxE + 1];
   __shared__ int running[kMaxE];
   __shared__ int wcnt[4][kMaxE];
+  __shared__ int tpb[kMaxE + 1];  // 256-row tile prefix (block 0)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = blockIdx.x;
@@ -106,12 +108,29 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
       for (int e = 0; e < Eall; ++e) {
         a.tile_prefix[e] = acc;
         a.tile_prefix_big[e] = acc_big;
+        tpb[e] = acc_big;
         const int c = e < E ? total[e] : a.T;
         acc += (c + a.tile_m - 1) / a.tile_m;
         acc_big += (c + a.tile_m_big - 1) / a.tile_m_big;
       }
       a.tile_prefix[Eall] = acc;
       a.tile_prefix_big[Eall] = acc_big;
+      tpb[Eall] = acc_big;
+    }
+    __syncthreads();
+    // one descriptor per 256-row tile: {expert, first row, end row, 0}
+    for (int e = tid; e < Eall; e += kThreads) {
+      const int first = tpb[e];
+      const int n = tpb[e + 1] - first;
+      const int r_begin = e < E ? off[e] : off[E];
+      const int r_end = e < E ? off[e + 1] : off[E] + a.T;
+      for (int j = 0; j < n; ++j) {
+        int32_t* d = a.tile_desc + 4 * (size_t)(first + j);
+        d[0] = e;
+        d[1] = r_begin + j * a.tile_m_big;
+        d[2] = r_end;
+        d[3] = 0;
+      }
     }
   }
 
@@ -176,6 +195,7 @@ hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s) {
   a.tile_m = kTileM;
   a.tile_m_big = kTileMBig;
   a.offsets = W.offsets; a.tile_prefix = W.tile_prefix; a.tile_prefix_big = W.tile_prefix_big;
+  a.tile_desc = W.tile_desc;
   a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
   a.user_offsets = L.routing.expert_offsets; a.user_sorted = L.routing.sorted_pair;
   permute_kernel<<<nblk, kThreads, 0, s>>>(a);
