@@ -40,10 +40,10 @@ constexpr int kXcds = 8;       // MI355X: workgroup i runs on XCD i % 8
 #define MOE_GEMM_GROUP_M 4
 #endif
 #ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 32
+#define MOE_GEMM_BK 64
 #endif
 #ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 4
+#define MOE_GEMM_STAGES 2
 #endif
 #ifndef MOE_GEMM_COPY_VIA_REGS
 #define MOE_GEMM_COPY_VIA_REGS 0
