@@ -7,23 +7,48 @@
 // (MaxText GPT-OSS weight mapping "MOE EXPERTS"; glm4_moe_lite.go
 // SwitchMLP.Forward and SharedExperts.Forward.)
 //
-// One block per (16 weight rows, expert); blocks of experts without rows exit
-// at once.  The weight rows are the 16-row operand of
-// v_mfma_f32_16x16x32_bf16 and the expert's tokens (zero-padded to 16) the
-// 16-column operand, so no cross-lane reduction is needed inside a
-// wavefront.  The block's 4 wavefronts split the reduction dimension into
-// contiguous quarters; their partial tiles are added in wavefront order
-// (deterministic).  Each lane reads 32 contiguous bytes of a weight row per
-// step of 64 elements (the two halves feed two MFMAs whose k order is the
-// same for both operands), so four lanes cover one 128-byte line.
+// The stage is bound by HBM reads of the weights, and HBM streams fastest when
+// every wavefront load instruction covers one contiguous kilobyte.  So the 64
+// lanes of a wavefront split the reduction dimension of ONE weight row: lane l
+// reads elements 512 c + 8 l .. +7 of chunk c, and multiplies them with the
+// same elements of each of the expert's token rows (v_dot2_f32_bf16, fp32
+// accumulation).  A wavefront owns kRowsPerWave consecutive weight rows (both
+// the gate and the up row in the gated stage); one block of kWaves wavefronts
+// owns kRowsPerWave * kWaves rows of one expert.  Blocks of experts without
+// rows exit at once.
+//
+// After the reduction loop every lane holds partial sums of all
+// (row, token) outputs; a reduce-scatter over the 64 lanes (halving the value
+// set at each of the 6 exchange steps, DPP within 16 lanes, lane shuffles
+// across) leaves each output summed over the whole wavefront in one lane, in a
+// fixed order, so the result does not depend on timing.
 #include "device_common.h"
 #include "moe_internal.h"
+
+#ifndef MOE_DECODE_WAVES
+#define MOE_DECODE_WAVES 4
+#endif
+#ifndef MOE_DECODE_ROWS
+#define MOE_DECODE_ROWS 4
+#endif
+#ifndef MOE_DECODE_MAX_TG
+#define MOE_DECODE_MAX_TG 16
+#endif
 
 namespace moe {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRows = 16;
+constexpr int kWaves = MOE_DECODE_WAVES;
+constexpr int kRowsPerWave = MOE_DECODE_ROWS;
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
+// Token rows handled in one pass over the weights (power of two).
+constexpr int kMaxTg = MOE_DECODE_MAX_TG;
+// Elements of a weight row covered by one wavefront load (64 lanes x 8).
+constexpr int kChunk = 512;
+static_assert((kRowsPerWave & (kRowsPerWave - 1)) == 0, "rows per wavefront must be a power of two");
+static_assert(kMaxTg >= 1 && kMaxTg <= kDecodeMaxTokens && (kMaxTg & (kMaxTg - 1)) == 0, "bad token group");
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct DecodeArgs {
   const uint16_t* a;          // gate|up: x [T, lda]; down: h [rows, lda]
@@ -44,76 +69,193 @@ struct DecodeArgs {
   float alpha, limit;
 };
 
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ u32x4_t ld16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// acc + sum over 8 bf16 products, pairwise in element order.  The pairs are
+// taken with shufflevector: a bit_cast of a subscripted vector element
+// (bit_cast<bf16x2>(w[i]) in an unrolled loop) is folded by this hipcc to
+// element 0 for every i.
+__device__ __forceinline__ float dot8(u32x4_t w, u32x4_t x, float acc) {
+  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w), b = __builtin_bit_cast(bf16x8_t, x);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc, false);
+  return acc;
+}
+
+// Exchange step j of the reduce-scatter: the partner of lane l is
+// l ^ {15, 7, 2, 1, 16, 32}[j] (row mirror, half-row mirror, quad swaps, then
+// across 16- and 32-lane halves).  Each partner differs from l in the step's
+// decision bit {3, 2, 1, 0, 4, 5}[j] and agrees on the earlier ones.
+constexpr int kDecisionBit[6] = {3, 2, 1, 0, 4, 5};
+template <int J>
+__device__ __forceinline__ float exchange(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  if constexpr (J == 0) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, true));
+  else if constexpr (J == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true));
+  else if constexpr (J == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));
+  else if constexpr (J == 3) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));
+  else if constexpr (J == 4) return __shfl_xor(v, 16, 64);
+  else return __shfl_xor(v, 32, 64);
+}
+
+// Reduce-scatter of v[0 .. C) over the wavefront.  While C > 1 a step keeps the
+// half of the values selected by the lane's decision bit and adds the
+// partner's copy of that half; once one value is left the remaining steps add
+// the partner's value.  Afterwards v[0 .. max(C/64, 1)) hold whole-wavefront
+// sums (see value_index).
+template <int J, int C>
+__device__ __forceinline__ void reduce_scatter(float* v, int lane) {
+  if constexpr (J < 6) {
+    const bool hi = (lane >> kDecisionBit[J]) & 1;
+    if constexpr (C > 1) {
+      constexpr int H = C / 2;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float keep = hi ? v[H + i] : v[i];
+        const float send = hi ? v[i] : v[H + i];
+        v[i] = keep + exchange<J>(send);
+      }
+      reduce_scatter<J + 1, H>(v, lane);
+    } else {
+      v[0] += exchange<J>(v[0]);
+      reduce_scatter<J + 1, 1>(v, lane);
+    }
+  }
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// After reduce_scatter of V values, lane `lane` holds in v[i] the value with
+// index lane_bits * max(V/64, 1) + i, where lane_bits collects the decision
+// bits of the first min(log2 V, 6) steps, most significant first.  Lanes that
+// differ only in the other bits hold the same sums; the one with those bits
+// zero is the owner.
+template <int V>
+__device__ __forceinline__ int lane_bits(int lane) {
+  constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
+  int b = 0;
+#pragma unroll
+  for (int j = 0; j < S; ++j) b = (b << 1) | ((lane >> kDecisionBit[j]) & 1);
+  return b;
+}
+template <int V>
+__device__ __forceinline__ bool lane_owns(int lane) {
+  constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
+  bool own = true;
+#pragma unroll
+  for (int j = S; j < 6; ++j) own = own && !((lane >> kDecisionBit[j]) & 1);
+  return own;
+}
+
+// One pass over the wavefront's weight rows for token slots t0 .. t0+TG-1
+// of the expert (slots >= m contribute zeros and are not stored).
+template <bool GATED, int TG>
+__device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool shared, int N, int K, int nw, int m0,
+                                            int m, int t0, int lane) {
+  constexpr int G = GATED ? 2 : 1;
+  constexpr int R = kRowsPerWave;
+  constexpr int V = G * R * TG;  // value index ((g R + r) TG + t)
+  static_assert((V & (V - 1)) == 0, "value count must be a power of two");
+
+  const uint16_t* Wb0 = shared ? a.sh_w0 : a.w0 + (size_t)e * a.N * a.K;
+  const uint16_t* Wb1 = GATED ? (shared ? a.sh_w1 : a.w1 + (size_t)e * a.N * a.K) : nullptr;
+  const uint16_t* Wr[G][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t row = (size_t)min(nw + r, N - 1) * K;  // rows past N are computed but not stored
+    Wr[0][r] = Wb0 + row;
+    if constexpr (GATED) Wr[1][r] = Wb1 + row;
+  }
+  const uint16_t* X[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const int slot = min(t0 + t, m - 1);
+    const int brow = a.row_token ? a.row_token[m0 + slot] : m0 + slot;
+    X[t] = a.a + (size_t)brow * a.lda;
+  }
+
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = 0.f;
+
+  const int chunks = (K + kChunk - 1) / kChunk;
+  for (int c = 0; c < chunks; ++c) {
+    const int k = c * kChunk + 8 * lane;
+    if (k < K) {  // K % 8 == 0: a lane's 8 elements are all in range or all out
+      u32x4_t w[G][R], x[TG];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[g][r] = ld16_stream(Wr[g][r] + k);
+#pragma unroll
+      for (int t = 0; t < TG; ++t) x[t] = (t0 + t < m) ? ld16(X[t] + k) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int t = 0; t < TG; ++t) v[(g * R + r) * TG + t] = dot8(w[g][r], x[t], v[(g * R + r) * TG + t]);
+    }
+  }
+
+  reduce_scatter<0, V>(v, lane);
+
+  constexpr int C = V >= 64 ? V / 64 : 1;
+  const int lb = lane_bits<V>(lane);
+  const bool own = lane_owns<V>(lane);
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    // the gate/up index bit is the most significant, taken from lane bit 3:
+    // the up value of a gate lane sits in lane ^ 8 (row rotate by 8)
+    float up = 0.f;
+    if constexpr (GATED)
+      up = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0x128, 0xF, 0xF, true));
+    const int idx = lb * C + i;
+    const int g = idx / (R * TG), r = (idx / TG) % R, t = idx % TG;
+    const int n = nw + r;
+    if (!own || g != 0 || t0 + t >= m || n >= N) continue;
+    float val = v[i];
+    if (!shared && a.bias0) val += bf16_to_f32(a.bias0[(size_t)e * N + n]);
+    if constexpr (GATED) {
+      if (!shared && a.bias1) up += bf16_to_f32(a.bias1[(size_t)e * N + n]);
+      val = expert_act(shared ? 1 : a.act, val, up, a.alpha, a.limit);
+    }
+    a.out[(size_t)(m0 + t0 + t) * a.ldo + n] = f32_to_bf16(val);
+  }
+}
+
 template <bool GATED>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
-  __shared__ float red[kWaves][GATED ? 2 : 1][kRows][kRows + 1];
-
   const int e = blockIdx.y;
   const bool shared = e >= a.E;
   const int N = shared ? a.N_sh : a.N;
   const int K = shared ? a.K_sh : a.K;
-  const int n0 = blockIdx.x * kRows;
-  if (n0 >= N) return;
+  const int nb = blockIdx.x * kRowsPerBlock;
+  if (nb >= N) return;
   const int m0 = a.offsets[e];
-  const int m = a.offsets[e + 1] - m0;  // <= 16 on this path
+  const int m = a.offsets[e + 1] - m0;  // <= kDecodeMaxTokens on this path
   if (m <= 0) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int row = lane & 15, kg = lane >> 4;
-
-  // A operand: weight row n0 + row
-  const bool row_ok = n0 + row < N;
-  const size_t wrow = (size_t)(row_ok ? n0 + row : n0) * K;
-  const uint16_t* W0 = (shared ? a.sh_w0 : a.w0 + (size_t)e * a.N * a.K) + wrow;
-  const uint16_t* W1 = GATED ? (shared ? a.sh_w1 : a.w1 + (size_t)e * a.N * a.K) + wrow : nullptr;
-  // B operand: token slot `row` of this expert
-  const bool tok_ok = row < m;
-  const int brow = tok_ok ? (a.row_token ? a.row_token[m0 + row] : m0 + row) : 0;
-  const uint16_t* B = a.a + (size_t)brow * a.lda;
-
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int steps = (K + 63) / 64;
-  const int s_begin = (steps * wv) / kWaves, s_end = (steps * (wv + 1)) / kWaves;
-#pragma unroll 4
-  for (int s = s_begin; s < s_end; ++s) {
-    const int k = 64 * s + 16 * kg;
-    const bool k0 = k < K, k1 = k + 8 < K;  // K % 8 == 0
-    const bf16x8_t b0 = (tok_ok && k0) ? load_bf16x8(B + k) : zero_bf16x8();
-    const bf16x8_t b1 = (tok_ok && k1) ? load_bf16x8(B + k + 8) : zero_bf16x8();
-    const bf16x8_t g0 = (row_ok && k0) ? load_bf16x8_stream(W0 + k) : zero_bf16x8();
-    const bf16x8_t g1 = (row_ok && k1) ? load_bf16x8_stream(W0 + k + 8) : zero_bf16x8();
-    acc0 = mfma_16x16x32(g0, b0, acc0);
-    acc0 = mfma_16x16x32(g1, b1, acc0);
-    if constexpr (GATED) {
-      const bf16x8_t u0 = (row_ok && k0) ? load_bf16x8_stream(W1 + k) : zero_bf16x8();
-      const bf16x8_t u1 = (row_ok && k1) ? load_bf16x8_stream(W1 + k + 8) : zero_bf16x8();
-      acc1 = mfma_16x16x32(u0, b0, acc1);
-      acc1 = mfma_16x16x32(u1, b1, acc1);
-    }
+  const int lane = threadIdx.x & 63;
+  const int nw = nb + (threadIdx.x >> 6) * kRowsPerWave;
+  if (nw >= N) return;
+  // token group: the smallest power of two covering m, up to kMaxTg per pass
+  if (m <= 1) {
+    decode_pass<GATED, 1>(a, e, shared, N, K, nw, m0, m, 0, lane);
+  } else if (m <= 2) {
+    decode_pass<GATED, 2>(a, e, shared, N, K, nw, m0, m, 0, lane);
+  } else if (m <= 4 || kMaxTg < 8) {
+    for (int t0 = 0; t0 < m; t0 += 4 < kMaxTg ? 4 : kMaxTg)
+      decode_pass<GATED, (4 < kMaxTg ? 4 : kMaxTg)>(a, e, shared, N, K, nw, m0, m, t0, lane);
+  } else if (m <= 8 || kMaxTg < 16) {
+    for (int t0 = 0; t0 < m; t0 += 8) decode_pass<GATED, 8>(a, e, shared, N, K, nw, m0, m, t0, lane);
+  } else {
+    decode_pass<GATED, (kMaxTg < 16 ? 8 : 16)>(a, e, shared, N, K, nw, m0, m, 0, lane);
   }
-  // D[weight row][token slot]: lane holds rows 4 kg + r of column `row`
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    red[wv][0][4 * kg + r][row] = acc0[r];
-    if constexpr (GATED) red[wv][1][4 * kg + r][row] = acc1[r];
-  }
-  __syncthreads();
-  // epilogue: thread -> (weight row, token slot), weight row fastest
-  const int er = tid & 15, slot = tid >> 4;
-  if (slot >= m || n0 + er >= N) return;
-  float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    v0 += red[w][0][er][slot];
-    if constexpr (GATED) v1 += red[w][1][er][slot];
-  }
-  const int n = n0 + er;
-  if (!shared && a.bias0) v0 += bf16_to_f32(a.bias0[(size_t)e * N + n]);
-  if constexpr (GATED) {
-    if (!shared && a.bias1) v1 += bf16_to_f32(a.bias1[(size_t)e * N + n]);
-    v0 = expert_act(shared ? 1 : a.act, v0, v1, a.alpha, a.limit);
-  }
-  a.out[(size_t)(m0 + slot) * a.ldo + n] = f32_to_bf16(v0);
 }
 
 DecodeArgs base_args(const Layer& L, const Work& W) {
@@ -142,7 +284,7 @@ hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.N = L.F; d.K = L.d; d.N_sh = L.F_sh; d.K_sh = L.d;
   d.out = static_cast<uint16_t*>(W.h);
   d.ldo = L.F_max();
-  const dim3 grid((L.F_max() + kRows - 1) / kRows, L.n_experts_all());
+  const dim3 grid((L.F_max() + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
   decode_kernel<true><<<grid, 64 * kWaves, 0, s>>>(d);
   return hipGetLastError();
 }
@@ -158,7 +300,7 @@ hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.N = L.d; d.K = L.F; d.N_sh = L.d; d.K_sh = L.F_sh;
   d.out = static_cast<uint16_t*>(W.y);
   d.ldo = L.d;
-  const dim3 grid((L.d + kRows - 1) / kRows, L.n_experts_all());
+  const dim3 grid((L.d + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
   decode_kernel<false><<<grid, 64 * kWaves, 0, s>>>(d);
   return hipGetLastError();
 }

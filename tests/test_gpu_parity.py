@@ -66,6 +66,14 @@ SMALL = [
     W.GLM4_MOE_LITE.scaled(T=70, d=96, d_ff=64, E=16, k=3, n_group=4, topk_group=2,
                            dtype="f32", act="clipped_swiglu", expert_bias=True, router_bias="normal",
                            d_ff_shared=32, name="glm_f32_clipped_shared"),
+    # few-token (weight-streaming) path: K ragged against 512-element chunks,
+    # weight rows ragged against the 16-row blocks, 1 .. 16 rows per expert
+    W.GPTOSS_DECODE.scaled(T=5, d=520, d_ff=72, E=8, k=3, name="decode_T5_ragged"),
+    W.GPTOSS_DECODE.scaled(T=16, d=1096, d_ff=200, E=4, k=4, name="decode_T16_every_expert_full"),
+    W.GPTOSS_DECODE.scaled(T=11, d=64, d_ff=24, E=3, k=2, name="decode_T11_short_rows"),
+    W.GLM4_MOE_LITE.scaled(T=12, d=576, d_ff=96, E=16, k=4, n_group=4, topk_group=2,
+                           d_ff_shared=160, name="glm_decode_T12_shared"),
+    W.GLM4_MOE_LITE.scaled(T=3, d=1024, d_ff=256, E=64, k=6, d_ff_shared=40, name="glm_decode_T3"),
 ]
 
 
