@@ -8,10 +8,13 @@
 // SwitchMLP.Forward: per-expert gathered products, activation, down product;
 // SharedExperts.Forward for the shared expert, handled as expert E.)
 //
-// Block tile 256 rows x (64 NJ) columns; K is staged BK at a time through NS
-// LDS buffers.  Global -> LDS copies go straight into LDS (no registers) and
-// run NS - 1 tiles ahead of the multiply, so the latency of a copy is covered
-// by NS - 1 tiles of MFMA work.
+// Block tile 256 rows x (64 NJ) columns; K is staged BK at a time through LDS
+// buffers filled by global -> LDS copies (no registers).  The A operand (token
+// rows: a few tens of megabytes, mostly cache hits) has NS buffers and runs
+// NS - 1 tiles ahead of the multiply; the B operand (expert weights, streamed
+// from HBM) may have NSB = NS + 1 buffers to run one tile further ahead.  On
+// MI355X the copies are bound by the L2 requests a CU keeps in flight, not by
+// how far ahead they are issued, so the default is NSB = NS = 2.
 // 4 wavefronts, each owning a 128 x (32 NJ) sub-tile as 4 x NJ results of
 // v_mfma_f32_32x32x16_bf16 (fp32 accumulators).  An LDS row holds BK bf16;
 // its 16-byte chunks are stored XOR-swizzled by the row's position within a
@@ -45,15 +48,13 @@ constexpr int kXcds = 8;       // MI355X: workgroup i runs on XCD i % 8
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 2
 #endif
-#ifndef MOE_GEMM_COPY_VIA_REGS
-#define MOE_GEMM_COPY_VIA_REGS 0
+#ifndef MOE_GEMM_STAGES_B
+#define MOE_GEMM_STAGES_B 2
 #endif
 constexpr int kGroupM = MOE_GEMM_GROUP_M;  // row tiles walked together within an XCD
-// 0: global -> LDS copies (global_load_lds); 1: global -> registers at the
-// start of a tile, registers -> LDS after its last barrier.
-constexpr bool kCopyViaRegs = MOE_GEMM_COPY_VIA_REGS != 0;
 constexpr int kBK = MOE_GEMM_BK;           // K elements per LDS stage
-constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages (copies run this many tiles ahead)
+constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages of the A operand
+constexpr int kStagesB = MOE_GEMM_STAGES_B;  // LDS stages of the (dense) B operand
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -156,22 +157,43 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, uint32_t s) {
   return u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
-// NJ = 32-column result tiles per wavefront (block columns BN = 64 NJ).
 // NJ = 32-column result tiles per wavefront (block columns BN = 64 NJ);
-// BK = K elements per stage; NS = LDS stages.
-template <int WF, bool GATED, int NJ, int BK, int NS>
+// BK = K elements per stage; NS / NSB = LDS stages of A / B.
+template <int WF, bool GATED, int NJ, int BK, int NS, int NSB>
 __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int BN = 64 * NJ;
   constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
   constexpr int SEG_ROWS = 1024 / (2 * BK);  // rows per 1 KB copy segment
-  constexpr int RA = BM * CPR / kThreads; // copy rounds per stage, A
-  constexpr int RB = BN * CPR / kThreads; // copy rounds per stage, B (dense)
-  constexpr int R = RA + (WF == WF_MXFP4 ? 0 : RB);
+  constexpr int RA = BM * CPR / kThreads; // copy instructions per wavefront and tile, A
+  constexpr int RB = WF == WF_MXFP4 ? 0 : BN * CPR / kThreads;  // same, B (MXFP4: register loads)
   static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
-  static_assert(NS >= 2 && NS <= 4, "LDS stages");
-  constexpr bool REGS = kCopyViaRegs && WF != WF_MXFP4;  // MXFP4 B goes through registers anyway
+  static_assert(NS >= 2 && NSB >= NS && NSB <= NS + 1, "LDS stages");
+  static_assert(WF != WF_MXFP4 || NSB == NS, "MXFP4 weights use symmetric stages");
   static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "copy rounds");
-  __shared__ uint16_t lds[NS][2][BM * BK];  // [stage][A | B]
+  static_assert(NS <= 3 && NSB <= 4, "stage variables");
+  // One LDS variable per stage: the compiler tells copies into one stage from
+  // reads of another only by the variable they address (see the pipeline).
+  __shared__ uint16_t lds_a0[BM * BK], lds_a1[BM * BK], lds_a2[NS > 2 ? BM * BK : 8];
+  __shared__ uint16_t lds_b0[BN * BK], lds_b1[BN * BK], lds_b2[NSB > 2 ? BN * BK : 8], lds_b3[NSB > 3 ? BN * BK : 8];
+  // MXFP4 (every wait drains the copies anyway): one array per operand
+  __shared__ uint16_t lds_mx_a[NS][BM * BK], lds_mx_b[NS][BN * BK];
+  auto stage_a = [&](int st) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (WF == WF_MXFP4) return lds_mx_a[st];
+    if constexpr (NS > 2) {
+      if (st == 2) return lds_a2;
+    }
+    return st == 0 ? lds_a0 : lds_a1;
+  };
+  auto stage_b = [&](int st) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (WF == WF_MXFP4) return lds_mx_b[st];
+    if constexpr (NSB > 3) {
+      if (st == 3) return lds_b3;
+    }
+    if constexpr (NSB > 2) {
+      if (st == 2) return lds_b2;
+    }
+    return st == 0 ? lds_b0 : lds_b1;
+  };
 
   // Tile order.  The real number of row tiles is known only on the device;
   // every block reads it and the blocks of XCD x take the x-th contiguous
@@ -210,9 +232,6 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   // epilogue drops.
   const int ld_sub = lane / CPR;
   const int ld_phys = lane % CPR;
-  // The hash of swz() depends on row bits 1..4 (BK 32) or 0..5 (BK 64);
-  // segments start at multiples of SEG_ROWS (16 or 8 rows), so the hash of a
-  // copied row also depends on its segment: computed per round below.
   int a_row[RA];
 #pragma unroll
   for (int i = 0; i < RA; ++i) {
@@ -220,7 +239,8 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     const int gr = r0 + r < r_end ? r0 + r : r0;
     a_row[i] = a.row_token ? a.row_token[gr] : gr;
   }
-  int b_row[RB];
+  constexpr int RBX = RB > 0 ? RB : 1;
+  int b_row[RBX];
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
@@ -258,71 +278,38 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       mx_scales = (up ? a.s1 : a.s0) + row * (K / 32);
     }
   }
-  u32x4_t mxr[2];   // codes of BK elements (BK / 2 bytes)
-  uint32_t mxs[2];  // their scale bytes (one per 32 elements)
+  // codes of BK elements (BK / 2 bytes) and their scale bytes (one per 32
+  // elements), kept in named registers (an array here ends up in scratch)
+  static_assert(WF != WF_MXFP4 || BK == 64, "MXFP4 stages hold 64 elements");
+  u32x4_t mxr0 = {0u, 0u, 0u, 0u}, mxr1 = {0u, 0u, 0u, 0u};
+  uint32_t mxs0 = 127u, mxs1 = 127u;
 
-  // Every tile issues exactly R copy instructions per wavefront (the K tail
-  // copies clamped, valid addresses and is zeroed after it lands), so the
-  // counted waits below are exact.
+  // Every copy of a tile issues exactly RA (A) and RB (B) instructions per
+  // wavefront (the K tail copies clamped, valid addresses and is zeroed after
+  // it lands), so the counted waits below are exact.
   // logical chunk that lane slot ld_phys of round i holds (inverse of swz)
-  auto ld_chunk_of = [&](int i) {
+  auto ld_chunk_of = [&](int i) __attribute__((always_inline)) {
     const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
     return (swz<BK>(row, ld_phys) - row * BK) >> 3;  // XOR is an involution
   };
-  u32x4_t stage_a[REGS ? RA : 1], stage_b[REGS ? RB : 1];
-  // register path: fetch tile kt into registers
-  auto fetch_regs = [&](int kt) {
-    if constexpr (REGS) {
-#pragma unroll
-      for (int i = 0; i < RA; ++i) {
-        const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
-        stage_a[i] = *reinterpret_cast<const u32x4_t*>(a.a + (size_t)a_row[i] * a.lda + k);
-      }
-      if constexpr (WF != WF_MXFP4) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
-          const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
-          stage_b[i] = *reinterpret_cast<const u32x4_t*>(wsrc + (size_t)(b_row[i] >> 1) * K + k);
-        }
-      }
-    }
-  };
-  // register path: store the fetched tile into its stage
-  auto land_regs = [&](int kt) {
-    if constexpr (REGS) {
-      uint16_t* As = lds[kt % NS][0];
-      uint16_t* Bs = lds[kt % NS][1];
-#pragma unroll
-      for (int i = 0; i < RA; ++i) *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = stage_a[i];
-      if constexpr (WF != WF_MXFP4) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) *reinterpret_cast<u32x4_t*>(Bs + (4 * i + wv) * 512 + 8 * lane) = stage_b[i];
-      }
-    }
-  };
-  auto issue_tile = [&](int kt) {
-    const int stage = kt % NS;
-    uint16_t* As = lds[stage][0];
-    uint16_t* Bs = lds[stage][1];
-    if constexpr (REGS) {
-      (void)As; (void)Bs;
-      return;
-    }
+  auto issue_a = [&](int kt, int sa) __attribute__((always_inline)) {
+    uint16_t* As = stage_a(sa);
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
       const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
       __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (4 * i + wv) * 512, 16, 0, 0);
     }
+  };
+  auto issue_b = [&](int kt, int sb) __attribute__((always_inline)) {
     if constexpr (WF == WF_MXFP4) {
       const int k0 = kt * BK;
-#pragma unroll
-      for (int h = 0; h < BK / 32; ++h) {
-        const bool ok = mx_codes && k0 + 32 * h < K;
-        mxr[h] = ok ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2 + 16 * h) : u32x4_t{0u, 0u, 0u, 0u};
-        mxs[h] = ok ? (uint32_t)mx_scales[k0 / 32 + h] : 127u;
-      }
+      const bool ok0 = mx_codes && k0 < K, ok1 = mx_codes && k0 + 32 < K;
+      mxr0 = ok0 ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2) : u32x4_t{0u, 0u, 0u, 0u};
+      mxs0 = ok0 ? (uint32_t)mx_scales[k0 / 32] : 127u;
+      mxr1 = ok1 ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2 + 16) : u32x4_t{0u, 0u, 0u, 0u};
+      mxs1 = ok1 ? (uint32_t)mx_scales[k0 / 32 + 1] : 127u;
     } else {
+      uint16_t* Bs = stage_b(sb);
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
@@ -332,30 +319,33 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     }
   };
   // MXFP4 only: decode the staged codes of row tid into the tile's stage
-  auto finish_tile = [&](int kt) {
+  auto finish_b = [&](int sb) __attribute__((always_inline)) {
     if constexpr (WF == WF_MXFP4) {
-      uint16_t* Bs = lds[kt % NS][1];
+      uint16_t* Bs = stage_b(sb);
       if (tid < BN) {
-#pragma unroll
-        for (int c = 0; c < CPR; ++c)
-          *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, c)) = decode_e2m1x8(mxr[c / 4][c % 4], mxs[c / 4]);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 0)) = decode_e2m1x8(mxr0.x, mxs0);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 1)) = decode_e2m1x8(mxr0.y, mxs0);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 2)) = decode_e2m1x8(mxr0.z, mxs0);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 3)) = decode_e2m1x8(mxr0.w, mxs0);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 4)) = decode_e2m1x8(mxr1.x, mxs1);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 5)) = decode_e2m1x8(mxr1.y, mxs1);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 6)) = decode_e2m1x8(mxr1.z, mxs1);
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 7)) = decode_e2m1x8(mxr1.w, mxs1);
       }
     }
   };
   // zero the chunks of the tile past K (the last tile only)
-  auto zero_tail = [&](int kt) {
-    uint16_t* As = lds[kt % NS][0];
-    uint16_t* Bs = lds[kt % NS][1];
+  auto zero_tail = [&](int kt, int sa, int sb) __attribute__((always_inline)) {
+    uint16_t* As = stage_a(sa);
+    uint16_t* Bs = stage_b(sb);
 #pragma unroll
     for (int i = 0; i < RA; ++i)
       if (kt * BK + 8 * ld_chunk_of(i) >= K)
         *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (WF != WF_MXFP4) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
-        if (kt * BK + 8 * ld_chunk_of(i) >= K)
-          *reinterpret_cast<u32x4_t*>(Bs + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < RB; ++i)
+      if (kt * BK + 8 * ld_chunk_of(i) >= K)
+        *reinterpret_cast<u32x4_t*>(Bs + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
   };
 
   f32x16_t acc[4][NJ];
@@ -366,25 +356,39 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  // ---- pipeline.  The copies of tile t are issued NS tiles ahead: the
-  // prologue issues tiles 0 .. NS-1 into all stages; in the last 16-wide K
-  // step of tile kt the block waits for tile kt+1, meets at a barrier (after
-  // which nobody reads tile kt from LDS: its last fragments are in
-  // registers), issues tile kt+NS into tile kt's stage and reads the first
-  // fragments of tile kt+1, all before the last MFMAs of tile kt.  Within a
-  // tile the fragments of step kk+1 are read while step kk multiplies (two
-  // register sets).  sched_barrier(0) keeps the compiler from sinking those
-  // reads below the MFMAs they are meant to overlap.
+  // ---- pipeline.  Copies are issued in batches, one per tile boundary: the
+  // batch of slot s holds A(s + NS) then B(s + NSB) (each if it exists), and
+  // slot s's batch is issued in the last 16-wide K step of tile s, right after
+  // the barrier that ends all reads of tile s (its last fragments are already
+  // in registers) -- into the stages tile s used.  The prologue issues the
+  // batches of slots -NSB .. -1.  Before the barrier of tile kt the block
+  // needs tile kt+1, whose last instruction is A(kt+1) (B(kt+1) when NSB ==
+  // NS); only the instructions issued after it may still be in flight.  In
+  // steady state those are B(kt+1+NSB-NS) (NSB > NS) and NS - 2 whole
+  // batches; near the end of K the block simply waits for everything.
+  // Within a tile the fragments of step kk+1 are read while step kk
+  // multiplies (two register sets).  sched_barrier(0) keeps the compiler from
+  // sinking those reads below the MFMAs they are meant to overlap.
+  //
+  // The compiler adds its own wait before an LDS read for every copy in
+  // flight into the LDS variable that read addresses.  Each stage is its own
+  // variable, and the steady loop is unrolled by P = lcm(NS, NSB) tiles so
+  // that every stage index is a compile-time constant: the reads of tile kt+1
+  // then never wait for the copies into other stages (with run-time indices
+  // they would wait for all copies).
   constexpr int KK = BK / 16;
   static_assert(KK % 2 == 0, "fragment double buffering needs an even step count");
+  constexpr int kSteadyWait = (NSB > NS ? RB : 0) + (NS - 2) * (RA + RB);
+  constexpr int kPrologueWait = (NSB > NS ? RB : 0) + (NS - 1) * (RA + RB);
+  constexpr int P = NS == NSB ? NS : NS * NSB;  // NSB = NS + 1 is coprime to NS
   const int ktiles = (K + BK - 1) / BK;
   const int tail_tile = (K % BK) != 0 ? ktiles - 1 : -1;
   const int fr = lane & 31, fk = lane >> 5;
 
   bf16x8_t fa[2][4], fb[2][NJ];
-  auto load_frags = [&](int stage, int kk, int buf) {
-    const uint16_t* As = lds[stage][0];
-    const uint16_t* Bs = lds[stage][1];
+  auto load_frags = [&](int sa, int sb, int kk, int buf) __attribute__((always_inline)) {
+    const uint16_t* As = stage_a(sa);
+    const uint16_t* Bs = stage_b(sb);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       fa[buf][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(As + swz<BK>(wm * 128 + 32 * i + fr, 2 * kk + fk)));
@@ -392,42 +396,33 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     for (int j = 0; j < NJ; ++j)
       fb[buf][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Bs + swz<BK>(wn * 32 * NJ + 32 * j + fr, 2 * kk + fk)));
   };
-  // wait until tile t has landed, given that tiles up to `last` are issued
-  auto wait_tile = [&](int t, int last) {
-    const int after = last - t;  // tiles issued after t
-    if constexpr (WF == WF_MXFP4) {
-      wait_vmcnt<0>();
-    } else {
-      if (NS >= 4 && after >= 3) wait_vmcnt<(NS >= 4 ? 3 * R : 0)>();
-      else if (NS >= 3 && after >= 2) wait_vmcnt<(NS >= 3 ? 2 * R : 0)>();
-      else if (NS >= 2 && after >= 1) wait_vmcnt<(NS >= 2 ? R : 0)>();
-      else wait_vmcnt<0>();
-    }
-  };
 
 #pragma unroll
-  for (int t = 0; t < NS; ++t) {
-    if (t < ktiles) {
-      issue_tile(t);
-      finish_tile(t);
-      fetch_regs(t);
-      land_regs(t);
+  for (int s = -NSB; s < 0; ++s) {
+    if (s + NS >= 0 && s + NS < ktiles) issue_a(s + NS, s + NS);
+    if (s + NSB < ktiles) {
+      issue_b(s + NSB, s + NSB);
+      finish_b(s + NSB);
     }
   }
-  if constexpr (REGS) wait_vmcnt<0>();
-  else wait_tile(0, min(NS - 1, ktiles - 1));
+  if (WF != WF_MXFP4 && ktiles >= NSB) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kPrologueWait)>();
+  else wait_vmcnt<0>();
   barrier_lds();
   if (tail_tile == 0) {
-    zero_tail(0);
+    zero_tail(0, 0, 0);
     barrier_lds();
   }
-  load_frags(0, 0, 0);
-  // One K tile.  STEADY: tiles kt+1 and kt+NS exist and kt+1 is no tail, so
-  // the step runs without branches (and the compiler's wait counting stays exact).
-  auto tile_step = [&](int kt, auto steady_tag) {
+  load_frags(0, 0, 0, 0);
+  // One K tile.  STEADY: every batch up to slot kt is whole and tile kt+1 is
+  // no tail, so the step runs without branches and with a counted wait.
+  // PH >= 0: kt % P == PH (stage indices are constants); PH < 0: run time.
+  auto tile_step = [&](int kt, auto steady_tag, auto phase_tag) __attribute__((always_inline)) {
     constexpr bool STEADY = decltype(steady_tag)::value;
-    const int st = kt % NS;
-    if (REGS && (STEADY || kt + NS < ktiles)) fetch_regs(kt + NS);
+    constexpr int PH = decltype(phase_tag)::value;
+    const int sa = PH >= 0 ? PH % NS : kt % NS;            // stages of tile kt (and of the batch issued now)
+    const int sb = PH >= 0 ? PH % NSB : kt % NSB;
+    const int sa1 = PH >= 0 ? (PH + 1) % NS : (kt + 1) % NS;  // stages of tile kt+1
+    const int sb1 = PH >= 0 ? (PH + 1) % NSB : (kt + 1) % NSB;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
@@ -435,21 +430,18 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         // this step's fragments were read a whole MFMA run ago; waiting for
         // them here keeps the wait from also covering the reads issued next
         wait_lgkmcnt0();
-        load_frags(st, kk + 1, cur ^ 1);
+        load_frags(sa, sb, kk + 1, cur ^ 1);
       } else if (STEADY || kt + 1 < ktiles) {
-        if constexpr (REGS) wait_vmcnt<0>();  // the registers of tile kt+NS
-        else if (STEADY) wait_tile(kt + 1, kt + NS - 1);
-        else wait_tile(kt + 1, min(kt + NS - 1, ktiles - 1));
+        if (STEADY && WF != WF_MXFP4) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kSteadyWait)>();
+        else wait_vmcnt<0>();
         barrier_lds();  // tile kt+1 is in LDS; every wavefront is done reading tile kt
         if (!STEADY && kt + 1 == tail_tile) {
-          zero_tail(kt + 1);
+          zero_tail(kt + 1, sa1, sb1);
           barrier_lds();
         }
-        if (STEADY || kt + NS < ktiles) {
-          issue_tile(kt + NS);
-          land_regs(kt + NS);
-        }
-        load_frags((kt + 1) % NS, 0, cur ^ 1);
+        if (STEADY || kt + NS < ktiles) issue_a(kt + NS, sa);
+        if (STEADY || kt + NSB < ktiles) issue_b(kt + NSB, sb);
+        load_frags(sa1, sb1, 0, cur ^ 1);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -458,13 +450,26 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (STEADY || kt + NS < ktiles) finish_tile(kt + NS);
+    if (STEADY || kt + NSB < ktiles) finish_b(sb);
+  };
+  // P consecutive steady tiles starting at kt0 (kt0 % P == 0)
+  auto steady_group = [&](int kt0, auto self, auto phase_tag) __attribute__((always_inline)) {
+    constexpr int PH = decltype(phase_tag)::value;
+    if constexpr (PH < P) {
+      tile_step(kt0 + PH, std::true_type{}, phase_tag);
+      self(kt0, self, std::integral_constant<int, PH + 1>{});
+    }
   };
   int kt = 0;
-  // steady state needs tile kt+NS < ktiles and no tail tile at kt+1
-  const int steady_end = ktiles - NS - (tail_tile >= 0 ? 1 : 0);
-  for (; kt < steady_end; ++kt) tile_step(kt, std::true_type{});
-  for (; kt < ktiles; ++kt) tile_step(kt, std::false_type{});
+  const int steady_end = ktiles - NSB - (tail_tile >= 0 ? 1 : 0);
+  if constexpr (WF == WF_MXFP4) {
+    // MXFP4 waits for every copy at each tile boundary anyway (its weight
+    // codes come through registers), and unrolling would spill registers
+    for (; kt < steady_end; ++kt) tile_step(kt, std::true_type{}, std::integral_constant<int, -1>{});
+  } else {
+    for (; kt + P <= steady_end; kt += P) steady_group(kt, steady_group, std::integral_constant<int, 0>{});
+  }
+  for (; kt < ktiles; ++kt) tile_step(kt, std::false_type{}, std::integral_constant<int, -1>{});
   wait_vmcnt<0>();
   barrier_lds();  // every wavefront is done with the stages before they are reused
 
@@ -561,8 +566,8 @@ hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.ldo = L.F_max();
   m.n_tiles = (L.F_max() + 127) / 128;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
-  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, true, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
-  else mfma_gemm_kernel<WF_BF16, true, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, true, 4, kBK, kStages, kStages><<<grid, kThreads, 0, s>>>(m);
+  else mfma_gemm_kernel<WF_BF16, true, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
 
@@ -584,11 +589,11 @@ hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.n_tiles = narrow ? t192 : t256;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
   if (L.wfmt == WF_MXFP4) {
-    if (narrow) mfma_gemm_kernel<WF_MXFP4, false, 3, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
-    else mfma_gemm_kernel<WF_MXFP4, false, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+    if (narrow) mfma_gemm_kernel<WF_MXFP4, false, 3, kBK, kStages, kStages><<<grid, kThreads, 0, s>>>(m);
+    else mfma_gemm_kernel<WF_MXFP4, false, 4, kBK, kStages, kStages><<<grid, kThreads, 0, s>>>(m);
   } else {
-    if (narrow) mfma_gemm_kernel<WF_BF16, false, 3, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
-    else mfma_gemm_kernel<WF_BF16, false, 4, kBK, kStages><<<grid, kThreads, 0, s>>>(m);
+    if (narrow) mfma_gemm_kernel<WF_BF16, false, 3, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
+    else mfma_gemm_kernel<WF_BF16, false, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   }
   return hipGetLastError();
 }
