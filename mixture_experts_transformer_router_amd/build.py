@@ -56,6 +56,15 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # A host pass can drop a kernel's launch stub without a diagnostic (then
+    # the library links but cannot be loaded): refuse such a build here.
+    nm = shutil.which("nm")
+    if nm:
+        r = subprocess.run([nm, "-u", tmp], capture_output=True, text=True)
+        missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError(f"link left kernel stubs undefined: {missing[:4]}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")

@@ -55,6 +55,13 @@ constexpr int kGroupM = MOE_GEMM_GROUP_M;  // row tiles walked together within a
 constexpr int kBK = MOE_GEMM_BK;           // K elements per LDS stage
 constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages of the A operand
 constexpr int kStagesB = MOE_GEMM_STAGES_B;  // LDS stages of the (dense) B operand
+#ifndef MOE_GEMM_INTERLEAVE
+#define MOE_GEMM_INTERLEAVE 1
+#endif
+// 1: the copies issued at a tile boundary alternate with that step's MFMAs
+// (instead of one burst ahead of them), so the address unit works through
+// them while the matrix cores run.
+constexpr bool kInterleave = MOE_GEMM_INTERLEAVE != 0;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -292,13 +299,23 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
     return (swz<BK>(row, ld_phys) - row * BK) >> 3;  // XOR is an involution
   };
+  // round i of the copies of A / (dense) B tile kt into the stage at As / Bs.
+  // (The stage pointer comes from the caller: a lambda that calls stage_a()
+  // from inside another lambda makes this hipcc's host pass drop the kernel
+  // stubs without a diagnostic.)
+  auto copy_a = [&](int kt, uint16_t* As, int i) __attribute__((always_inline)) {
+    const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
+    __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (4 * i + wv) * 512, 16, 0, 0);
+  };
+  auto copy_b = [&](int kt, uint16_t* Bs, int i) __attribute__((always_inline)) {
+    const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
+    const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
+    __builtin_amdgcn_global_load_lds(wsrc + (size_t)(b_row[i] >> 1) * K + k, Bs + (4 * i + wv) * 512, 16, 0, 0);
+  };
   auto issue_a = [&](int kt, int sa) __attribute__((always_inline)) {
     uint16_t* As = stage_a(sa);
 #pragma unroll
-    for (int i = 0; i < RA; ++i) {
-      const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
-      __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (4 * i + wv) * 512, 16, 0, 0);
-    }
+    for (int i = 0; i < RA; ++i) copy_a(kt, As, i);
   };
   auto issue_b = [&](int kt, int sb) __attribute__((always_inline)) {
     if constexpr (WF == WF_MXFP4) {
@@ -311,11 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     } else {
       uint16_t* Bs = stage_b(sb);
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
-        const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
-        __builtin_amdgcn_global_load_lds(wsrc + (size_t)(b_row[i] >> 1) * K + k, Bs + (4 * i + wv) * 512, 16, 0, 0);
-      }
+      for (int i = 0; i < RB; ++i) copy_b(kt, Bs, i);
     }
   };
   // MXFP4 only: decode the staged codes of row tid into the tile's stage
@@ -438,6 +451,29 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         if (!STEADY && kt + 1 == tail_tile) {
           zero_tail(kt + 1, sa1, sb1);
           barrier_lds();
+        }
+        if (STEADY && kInterleave && WF != WF_MXFP4) {
+          // the batch alternates with this step's MFMAs
+          uint16_t* As = stage_a(sa);
+          uint16_t* Bs = stage_b(sb);
+          load_frags(sa1, sb1, 0, cur ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+              const int m = i * NJ + j;
+              if (m < RA) copy_a(kt + NS, As, m);
+              else if (m - RA < RB) copy_b(kt + NSB, Bs, m - RA);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+          for (int m = 4 * NJ; m < RA + RB; ++m) {
+            if (m < RA) copy_a(kt + NS, As, m);
+            else copy_b(kt + NSB, Bs, m - RA);
+          }
+          continue;
         }
         if (STEADY || kt + NS < ktiles) issue_a(kt + NS, sa);
         if (STEADY || kt + NSB < ktiles) issue_b(kt + NSB, sb);
