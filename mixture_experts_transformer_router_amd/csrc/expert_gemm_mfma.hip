@@ -62,6 +62,19 @@ constexpr int kStagesB = MOE_GEMM_STAGES_B;  // LDS stages of the (dense) B oper
 // (instead of one burst ahead of them), so the address unit works through
 // them while the matrix cores run.
 constexpr bool kInterleave = MOE_GEMM_INTERLEAVE != 0;
+#ifndef MOE_GEMM_INTERLEAVE_LDS
+#define MOE_GEMM_INTERLEAVE_LDS 1
+#endif
+// Within a tile, the fragment reads for step kk+1 follow the MFMAs of step
+// kk one by one (1: after each of the first 4 + NJ MFMAs; 2: after every
+// other MFMA) instead of coming as one burst ahead of them (0).
+constexpr int kInterleaveLds = MOE_GEMM_INTERLEAVE_LDS;
+#ifndef MOE_GEMM_BOUNDARY_READS
+#define MOE_GEMM_BOUNDARY_READS 1
+#endif
+// At a tile boundary the first fragments of the next tile are read as one
+// burst right after the barrier (0) or one after each MFMA/copy pair (1).
+constexpr bool kBoundaryReadsInterleaved = MOE_GEMM_BOUNDARY_READS != 0;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -144,6 +157,20 @@ __device__ __forceinline__ float quad_xor1(float v) {
 }
 __device__ __forceinline__ float quad_xor2(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+
+// The expert activation with its kind fixed at compile time (no per-element
+// branch); the clamps are single v_med3_f32 (the C ABI guarantees limit > 0).
+// act 0: clipped SwiGLU, act 1: SiLU-GLU, as expert_act().
+template <int ACT>
+__device__ __forceinline__ float expert_act_t(float g, float u, float alpha, float limit) {
+  if constexpr (ACT == 0) {
+    const float gc = __builtin_amdgcn_fmed3f(g, 0.f, limit);
+    const float uc = __builtin_amdgcn_fmed3f(u, -limit, limit);
+    return gc * sigmoidf_(alpha * gc) * uc;
+  } else {
+    return g * sigmoidf_(g) * u;
+  }
 }
 
 // 8 e2m1 codes (one 32-bit word, element 0 in the low nibble) times the block
@@ -399,6 +426,13 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   const int fr = lane & 31, fk = lane >> 5;
 
   bf16x8_t fa[2][4], fb[2][NJ];
+  // fragment r of step kk (r < 4: A row block r; else B column block r - 4)
+  auto load_frag = [&](const uint16_t* As, const uint16_t* Bs, int kk, int buf, int r) __attribute__((always_inline)) {
+    if (r < 4)
+      fa[buf][r] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(As + swz<BK>(wm * 128 + 32 * r + fr, 2 * kk + fk)));
+    else
+      fb[buf][r - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Bs + swz<BK>(wn * 32 * NJ + 32 * (r - 4) + fr, 2 * kk + fk)));
+  };
   auto load_frags = [&](int sa, int sb, int kk, int buf) __attribute__((always_inline)) {
     const uint16_t* As = stage_a(sa);
     const uint16_t* Bs = stage_b(sb);
@@ -443,6 +477,24 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         // this step's fragments were read a whole MFMA run ago; waiting for
         // them here keeps the wait from also covering the reads issued next
         wait_lgkmcnt0();
+        if constexpr (kInterleaveLds != 0) {
+          const uint16_t* As = stage_a(sa);
+          const uint16_t* Bs = stage_b(sb);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+              const int m = i * NJ + j;
+              if (kInterleaveLds == 1 && m < 4 + NJ) load_frag(As, Bs, kk + 1, cur ^ 1, m);
+              if (kInterleaveLds == 2 && (m & 1) && (m >> 1) < 4 + NJ) load_frag(As, Bs, kk + 1, cur ^ 1, m >> 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+          for (int r = kInterleaveLds == 1 ? 4 * NJ : 2 * NJ; r < 4 + NJ; ++r) load_frag(As, Bs, kk + 1, cur ^ 1, r);
+          continue;
+        }
         load_frags(sa, sb, kk + 1, cur ^ 1);
       } else if (STEADY || kt + 1 < ktiles) {
         if (STEADY && WF != WF_MXFP4) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kSteadyWait)>();
@@ -456,7 +508,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
           // the batch alternates with this step's MFMAs
           uint16_t* As = stage_a(sa);
           uint16_t* Bs = stage_b(sb);
-          load_frags(sa1, sb1, 0, cur ^ 1);
+          const uint16_t* As1 = stage_a(sa1);
+          const uint16_t* Bs1 = stage_b(sb1);
+          if constexpr (!kBoundaryReadsInterleaved) load_frags(sa1, sb1, 0, cur ^ 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -466,12 +520,17 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
               const int m = i * NJ + j;
               if (m < RA) copy_a(kt + NS, As, m);
               else if (m - RA < RB) copy_b(kt + NSB, Bs, m - RA);
+              if (kBoundaryReadsInterleaved && m < 4 + NJ) load_frag(As1, Bs1, 0, cur ^ 1, m);
               __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
           for (int m = 4 * NJ; m < RA + RB; ++m) {
             if (m < RA) copy_a(kt + NS, As, m);
             else copy_b(kt + NSB, Bs, m - RA);
+          }
+          if constexpr (kBoundaryReadsInterleaved) {
+#pragma unroll
+            for (int r = 4 * NJ; r < 4 + NJ; ++r) load_frag(As1, Bs1, 0, cur ^ 1, r);
           }
           continue;
         }
@@ -527,44 +586,50 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     bv0[j] = (bias0 && c < N) ? bf16_to_f32(bias0[(size_t)e * N + c]) : 0.f;
     bv1[j] = (GATED && bias1 && c < N) ? bf16_to_f32(bias1[(size_t)e * N + c]) : 0.f;
   }
+  // the activation is a template argument of the loops (one copy per kind)
+  auto epilogue = [&](auto act_tag) __attribute__((always_inline)) {
+    constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {      // groups of 4 consecutive rows (q = 4 g .. 4 g + 3)
-      const int row_base = wm * 128 + 32 * i + 8 * g + 4 * fk;
+      for (int g = 0; g < 4; ++g) {      // groups of 4 consecutive rows (q = 4 g .. 4 g + 3)
+        const int row_base = wm * 128 + 32 * i + 8 * g + 4 * fk;
 #pragma unroll
-      for (int j = 0; j < OJ; ++j) {
-        float v[4];
+        for (int j = 0; j < OJ; ++j) {
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 4 * g + r;
-          if constexpr (GATED) v[r] = expert_act(act, acc[i][2 * j][q] + bv0[j], acc[i][2 * j + 1][q] + bv1[j], a.alpha, a.limit);
-          else v[r] = acc[i][j][q] + bv0[j];
-        }
-        // transpose within the lane quad: afterwards lane c4 holds row
-        // row_base + c4, columns (fr & ~3) .. +3
-        {
-          const bool odd = c4 & 1;
-          const float s0 = odd ? v[0] : v[1], s1 = odd ? v[2] : v[3];
-          const float r0_ = quad_xor1(s0), r1_ = quad_xor1(s1);
-          if (odd) { v[0] = r0_; v[2] = r1_; } else { v[1] = r0_; v[3] = r1_; }
-          // lane even: v = [row 0 c, row 0 c+1, row 2 c, row 2 c+1]; odd: rows 1 and 3
-        }
-        {
-          const bool hi = c4 & 2;
-          const float s0 = hi ? v[0] : v[2], s1 = hi ? v[1] : v[3];
-          const float r0_ = quad_xor2(s0), r1_ = quad_xor2(s1);
-          if (hi) { v[0] = r0_; v[1] = r1_; } else { v[2] = r0_; v[3] = r1_; }
-        }
-        const int row = r0 + row_base + c4;
-        const int col = colj[j] + (fr & ~3);
-        if (row < r_end && col < N) {
-          *reinterpret_cast<uint2*>(a.out + (size_t)row * a.ldo + col) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          for (int r = 0; r < 4; ++r) {
+            const int q = 4 * g + r;
+            if constexpr (GATED) v[r] = expert_act_t<ACT>(acc[i][2 * j][q] + bv0[j], acc[i][2 * j + 1][q] + bv1[j], a.alpha, a.limit);
+            else v[r] = acc[i][j][q] + bv0[j];
+          }
+          // transpose within the lane quad: afterwards lane c4 holds row
+          // row_base + c4, columns (fr & ~3) .. +3
+          {
+            const bool odd = c4 & 1;
+            const float s0 = odd ? v[0] : v[1], s1 = odd ? v[2] : v[3];
+            const float r0_ = quad_xor1(s0), r1_ = quad_xor1(s1);
+            if (odd) { v[0] = r0_; v[2] = r1_; } else { v[1] = r0_; v[3] = r1_; }
+            // lane even: v = [row 0 c, row 0 c+1, row 2 c, row 2 c+1]; odd: rows 1 and 3
+          }
+          {
+            const bool hi = c4 & 2;
+            const float s0 = hi ? v[0] : v[2], s1 = hi ? v[1] : v[3];
+            const float r0_ = quad_xor2(s0), r1_ = quad_xor2(s1);
+            if (hi) { v[0] = r0_; v[1] = r1_; } else { v[2] = r0_; v[3] = r1_; }
+          }
+          const int row = r0 + row_base + c4;
+          const int col = colj[j] + (fr & ~3);
+          if (row < r_end && col < N) {
+            *reinterpret_cast<uint2*>(a.out + (size_t)row * a.ldo + col) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
         }
       }
     }
-  }
+  };
+  if (!GATED || act == 0) epilogue(std::integral_constant<int, 0>{});
+  else epilogue(std::integral_constant<int, 1>{});
 }
 
 MfmaArgs base_args(const Layer& L, const Work& W) {
