@@ -55,6 +55,9 @@ constexpr int kGroupM = MOE_GEMM_GROUP_M;  // row tiles walked together within a
 constexpr int kBK = MOE_GEMM_BK;           // K elements per LDS stage
 constexpr int kStages = MOE_GEMM_STAGES;   // LDS stages of the A operand
 constexpr int kStagesB = MOE_GEMM_STAGES_B;  // LDS stages of the (dense) B operand
+// MXFP4 weights: 64-wide stages (a thread decodes 32 code bytes per stage), 2 LDS stages
+constexpr int kBKMx = 64;
+constexpr int kStagesMx = 2;
 #ifndef MOE_GEMM_INTERLEAVE
 #define MOE_GEMM_INTERLEAVE 1
 #endif
@@ -204,15 +207,24 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   static_assert(NS >= 2 && NSB >= NS && NSB <= NS + 1, "LDS stages");
   static_assert(WF != WF_MXFP4 || NSB == NS, "MXFP4 weights use symmetric stages");
   static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "copy rounds");
-  static_assert(NS <= 3 && NSB <= 4, "stage variables");
+  static_assert(NS <= 5 && NSB <= 5, "stage variables");
   // One LDS variable per stage: the compiler tells copies into one stage from
   // reads of another only by the variable they address (see the pipeline).
-  __shared__ uint16_t lds_a0[BM * BK], lds_a1[BM * BK], lds_a2[NS > 2 ? BM * BK : 8];
-  __shared__ uint16_t lds_b0[BN * BK], lds_b1[BN * BK], lds_b2[NSB > 2 ? BN * BK : 8], lds_b3[NSB > 3 ? BN * BK : 8];
+  // Unused stages (size 8) are never referenced and take no LDS.
+  __shared__ uint16_t lds_a0[BM * BK], lds_a1[BM * BK], lds_a2[NS > 2 ? BM * BK : 8],
+      lds_a3[NS > 3 ? BM * BK : 8], lds_a4[NS > 4 ? BM * BK : 8];
+  __shared__ uint16_t lds_b0[BN * BK], lds_b1[BN * BK], lds_b2[NSB > 2 ? BN * BK : 8],
+      lds_b3[NSB > 3 ? BN * BK : 8], lds_b4[NSB > 4 ? BN * BK : 8];
   // MXFP4 (every wait drains the copies anyway): one array per operand
   __shared__ uint16_t lds_mx_a[NS][BM * BK], lds_mx_b[NS][BN * BK];
   auto stage_a = [&](int st) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (WF == WF_MXFP4) return lds_mx_a[st];
+    if constexpr (NS > 4) {
+      if (st == 4) return lds_a4;
+    }
+    if constexpr (NS > 3) {
+      if (st == 3) return lds_a3;
+    }
     if constexpr (NS > 2) {
       if (st == 2) return lds_a2;
     }
@@ -220,6 +232,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   };
   auto stage_b = [&](int st) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (WF == WF_MXFP4) return lds_mx_b[st];
+    if constexpr (NSB > 4) {
+      if (st == 4) return lds_b4;
+    }
     if constexpr (NSB > 3) {
       if (st == 3) return lds_b3;
     }
@@ -667,7 +682,7 @@ hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.ldo = L.F_max();
   m.n_tiles = (L.F_max() + 127) / 128;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
-  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, true, 4, kBK, kStages, kStages><<<grid, kThreads, 0, s>>>(m);
+  if (L.wfmt == WF_MXFP4) mfma_gemm_kernel<WF_MXFP4, true, 4, kBKMx, kStagesMx, kStagesMx><<<grid, kThreads, 0, s>>>(m);
   else mfma_gemm_kernel<WF_BF16, true, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
@@ -690,8 +705,8 @@ hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.n_tiles = narrow ? t192 : t256;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
   if (L.wfmt == WF_MXFP4) {
-    if (narrow) mfma_gemm_kernel<WF_MXFP4, false, 3, kBK, kStages, kStages><<<grid, kThreads, 0, s>>>(m);
-    else mfma_gemm_kernel<WF_MXFP4, false, 4, kBK, kStages, kStages><<<grid, kThreads, 0, s>>>(m);
+    if (narrow) mfma_gemm_kernel<WF_MXFP4, false, 3, kBKMx, kStagesMx, kStagesMx><<<grid, kThreads, 0, s>>>(m);
+    else mfma_gemm_kernel<WF_MXFP4, false, 4, kBKMx, kStagesMx, kStagesMx><<<grid, kThreads, 0, s>>>(m);
   } else {
     if (narrow) mfma_gemm_kernel<WF_BF16, false, 3, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
     else mfma_gemm_kernel<WF_BF16, false, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
