@@ -177,21 +177,20 @@ __device__ __forceinline__ float expert_act_t(float g, float u, float alpha, flo
 }
 
 // 8 e2m1 codes (one 32-bit word, element 0 in the low nibble) times the block
-// scale 2^(s - 127) -> 8 bf16.
+// scale 2^(s - 127) -> 8 bf16 (element 0 in the low half of the first word).
+// gfx950's v_cvt_scalef32_pk_bf16_fp4 converts the two codes of one byte
+// (low nibble to the low half) with an fp32 scale; every product is a bf16
+// number, so the result is exact.  The NaN scale (s = 255) is set explicitly.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, uint32_t s) {
-  // fp32 bit patterns of 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  constexpr uint32_t kMag[8] = {0x00000000u, 0x3f000000u, 0x3f800000u, 0x3fc00000u,
-                                0x40000000u, 0x40400000u, 0x40800000u, 0x40c00000u};
-  const float scale = s == 0 ? __uint_as_float(0x00400000u)
-                             : (s == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(s << 23));
-  uint32_t h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = (codes >> (4 * i)) & 15u;
-    const float v = __uint_as_float(kMag[c & 7u] | ((c & 8u) << 28)) * scale;
-    h[i] = __float_as_uint(v) >> 16;  // exact: the low 16 bits are zero
-  }
-  return u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  const float scale = __uint_as_float(s == 0 ? 0x00400000u : (s << 23));
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  if (s == 255u) r = u32x4_t{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+  return r;
 }
 
 // NJ = 32-column result tiles per wavefront (block columns BN = 64 NJ);
@@ -373,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       for (int i = 0; i < RB; ++i) copy_b(kt, Bs, i);
     }
   };
-  // MXFP4 only: decode the staged codes of row tid into the tile's stage
+  // MXFP4 only: decode the codes in registers (row tid) into stage sb
   auto finish_b = [&](int sb) __attribute__((always_inline)) {
     if constexpr (WF == WF_MXFP4) {
       uint16_t* Bs = stage_b(sb);
@@ -464,7 +463,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     if (s + NS >= 0 && s + NS < ktiles) issue_a(s + NS, s + NS);
     if (s + NSB < ktiles) {
       issue_b(s + NSB, s + NSB);
-      finish_b(s + NSB);
+      // MXFP4: tile 0 is decoded now; every later tile t at the end of tile
+      // t-1, a whole tile after its codes were requested
+      if (s + NSB == 0) finish_b(0);
     }
   }
   if (WF != WF_MXFP4 && ktiles >= NSB) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kPrologueWait)>();
@@ -512,6 +513,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         }
         load_frags(sa, sb, kk + 1, cur ^ 1);
       } else if (STEADY || kt + 1 < ktiles) {
+        // MXFP4: decode tile kt+1 into its stage (free since the barrier that
+        // ended tile kt-1) from the codes requested at that barrier
+        if constexpr (WF == WF_MXFP4) finish_b(sb1);
         if (STEADY && WF != WF_MXFP4) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kSteadyWait)>();
         else wait_vmcnt<0>();
         barrier_lds();  // tile kt+1 is in LDS; every wavefront is done reading tile kt
@@ -560,7 +564,6 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (STEADY || kt + NSB < ktiles) finish_b(sb);
   };
   // P consecutive steady tiles starting at kt0 (kt0 % P == 0)
   auto steady_group = [&](int kt0, auto self, auto phase_tag) __attribute__((always_inline)) {
