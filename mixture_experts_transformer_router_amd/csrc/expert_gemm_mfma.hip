@@ -702,9 +702,12 @@ hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) {
   m.N = L.d; m.K = L.F; m.N_sh = L.d; m.K_sh = L.F_sh;
   m.out = static_cast<uint16_t*>(W.y);
   m.ldo = L.d;
-  // 192-column tiles when they waste fewer columns than 256-column ones
+  // Column tile width 192 or 256, whichever copies fewer bytes into LDS:
+  // per K step a row tile copies (256 + width) rows for each column tile.
+  // (The copies bound this kernel, so padded columns cost less than narrow
+  // tiles: d = 2880 takes 12 tiles of 256 rather than 15 of 192.)
   const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
-  const bool narrow = t192 * 192 < t256 * 256;
+  const bool narrow = t192 * (256 + 192) < t256 * (256 + 256);
   m.n_tiles = narrow ? t192 : t256;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
   if (L.wfmt == WF_MXFP4) {

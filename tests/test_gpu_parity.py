@@ -55,6 +55,9 @@ SMALL = [
     W.GPTOSS_DECODE.scaled(T=65, d=64, d_ff=136, E=6, k=6, name="k_equals_E"),
     W.GPTOSS_DECODE.scaled(T=130, d=128, d_ff=64, E=256, k=16, name="E256_k16"),
     W.GPTOSS_PREFILL.scaled(T=1000, d=384, d_ff=320, name="prefill_zipf_small"),
+    # grouped-GEMM path with K ragged against the 64-wide stages and many K
+    # tiles (steady, unrolled and tail tiles): d = 1000, d_ff = 712
+    W.GPTOSS_PREFILL.scaled(T=300, d=1000, d_ff=712, E=8, k=2, name="prefill_ragged_k"),
     W.GPTOSS_MXFP4.scaled(T=150, d=256, d_ff=160, E=8, k=2, name="mxfp4_small"),
     W.TINY_F32.scaled(T=300, d=96, d_ff=80, E=16, k=3, name="f32_T300"),
     W.GLM4_MOE_LITE.scaled(T=300, d=256, d_ff=192, E=64, k=6, d_ff_shared=128, name="glm_small"),
