@@ -174,6 +174,8 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   W->idx = static_cast<int32_t*>(take(P * 4));
   W->w = static_cast<float*>(take(P * 4));
   W->hist = static_cast<int32_t*>(take(nblk * L.E * 4));
+  const bool split_route = L.dt != MOE_F32 && L.T <= kDecodeMaxTokens;
+  W->route_part = static_cast<float*>(take(split_route ? (size_t)kRouteSplitK * 16 * L.E * 4 : 0));
   W->offsets = static_cast<int32_t*>(take((Eall + 1) * 4));
   W->tile_prefix = static_cast<int32_t*>(take((Eall + 1) * 4));
   W->tile_prefix_big = static_cast<int32_t*>(take((Eall + 1) * 4));

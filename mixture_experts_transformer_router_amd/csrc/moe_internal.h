@@ -20,6 +20,10 @@ constexpr int kMinRouteTokens = 16;
 // Largest token count that takes the weight-streaming (decode) expert path:
 // an expert then has at most this many rows, one MFMA column tile.
 constexpr int kDecodeMaxTokens = 16;
+// Few-token (T <= kDecodeMaxTokens, bf16) router: the input dimension is
+// split over this many blocks per 16-expert group, whose partial logits a
+// second kernel adds in a fixed order before choosing the experts.
+constexpr int kRouteSplitK = 16;
 // Rows per M-tile of the tiled grouped GEMMs (the permute kernel writes the
 // per-expert tile prefix for this size).
 constexpr int kTileM = 64;
@@ -74,6 +78,7 @@ struct Work {
   int32_t* idx = nullptr;          // [T*k] chosen experts
   float* w = nullptr;              // [T*k] routing weights
   int32_t* hist = nullptr;         // [n_route_blocks * E] per-block expert counts
+  float* route_part = nullptr;     // few-token router: [kRouteSplitK][16][E] partial logits
   int32_t* offsets = nullptr;      // [E_all + 1] row offsets of each expert (shared last)
   int32_t* tile_prefix = nullptr;  // [E_all + 1] first 64-row M-tile of each expert
   int32_t* tile_prefix_big = nullptr;  // [E_all + 1] first 256-row M-tile of each expert

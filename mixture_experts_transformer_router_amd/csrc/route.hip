@@ -4,9 +4,11 @@
 // Logits l[t,e] = sum_i x[t,i] Wr[e,i] + br[e], accumulated in fp32 (router
 // kernel and bias: MaxText GPT-OSS weight mapping, "MoE Router";
 // glm4_moe_lite.go, MoEGate.Forward).
-//   bf16: a [16 tokens x 16 experts] tile per MFMA; the block's 8 wavefronts
-//         split the input dimension and their partial tiles are added in
-//         wavefront order (deterministic).
+//   bf16: a [16 tokens x 16 experts] tile per MFMA; the block's wavefronts
+//         split the input dimension and their partial tiles are added in a
+//         fixed order (deterministic).  For T <= 16 the input dimension is
+//         also split over blocks (route_split_logits_kernel) and a one-block
+//         kernel adds the slices in order and chooses.
 //   fp32: 64 tokens per block on the vector ALUs, the input dimension
 //         streaming through LDS in chunks of 32.
 //
@@ -155,13 +157,23 @@ __device__ void choose_experts(const RouteArgs& a, float* lg, int t, int lane, i
 
 // ---- bf16: MFMA logits -----------------------------------------------------
 constexpr int kMfmaTokens = 16;
-constexpr int kMfmaWaves = 8;
+#ifndef MOE_ROUTE_UNROLL
+#define MOE_ROUTE_UNROLL 4
+#endif
+#ifndef MOE_ROUTE_TREE
+#define MOE_ROUTE_TREE 1
+#endif
 
-// EG = groups of 16 experts (E <= 16 * EG).
-template <int EG>
-__global__ __launch_bounds__(64 * kMfmaWaves) void route_mfma_kernel(RouteArgs a) {
+// EG = groups of 16 experts (E <= 16 * EG).  WAVES split the input dimension.
+// Their partial tiles are added either in wavefront order (sequential) or,
+// with TREE, pairwise in a fixed tree (wave w += wave w + n/2 for n = WAVES,
+// WAVES/2, ..., 2), both independent of timing.
+template <int EG, int WAVES, bool TREE>
+__global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   constexpr int EP = 16 * EG;
+  constexpr int kMfmaWaves = WAVES;
   __shared__ float lg[kMfmaTokens][EP + 1];
+  __shared__ float part[TREE ? WAVES / 2 : 1][TREE ? EG * 4 * 64 : 1];
   __shared__ int cnt[EP];
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
@@ -177,31 +189,79 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void route_mfma_kernel(RouteArgs a
   f32x4_t acc[EG];
 #pragma unroll
   for (int g = 0; g < EG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Batches of B steps: all loads of a batch are issued first, at clamped
+  // (always valid) addresses, and masked afterwards, so no load waits behind
+  // a branch or another step's MFMA.
   const int steps = (d + 31) / 32;
-#pragma unroll 2
-  for (int s = wv; s < steps; s += kMfmaWaves) {
-    const int k = 32 * s + 8 * kg;
-    const bool k_ok = k < d;  // d % 8 == 0: a lane's 8 elements are all in or all out
-    const bf16x8_t av = (tok_ok && k_ok) ? load_bf16x8(xr + k) : zero_bf16x8();
+  constexpr int B = MOE_ROUTE_UNROLL;
+  const uint16_t* wrow[EG];
+  bool e_ok[EG];
 #pragma unroll
-    for (int g = 0; g < EG; ++g) {
-      const int e = 16 * g + (lane & 15);
-      const bf16x8_t bv = (e < E && k_ok) ? load_bf16x8(wr + (size_t)e * d + k) : zero_bf16x8();
-      acc[g] = mfma_16x16x32(av, bv, acc[g]);
+  for (int g = 0; g < EG; ++g) {
+    const int e = 16 * g + (lane & 15);
+    e_ok[g] = e < E;
+    wrow[g] = wr + (size_t)(e_ok[g] ? e : 0) * d;
+  }
+  for (int s0 = wv; s0 < steps; s0 += B * kMfmaWaves) {
+    bf16x8_t av[B], bv[B][EG];
+    bool ok[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int k = 32 * (s0 + u * kMfmaWaves) + 8 * kg;
+      ok[u] = k < d;  // d % 8 == 0: a lane's 8 elements are all in or all out
+      const int kc = ok[u] ? k : 0;
+      av[u] = load_bf16x8(xr + kc);
+#pragma unroll
+      for (int g = 0; g < EG; ++g) bv[u][g] = load_bf16x8(wrow[g] + kc);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const bf16x8_t a_u = (tok_ok && ok[u]) ? av[u] : zero_bf16x8();
+#pragma unroll
+      for (int g = 0; g < EG; ++g) acc[g] = mfma_16x16x32(a_u, e_ok[g] ? bv[u][g] : zero_bf16x8(), acc[g]);
     }
   }
-  // partial tiles added in wavefront order
-  for (int w = 0; w < kMfmaWaves; ++w) {
-    if (wv == w) {
+  if constexpr (TREE) {
+    // fixed pairwise tree: in round n, waves n/2 .. n-1 hand their tiles to
+    // waves 0 .. n/2-1, which add them to their own
+#pragma unroll
+    for (int n = WAVES; n > 1; n /= 2) {
+      if (wv >= n / 2 && wv < n) {
+#pragma unroll
+        for (int g = 0; g < EG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[wv - n / 2][(g * 4 + r) * 64 + lane] = acc[g][r];
+      }
+      __syncthreads();
+      if (wv < n / 2) {
+#pragma unroll
+        for (int g = 0; g < EG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[g][r] += part[wv][(g * 4 + r) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (wv == 0) {
 #pragma unroll
       for (int g = 0; g < EG; ++g)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * kg + r, col = 16 * g + (lane & 15);
-          lg[row][col] = (w == 0) ? acc[g][r] : lg[row][col] + acc[g][r];
-        }
+        for (int r = 0; r < 4; ++r) lg[4 * kg + r][16 * g + (lane & 15)] = acc[g][r];
     }
     __syncthreads();
+  } else {
+    // partial tiles added in wavefront order
+    for (int w = 0; w < kMfmaWaves; ++w) {
+      if (wv == w) {
+#pragma unroll
+        for (int g = 0; g < EG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 4 * kg + r, col = 16 * g + (lane & 15);
+            lg[row][col] = (w == 0) ? acc[g][r] : lg[row][col] + acc[g][r];
+          }
+      }
+      __syncthreads();
+    }
   }
   for (int i = tid; i < kMfmaTokens * E; i += 64 * kMfmaWaves) {
     const int r = i / E, e = i % E;
@@ -215,6 +275,74 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void route_mfma_kernel(RouteArgs a
   }
   __syncthreads();
   for (int e = tid; e < E; e += 64 * kMfmaWaves) a.hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// ---- bf16, few tokens (T <= 16): split-K logits, then the choice --------------
+// A single block would read the whole router through one CU's memory
+// pipeline; here block (g, ks) computes the [16 tokens x 16 experts] tile of
+// expert group g over the ks-th of kRouteSplitK contiguous slices of the input
+// dimension (one wavefront, all loads of a slice issued before its MFMAs) and
+// stores it to part[ks].  route_choose_kernel adds the slices in ks order.
+constexpr int kSplitSteps = 8;  // 32-element steps loaded ahead by one wavefront
+
+__global__ __launch_bounds__(64) void route_split_logits_kernel(RouteArgs a, float* part) {
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
+  const int g = blockIdx.x, ks = blockIdx.y, lane = threadIdx.x;
+  const int kg = lane >> 4, d = a.d, E = a.E;
+  const int tok = lane & 15, e = 16 * g + (lane & 15);
+  const bool tok_ok = tok < a.T, e_ok = e < E;
+  const uint16_t* xr = x + (size_t)(tok_ok ? tok : 0) * d;
+  const uint16_t* wrow = wr + (size_t)(e_ok ? e : 0) * d;
+  const int steps = (d + 31) / 32;
+  const int s_begin = steps * ks / kRouteSplitK, s_end = steps * (ks + 1) / kRouteSplitK;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = s_begin; s0 < s_end; s0 += kSplitSteps) {
+    bf16x8_t av[kSplitSteps], bv[kSplitSteps];
+    bool ok[kSplitSteps];
+#pragma unroll
+    for (int u = 0; u < kSplitSteps; ++u) {
+      const int k = 32 * (s0 + u) + 8 * kg;
+      ok[u] = s0 + u < s_end && k < d;  // d % 8 == 0: a lane's 8 elements are all in or all out
+      const int kc = ok[u] ? k : 0;
+      av[u] = load_bf16x8(xr + kc);
+      bv[u] = load_bf16x8(wrow + kc);
+    }
+#pragma unroll
+    for (int u = 0; u < kSplitSteps; ++u)
+      acc = mfma_16x16x32((tok_ok && ok[u]) ? av[u] : zero_bf16x8(), (e_ok && ok[u]) ? bv[u] : zero_bf16x8(), acc);
+  }
+  // lane holds tokens 4 kg .. 4 kg + 3 of expert e
+  if (e_ok) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[((size_t)ks * 16 + 4 * kg + r) * E + e] = acc[r];
+  }
+}
+
+// One block: logits = sum of the kRouteSplitK slices in order + bias, then one
+// wavefront per token chooses its experts; writes the block's expert counts.
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_choose_kernel(RouteArgs a, const float* part) {
+  __shared__ float lg[16][64 * VPL + 1];
+  __shared__ int cnt[64 * VPL];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = a.E;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  for (int i = tid; i < a.T * E; i += 1024) {
+    const int t = i / E, e = i % E;
+    float pv[kRouteSplitK];  // all slices loaded first, then added in order
+#pragma unroll
+    for (int ks = 0; ks < kRouteSplitK; ++ks) pv[ks] = part[((size_t)ks * 16 + t) * E + e];
+    float v = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kRouteSplitK; ++ks) v += pv[ks];
+    if (a.br) v += bf16_to_f32(static_cast<const uint16_t*>(a.br)[e]);
+    lg[t][e] = v;
+  }
+  __syncthreads();
+  if (wv < a.T) choose_experts<VPL>(a, lg[wv], wv, lane, cnt);
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) a.hist[e] = cnt[e];
 }
 
 // ---- fp32: vector-ALU logits -------------------------------------------------
@@ -298,13 +426,20 @@ hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
     else if (L.E <= 32) route_valu_kernel<8><<<nblk, kValuThreads, 0, s>>>(a);
     else if (L.E <= 64) route_valu_kernel<16><<<nblk, kValuThreads, 0, s>>>(a);
     else route_valu_kernel<64><<<nblk, kValuThreads, 0, s>>>(a);
+  } else if (L.T <= kDecodeMaxTokens) {
+    route_split_logits_kernel<<<dim3((L.E + 15) / 16, kRouteSplitK), 64, 0, s>>>(a, W.route_part);
+    if (L.E <= 64) route_choose_kernel<1><<<1, 1024, 0, s>>>(a, W.route_part);
+    else if (L.E <= 128) route_choose_kernel<2><<<1, 1024, 0, s>>>(a, W.route_part);
+    else route_choose_kernel<4><<<1, 1024, 0, s>>>(a, W.route_part);
   } else {
-    const dim3 blk(64 * kMfmaWaves);
-    if (L.E <= 16) route_mfma_kernel<1><<<nblk, blk, 0, s>>>(a);
-    else if (L.E <= 32) route_mfma_kernel<2><<<nblk, blk, 0, s>>>(a);
-    else if (L.E <= 64) route_mfma_kernel<4><<<nblk, blk, 0, s>>>(a);
-    else if (L.E <= 128) route_mfma_kernel<8><<<nblk, blk, 0, s>>>(a);
-    else route_mfma_kernel<16><<<nblk, blk, 0, s>>>(a);
+    // up to 64 experts: 16 wavefronts and a tree sum; more: 8 in wavefront order
+    constexpr bool kTree = MOE_ROUTE_TREE != 0;
+    constexpr int kWide = kTree ? 16 : 8;
+    if (L.E <= 16) route_mfma_kernel<1, kWide, kTree><<<nblk, 64 * kWide, 0, s>>>(a);
+    else if (L.E <= 32) route_mfma_kernel<2, kWide, kTree><<<nblk, 64 * kWide, 0, s>>>(a);
+    else if (L.E <= 64) route_mfma_kernel<4, kWide, kTree><<<nblk, 64 * kWide, 0, s>>>(a);
+    else if (L.E <= 128) route_mfma_kernel<8, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+    else route_mfma_kernel<16, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -51,7 +51,9 @@ def test_workspace_bytes(lib):
     P = 8192 * 4
     assert big >= 2 * P * 2880 * 2          # hidden activations + expert outputs (bf16)
     assert big < 2 * P * 2880 * 2 + (8 << 20)
-    assert n(16, 64, 64, 8, 2, M.MOE_F32, 0) > n(16, 64, 64, 8, 2, M.MOE_BF16, 0)
+    assert n(64, 64, 64, 8, 2, M.MOE_F32, 0) > n(64, 64, 64, 8, 2, M.MOE_BF16, 0)
+    # bf16 with T <= 16 also holds the router's 16 partial-logit slices [16][16][E] fp32
+    assert n(1, 64, 64, 8, 2, M.MOE_BF16, 0) >= 16 * 16 * 8 * 4 + 2 * (64 + 64) * 2
     assert n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 1536) > n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 0)
     bad = ctypes.c_size_t(-1).value
     assert n(8, 64, 64, 300, 2, M.MOE_BF16, 0) == bad
