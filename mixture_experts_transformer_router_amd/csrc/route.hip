@@ -432,14 +432,22 @@ hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
     else if (L.E <= 128) route_choose_kernel<2><<<1, 1024, 0, s>>>(a, W.route_part);
     else route_choose_kernel<4><<<1, 1024, 0, s>>>(a, W.route_part);
   } else {
-    // up to 64 experts: 16 wavefronts and a tree sum; more: 8 in wavefront order
+    // Fewer blocks than CUs (latency-bound): up to 64 experts take 16
+    // wavefronts and a tree sum.  Otherwise 8 wavefronts in wavefront order
+    // (more blocks resident per CU).
     constexpr bool kTree = MOE_ROUTE_TREE != 0;
-    constexpr int kWide = kTree ? 16 : 8;
-    if (L.E <= 16) route_mfma_kernel<1, kWide, kTree><<<nblk, 64 * kWide, 0, s>>>(a);
-    else if (L.E <= 32) route_mfma_kernel<2, kWide, kTree><<<nblk, 64 * kWide, 0, s>>>(a);
-    else if (L.E <= 64) route_mfma_kernel<4, kWide, kTree><<<nblk, 64 * kWide, 0, s>>>(a);
-    else if (L.E <= 128) route_mfma_kernel<8, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
-    else route_mfma_kernel<16, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+    const bool wide = kTree && nblk < 256 && L.E <= 64;
+    if (wide) {
+      if (L.E <= 16) route_mfma_kernel<1, 16, true><<<nblk, 64 * 16, 0, s>>>(a);
+      else if (L.E <= 32) route_mfma_kernel<2, 16, true><<<nblk, 64 * 16, 0, s>>>(a);
+      else route_mfma_kernel<4, 16, true><<<nblk, 64 * 16, 0, s>>>(a);
+    } else {
+      if (L.E <= 16) route_mfma_kernel<1, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+      else if (L.E <= 32) route_mfma_kernel<2, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+      else if (L.E <= 64) route_mfma_kernel<4, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+      else if (L.E <= 128) route_mfma_kernel<8, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+      else route_mfma_kernel<16, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
+    }
   }
   return hipGetLastError();
 }
