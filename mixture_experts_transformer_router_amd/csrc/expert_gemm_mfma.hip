@@ -595,6 +595,11 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   const int act = shared ? 1 : a.act;
   const int c4 = fr & 3;            // position in the lane quad
   constexpr int OJ = GATED ? NJ / 2 : NJ;  // output column tiles per wavefront
+  // this lane's first output row, and whether the whole tile is inside the
+  // expert's rows and the N columns (then the stores need no bounds check)
+  const int lane_row = r0 + wm * 128 + 4 * fk + c4;
+  uint16_t* const lane_out = a.out + (size_t)lane_row * a.ldo + (fr & ~3);
+  const bool tile_inside = r0 + BM <= r_end && n0 + (GATED ? BN / 2 : BN) <= N;
   float bv0[OJ], bv1[OJ];
   int colj[OJ];
 #pragma unroll
@@ -605,13 +610,13 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     bv1[j] = (GATED && bias1 && c < N) ? bf16_to_f32(bias1[(size_t)e * N + c]) : 0.f;
   }
   // the activation is a template argument of the loops (one copy per kind)
-  auto epilogue = [&](auto act_tag) __attribute__((always_inline)) {
+  auto epilogue = [&](auto act_tag, auto inside_tag) __attribute__((always_inline)) {
     constexpr int ACT = decltype(act_tag)::value;
+    constexpr bool INSIDE = decltype(inside_tag)::value;  // no bounds checks
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {      // groups of 4 consecutive rows (q = 4 g .. 4 g + 3)
-        const int row_base = wm * 128 + 32 * i + 8 * g + 4 * fk;
 #pragma unroll
         for (int j = 0; j < OJ; ++j) {
           float v[4];
@@ -636,18 +641,23 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
             const float r0_ = quad_xor2(s0), r1_ = quad_xor2(s1);
             if (hi) { v[0] = r0_; v[1] = r1_; } else { v[2] = r0_; v[3] = r1_; }
           }
-          const int row = r0 + row_base + c4;
+          const int drow = 32 * i + 8 * g;  // row_base + c4 - (lane_row - r0)
           const int col = colj[j] + (fr & ~3);
-          if (row < r_end && col < N) {
-            *reinterpret_cast<uint2*>(a.out + (size_t)row * a.ldo + col) =
+          if (INSIDE || (lane_row + drow < r_end && col < N)) {
+            *reinterpret_cast<uint2*>(lane_out + (size_t)drow * a.ldo + colj[j]) =
                 make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           }
         }
       }
     }
   };
-  if (!GATED || act == 0) epilogue(std::integral_constant<int, 0>{});
-  else epilogue(std::integral_constant<int, 1>{});
+  if (tile_inside) {
+    if (!GATED || act == 0) epilogue(std::integral_constant<int, 0>{}, std::true_type{});
+    else epilogue(std::integral_constant<int, 1>{}, std::true_type{});
+  } else {
+    if (!GATED || act == 0) epilogue(std::integral_constant<int, 0>{}, std::false_type{});
+    else epilogue(std::integral_constant<int, 1>{}, std::false_type{});
+  }
 }
 
 MfmaArgs base_args(const Layer& L, const Work& W) {
