@@ -7,153 +7,16 @@
 //   bf16: a [16 tokens x 16 experts] tile per MFMA; the block's wavefronts
 //         split the input dimension and their partial tiles are added in a
 //         fixed order (deterministic).  For T <= 16 the input dimension is
-//         also split over blocks (route_split_logits_kernel) and a one-block
-//         kernel adds the slices in order and chooses.
+//         also split over blocks (route_split_logits_kernel); the permute
+//         stage adds the slices in order and chooses.
 //   fp32: 64 tokens per block on the vector ALUs, the input dimension
 //         streaming through LDS in chunks of 32.
 //
-// Choice: one wavefront per token; lane l holds the scores of experts l,
-// l+64, ...; k rounds of a wave arg-max by (score desc, index asc) pick the
-// experts best first.
-//   GPT-OSS:  score = logit, w = softmax over the k chosen logits.
-//   grouped:  s = softmax(l) over E (or sigmoid(l)), s' = s + correction bias,
-//             group score = max s' in each of n_group contiguous groups, the
-//             topk_group best groups are kept, top-k by s' among them,
-//             w = s[chosen], renormalised if k > 1 and norm, times rsf
-//             (glm4_moe_lite.go: Config n_group/topk_group, MoEGate.Forward).
-#include "device_common.h"
-#include "moe_internal.h"
+// Choice: see route_common.h.
+#include "route_common.h"
 
 namespace moe {
 namespace {
-
-struct RouteArgs {
-  const void* x;
-  const void* wr;
-  const void* br;
-  const float* e_bias;
-  int T, d, E, k;
-  int grouped, n_group, topk_group, norm, score;
-  float rsf;
-  int32_t* idx;
-  float* w;
-  int32_t* hist;
-  int32_t* user_idx;
-  float* user_w;
-};
-
-// Choose the experts of token t from its logits row `lg` (LDS, E entries;
-// overwritten with selection scores on the grouped path) with one wavefront.
-// VPL = experts per lane (E <= 64 * VPL).  Adds the chosen experts to `cnt`.
-template <int VPL>
-__device__ void choose_experts(const RouteArgs& a, float* lg, int t, int lane, int* cnt) {
-  const int E = a.E;
-  float sc[VPL];    // selection score
-  float base[VPL];  // weight source (logit for GPT-OSS, s for grouped)
-  bool allowed[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane + 64 * v;
-    const float l = e < E ? lg[e] : -INFINITY;
-    sc[v] = l != l ? -INFINITY : l;  // NaN never outranks a number
-    allowed[v] = e < E;
-  }
-
-  if (a.grouped) {
-    if (a.score == MOE_SCORE_SOFTMAX) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) m = fmaxf(m, sc[v]);
-      m = wave_max(m);
-      float s = 0.f;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        base[v] = allowed[v] ? expf(sc[v] - m) : 0.f;
-        s += base[v];
-      }
-      s = wave_sum(s);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) base[v] = base[v] / s;
-    } else {
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) base[v] = allowed[v] ? 1.0f / (1.0f + expf(-sc[v])) : 0.f;
-    }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + 64 * v;
-      const float sel = base[v] + ((a.e_bias != nullptr && e < E) ? a.e_bias[e] : 0.f);
-      sc[v] = (allowed[v] && sel == sel) ? sel : -INFINITY;
-      if (e < E) lg[e] = sc[v];  // read back per group below (same wavefront)
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // group scores: lane g < n_group takes the max over its contiguous group
-    const int gsz = E / a.n_group;
-    float gscore = -INFINITY;
-    int gidx = kNoIndex;
-    if (lane < a.n_group) {
-      for (int i = 0; i < gsz; ++i) gscore = fmaxf(gscore, lg[lane * gsz + i]);
-      gidx = lane;
-    }
-    uint64_t kept = 0;
-    for (int j = 0; j < a.topk_group; ++j) {
-      float bv = gscore;
-      int bi = gidx;
-      wave_argmax(bv, bi);
-      kept |= 1ull << bi;
-      if (lane == bi) { gscore = -INFINITY; gidx = kNoIndex; }
-    }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + 64 * v;
-      if (e < E && !((kept >> (e / gsz)) & 1ull)) allowed[v] = false;
-    }
-  } else {
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) base[v] = sc[v];
-  }
-
-  // k rounds of arg-max over the allowed experts; the host guarantees at
-  // least k allowed experts, so every round finds one (bi < E).
-  int my_e = -1;
-  float my_base = 0.f, first_base = 0.f;
-  for (int j = 0; j < a.k; ++j) {
-    float bv = -INFINITY;
-    int bi = kNoIndex;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + 64 * v;
-      if (allowed[v] && precedes(sc[v], e, bv, bi)) { bv = sc[v]; bi = e; }
-    }
-    wave_argmax(bv, bi);
-    float bb = 0.f;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      if (lane + 64 * v == bi) { allowed[v] = false; bb = base[v]; }
-    }
-    bb = __shfl(bb, bi & 63, 64);
-    if (j == 0) first_base = bb;
-    if (lane == j) { my_e = bi; my_base = bb; }
-  }
-  float wt;
-  if (!a.grouped) {
-    const float ex = lane < a.k ? expf(my_base - first_base) : 0.f;
-    wt = ex / wave_sum(ex);
-  } else {
-    wt = lane < a.k ? my_base : 0.f;
-    if (a.k > 1 && a.norm) wt = wt / wave_sum(wt);
-    wt *= a.rsf;
-  }
-  if (lane < a.k) {
-    const size_t o = (size_t)t * a.k + lane;
-    a.idx[o] = my_e;
-    a.w[o] = wt;
-    if (a.user_idx) a.user_idx[o] = my_e;
-    if (a.user_w) a.user_w[o] = wt;
-    atomicAdd(&cnt[my_e], 1);
-  }
-}
 
 // ---- bf16: MFMA logits -----------------------------------------------------
 constexpr int kMfmaTokens = 16;
@@ -282,7 +145,8 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
 // pipeline; here block (g, ks) computes the [16 tokens x 16 experts] tile of
 // expert group g over the ks-th of kRouteSplitK contiguous slices of the input
 // dimension (one wavefront, all loads of a slice issued before its MFMAs) and
-// stores it to part[ks].  route_choose_kernel adds the slices in ks order.
+// stores it to part[ks].  select_permute_small_kernel (permute.hip) adds the
+// slices in ks order and chooses.
 constexpr int kSplitSteps = 8;  // 32-element steps loaded ahead by one wavefront
 
 __global__ __launch_bounds__(64) void route_split_logits_kernel(RouteArgs a, float* part) {
@@ -317,32 +181,6 @@ __global__ __launch_bounds__(64) void route_split_logits_kernel(RouteArgs a, flo
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[((size_t)ks * 16 + 4 * kg + r) * E + e] = acc[r];
   }
-}
-
-// One block: logits = sum of the kRouteSplitK slices in order + bias, then one
-// wavefront per token chooses its experts; writes the block's expert counts.
-template <int VPL>
-__global__ __launch_bounds__(1024) void route_choose_kernel(RouteArgs a, const float* part) {
-  __shared__ float lg[16][64 * VPL + 1];
-  __shared__ int cnt[64 * VPL];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int E = a.E;
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
-  for (int i = tid; i < a.T * E; i += 1024) {
-    const int t = i / E, e = i % E;
-    float pv[kRouteSplitK];  // all slices loaded first, then added in order
-#pragma unroll
-    for (int ks = 0; ks < kRouteSplitK; ++ks) pv[ks] = part[((size_t)ks * 16 + t) * E + e];
-    float v = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < kRouteSplitK; ++ks) v += pv[ks];
-    if (a.br) v += bf16_to_f32(static_cast<const uint16_t*>(a.br)[e]);
-    lg[t][e] = v;
-  }
-  __syncthreads();
-  if (wv < a.T) choose_experts<VPL>(a, lg[wv], wv, lane, cnt);
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024) a.hist[e] = cnt[e];
 }
 
 // ---- fp32: vector-ALU logits -------------------------------------------------
@@ -411,13 +249,12 @@ __global__ __launch_bounds__(kValuThreads) void route_valu_kernel(RouteArgs a) {
 int route_block_tokens(const Layer& L) { return L.dt == MOE_F32 ? kValuTokens : kMfmaTokens; }
 
 hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
-  RouteArgs a;
-  a.x = L.x; a.wr = L.router_w; a.br = L.router_b; a.e_bias = L.e_bias;
-  a.T = L.T; a.d = L.d; a.E = L.E; a.k = L.k;
-  a.grouped = L.grouped; a.n_group = L.n_group; a.topk_group = L.topk_group;
-  a.norm = L.norm; a.score = L.score; a.rsf = L.rsf;
-  a.idx = W.idx; a.w = W.w; a.hist = W.hist;
-  a.user_idx = L.routing.topk_idx; a.user_w = L.routing.topk_w;
+  const RouteArgs a = route_args(L, W);
+  if (few_token_route(L)) {
+    // the choice runs in the permute stage (select_permute_small_kernel)
+    route_split_logits_kernel<<<dim3((L.E + 15) / 16, kRouteSplitK), 64, 0, s>>>(a, W.route_part);
+    return hipGetLastError();
+  }
   const int tb = route_block_tokens(L);
   const int nblk = (L.T + tb - 1) / tb;
   if (L.dt == MOE_F32) {
@@ -426,11 +263,6 @@ hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
     else if (L.E <= 32) route_valu_kernel<8><<<nblk, kValuThreads, 0, s>>>(a);
     else if (L.E <= 64) route_valu_kernel<16><<<nblk, kValuThreads, 0, s>>>(a);
     else route_valu_kernel<64><<<nblk, kValuThreads, 0, s>>>(a);
-  } else if (L.T <= kDecodeMaxTokens) {
-    route_split_logits_kernel<<<dim3((L.E + 15) / 16, kRouteSplitK), 64, 0, s>>>(a, W.route_part);
-    if (L.E <= 64) route_choose_kernel<1><<<1, 1024, 0, s>>>(a, W.route_part);
-    else if (L.E <= 128) route_choose_kernel<2><<<1, 1024, 0, s>>>(a, W.route_part);
-    else route_choose_kernel<4><<<1, 1024, 0, s>>>(a, W.route_part);
   } else {
     // Fewer blocks than CUs (latency-bound): up to 64 experts take 16
     // wavefronts and a tree sum.  Otherwise 8 wavefronts in wavefront order
