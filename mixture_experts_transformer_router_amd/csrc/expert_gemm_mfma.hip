@@ -201,7 +201,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
   constexpr int SEG_ROWS = 1024 / (2 * BK);  // rows per 1 KB copy segment
   constexpr int RA = BM * CPR / kThreads; // copy instructions per wavefront and tile, A
-  constexpr int RB = WF == WF_MXFP4 ? 0 : BN * CPR / kThreads;  // same, B (MXFP4: register loads)
+  constexpr int RB = WF == WF_MXFP4 ? 0 : BN * CPR / kThreads;  // same, B (MXFP4: none)
+  // MXFP4: code copies per wavefront and 4-tile group (8 rows x 128 B each)
+  constexpr int RC = WF == WF_MXFP4 ? BN * 8 / kThreads : 0;
   static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
   static_assert(NS >= 2 && NSB >= NS && NSB <= NS + 1, "LDS stages");
   static_assert(WF != WF_MXFP4 || NSB == NS, "MXFP4 weights use symmetric stages");
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       lds_b3[NSB > 3 ? BN * BK : 8], lds_b4[NSB > 4 ? BN * BK : 8];
   // MXFP4 (every wait drains the copies anyway): one array per operand
   __shared__ uint16_t lds_mx_a[NS][BM * BK], lds_mx_b[NS][BN * BK];
+  __shared__ uint16_t lds_mx_code[WF == WF_MXFP4 ? BN * 64 : 8];  // codes of 4 tiles, 128 B per row
   auto stage_a = [&](int st) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (WF == WF_MXFP4) return lds_mx_a[st];
     if constexpr (NS > 4) {
@@ -287,10 +290,11 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     const int gr = r0 + r < r_end ? r0 + r : r0;
     a_row[i] = a.row_token ? a.row_token[gr] : gr;
   }
-  constexpr int RBX = RB > 0 ? RB : 1;
+  constexpr int NBR = RB > RC ? RB : RC;  // B row rounds (bf16 copies or MXFP4 code copies)
+  constexpr int RBX = NBR > 0 ? NBR : 1;
   int b_row[RBX];
 #pragma unroll
-  for (int i = 0; i < RB; ++i) {
+  for (int i = 0; i < NBR; ++i) {
     const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
     int wrow, up = 0;
     if constexpr (GATED) {
@@ -306,8 +310,12 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   const uint16_t* w_gate = shared ? a.sh_w0 : a.w0 + (size_t)e * a.N * K;
   const uint16_t* w_up = GATED ? (shared ? a.sh_w1 : a.w1 + (size_t)e * a.N * K) : nullptr;
 
-  // MXFP4: thread t < BN decodes B row t through registers
-  const uint8_t* mx_codes = nullptr;
+  // MXFP4: the codes of 4 K tiles (128 bytes of each B row) are copied into
+  // lds_mx_code (8 rows x 128 B per instruction, like the bf16 weights; the
+  // 16-byte chunks of row r are XOR-swizzled by r & 7); thread t < BN then
+  // decodes row t of each tile from there with the tile's two scale bytes,
+  // which it loads a tile ahead.
+  bool mx_row_ok = false;
   const uint8_t* mx_scales = nullptr;
   if constexpr (WF == WF_MXFP4) {
     const int r = tid < BN ? tid : BN - 1;
@@ -320,17 +328,12 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
     } else {
       wrow = n0 + r;
     }
-    if (wrow < N) {
-      const size_t row = (size_t)e * a.N + wrow;
-      mx_codes = (up ? a.c1 : a.c0) + row * (K / 2);
-      mx_scales = (up ? a.s1 : a.s0) + row * (K / 32);
-    }
+    mx_row_ok = tid < BN && wrow < N;
+    const size_t row = (size_t)e * a.N + (wrow < N ? wrow : n0);
+    mx_scales = (up ? a.s1 : a.s0) + row * (K / 32);
   }
-  // codes of BK elements (BK / 2 bytes) and their scale bytes (one per 32
-  // elements), kept in named registers (an array here ends up in scratch)
   static_assert(WF != WF_MXFP4 || BK == 64, "MXFP4 stages hold 64 elements");
-  u32x4_t mxr0 = {0u, 0u, 0u, 0u}, mxr1 = {0u, 0u, 0u, 0u};
-  uint32_t mxs0 = 127u, mxs1 = 127u;
+  uint32_t mxsc = 0x7f7fu;  // scale bytes of the next tile to decode (low: first 32 elements)
 
   // Every copy of a tile issues exactly RA (A) and RB (B) instructions per
   // wavefront (the K tail copies clamped, valid addresses and is zeroed after
@@ -358,33 +361,62 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
     for (int i = 0; i < RA; ++i) copy_a(kt, As, i);
   };
+  // MXFP4: copy the codes of 4-tile group g into lds_mx_code.  Chunks past
+  // the row end copy the row's first chunk instead (decoded as zeros).
+  auto mx_copy_codes = [&](int g, uint16_t* Cs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      const int logical = ld_phys ^ (ld_sub & 7);  // the row's r & 7 is ld_sub
+      int off = 128 * g + 16 * logical;
+      if (off + 16 > K / 2) off = 0;
+      const uint8_t* src = ((b_row[i] & 1) ? a.c1 : a.c0) + ((size_t)e * a.N + (b_row[i] >> 1)) * (K / 2) + off;
+      __builtin_amdgcn_global_load_lds(src, Cs + (4 * i + wv) * 512, 16, 0, 0);
+    }
+  };
   auto issue_b = [&](int kt, int sb) __attribute__((always_inline)) {
     if constexpr (WF == WF_MXFP4) {
+      // the tile's two scale bytes: one 2-byte load when K % 64 == 0 (rows of
+      // K / 32 bytes keep it aligned), else byte loads of the halves inside K
       const int k0 = kt * BK;
-      const bool ok0 = mx_codes && k0 < K, ok1 = mx_codes && k0 + 32 < K;
-      mxr0 = ok0 ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2) : u32x4_t{0u, 0u, 0u, 0u};
-      mxs0 = ok0 ? (uint32_t)mx_scales[k0 / 32] : 127u;
-      mxr1 = ok1 ? *reinterpret_cast<const u32x4_t*>(mx_codes + k0 / 2 + 16) : u32x4_t{0u, 0u, 0u, 0u};
-      mxs1 = ok1 ? (uint32_t)mx_scales[k0 / 32 + 1] : 127u;
+      if ((K & 63) == 0 && k0 + 64 <= K) {
+        mxsc = *reinterpret_cast<const uint16_t*>(mx_scales + k0 / 32);
+      } else {
+        const uint32_t b0 = k0 < K ? (uint32_t)mx_scales[k0 / 32] : 127u;
+        const uint32_t b1 = k0 + 32 < K ? (uint32_t)mx_scales[k0 / 32 + 1] : 127u;
+        mxsc = b0 | (b1 << 8);
+      }
+      if (kt % 4 == 0) mx_copy_codes(kt / 4, lds_mx_code);
     } else {
       uint16_t* Bs = stage_b(sb);
 #pragma unroll
       for (int i = 0; i < RB; ++i) copy_b(kt, Bs, i);
     }
   };
-  // MXFP4 only: decode the codes in registers (row tid) into stage sb
-  auto finish_b = [&](int sb) __attribute__((always_inline)) {
+  // MXFP4 only: decode tile t (row tid) from lds_mx_code into stage sb.  The
+  // first tile of a group waits for the group's copies and meets the other
+  // wavefronts first (the copies land in LDS asynchronously).
+  auto finish_b = [&](int t, int sb) __attribute__((always_inline)) {
     if constexpr (WF == WF_MXFP4) {
+      if (t % 4 == 0) {
+        wait_vmcnt<0>();
+        barrier_lds();
+      }
       uint16_t* Bs = stage_b(sb);
       if (tid < BN) {
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 0)) = decode_e2m1x8(mxr0.x, mxs0);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 1)) = decode_e2m1x8(mxr0.y, mxs0);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 2)) = decode_e2m1x8(mxr0.z, mxs0);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 3)) = decode_e2m1x8(mxr0.w, mxs0);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 4)) = decode_e2m1x8(mxr1.x, mxs1);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 5)) = decode_e2m1x8(mxr1.y, mxs1);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 6)) = decode_e2m1x8(mxr1.z, mxs1);
-        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 7)) = decode_e2m1x8(mxr1.w, mxs1);
+        const int q = t & 3, sw = tid & 7;
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(lds_mx_code + tid * 64 + ((2 * q) ^ sw) * 8);
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(lds_mx_code + tid * 64 + ((2 * q + 1) ^ sw) * 8);
+        const bool ok0 = mx_row_ok && t * BK < K, ok1 = mx_row_ok && t * BK + 32 < K;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        const uint32_t s0 = mxsc & 0xffu, s1 = (mxsc >> 8) & 0xffu;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 0)) = ok0 ? decode_e2m1x8(c0.x, s0) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 1)) = ok0 ? decode_e2m1x8(c0.y, s0) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 2)) = ok0 ? decode_e2m1x8(c0.z, s0) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 3)) = ok0 ? decode_e2m1x8(c0.w, s0) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 4)) = ok1 ? decode_e2m1x8(c1.x, s1) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 5)) = ok1 ? decode_e2m1x8(c1.y, s1) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 6)) = ok1 ? decode_e2m1x8(c1.z, s1) : z;
+        *reinterpret_cast<u32x4_t*>(Bs + swz<BK>(tid, 7)) = ok1 ? decode_e2m1x8(c1.w, s1) : z;
       }
     }
   };
@@ -465,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       issue_b(s + NSB, s + NSB);
       // MXFP4: tile 0 is decoded now; every later tile t at the end of tile
       // t-1, a whole tile after its codes were requested
-      if (s + NSB == 0) finish_b(0);
+      if (s + NSB == 0) finish_b(0, 0);
     }
   }
   if (WF != WF_MXFP4 && ktiles >= NSB) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kPrologueWait)>();
@@ -515,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
       } else if (STEADY || kt + 1 < ktiles) {
         // MXFP4: decode tile kt+1 into its stage (free since the barrier that
         // ended tile kt-1) from the codes requested at that barrier
-        if constexpr (WF == WF_MXFP4) finish_b(sb1);
+        if constexpr (WF == WF_MXFP4) finish_b(kt + 1, sb1);
         if (STEADY && WF != WF_MXFP4) wait_vmcnt<(WF == WF_MXFP4 ? 0 : kSteadyWait)>();
         else wait_vmcnt<0>();
         barrier_lds();  // tile kt+1 is in LDS; every wavefront is done reading tile kt
