@@ -130,7 +130,9 @@ moe_status moe_ffn_forward(const void* x, const void* router_w, const void* rout
  *            32 consecutive elements along cols (the input dimension).
  * (rows, cols) = (d_ff, d) for gate and up, (d, d_ff) for down.  x, router
  * weight and bias, expert biases and out are bf16.  d and d_ff must be
- * multiples of 32.  A scale byte of 255 (NaN) yields NaN outputs. */
+ * multiples of 32, d * d_ff < 2^33 and T * k * max(d, d_ff) < 2^32
+ * (MOE_ERR_UNSUPPORTED otherwise).  A scale byte of 255 (NaN) yields NaN
+ * outputs. */
 moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void* router_b,
                                  const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
                                  const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,

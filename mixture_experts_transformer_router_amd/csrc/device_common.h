@@ -36,12 +36,19 @@ template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, siz
 // Logistic function with the hardware exp2 and reciprocal (about 2 ulp).
 __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// v clipped to [lo, hi]; NaN stays NaN (the hardware min / max / median
+// return the other operand for a NaN input).
+__device__ __forceinline__ float clip_nan(float v, float lo, float hi) {
+  return __builtin_isnan(v) ? v : __builtin_amdgcn_fmed3f(v, lo, hi);
+}
+
 // Expert activation.  act 0: clipped SwiGLU (gate clipped to [0, limit], up to
 // [-limit, limit], h = g' * sigmoid(alpha g') * u').  act 1: h = g sigmoid(g) u.
+// A NaN gate or up value gives a NaN h.
 __device__ __forceinline__ float expert_act(int act, float g, float u, float alpha, float limit) {
   if (act == 0) {
-    float gc = fminf(fmaxf(g, 0.f), limit);
-    float uc = fminf(fmaxf(u, -limit), limit);
+    const float gc = clip_nan(g, 0.f, limit);
+    const float uc = clip_nan(u, -limit, limit);
     return gc * sigmoidf_(alpha * gc) * uc;
   }
   return g * sigmoidf_(g) * u;

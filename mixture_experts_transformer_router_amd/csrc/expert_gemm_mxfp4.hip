@@ -1,0 +1,496 @@
+// Grouped expert GEMMs with MXFP4 weights on bf16 MFMA.
+//
+//   gate|up:  h[r][f] = act(x[t] . Wg[e][f] + bg[e][f], x[t] . Wu[e][f] + bu[e][f])
+//   down:     y[r][n] = h[r] . Wd[e][n] + bd[e][n]
+//   with W[e][n][k] = e2m1(code[e][n][k]) * 2^(scale[e][n][k / 32] - 127)
+//
+// (MaxText GPT-OSS weight mapping "MOE EXPERTS"; the weight format of the
+// MXFP4 GPT-OSS checkpoints; OCP Microscaling Formats v1.0 for e2m1 / e8m0.)
+//
+// Same tile geometry, tile order and epilogue as the dense bf16 kernel, but
+// the weights stay 4-bit until they reach registers: the codes are copied
+// into LDS (a quarter of the bf16 bytes), each wavefront reads its own code
+// fragments from there and gfx950's v_cvt_scalef32_pk_bf16_fp4 turns them,
+// with the block scale, into the bf16 B operands of the MFMAs, in the shadow
+// of the previous step's MFMAs.  Every product e2m1 * 2^s is a bf16 number,
+// so the decoded operands are exact.
+//
+// K permutation.  v_mfma_f32_32x32x16_bf16 takes 8 k values from each lane
+// half h = lane / 32.  Within a 64-wide K tile, half h of step s (0..3) holds
+// k = 32 h + 8 s .. +7 for both operands (the MFMA sums over k in any order as
+// long as A and B agree): a lane's B codes for the whole tile are then one
+// 16-byte piece of its weight row (32 codes, one e8m0 scale), and its A
+// fragment of step s is 16-byte chunk 4 h + s of its LDS row.
+//
+// Codes of 4 K tiles (128 bytes of each weight row) are copied as one group,
+// 8 rows x 128 B per 1 KB instruction, into one of two group buffers; the
+// copies of group g + 1 are issued when tile 4 g starts, into the buffer that
+// group g - 1 used.  FAST kernels (K % 64 == 0, scale tensors 4-byte aligned
+// in base and size) copy the 8 scale bytes of each row and group the same way
+// (as the 3 aligned dwords that hold them) and run every K tile but the last
+// with the same branch-free step; the general kernel loads each lane's scale
+// bytes into registers a tile ahead and handles a K tail.
+#include <type_traits>
+
+#include "gemm_common.h"
+
+#ifndef MOE_MX_GROUP_M
+#define MOE_MX_GROUP_M 4
+#endif
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+constexpr int kGroupM = MOE_MX_GROUP_M;  // row tiles walked together within an XCD
+constexpr int BK = 64;                   // K elements per A stage and per decode tile
+constexpr int kTilesPerGroup = 4;        // K tiles per code group (128 code bytes of a row)
+constexpr int kCodeRowBytes = 128;
+// kinds of K-tile step (see tile_step)
+constexpr int kSteady = 0, kGeneral = 1, kLast = 2;
+template <int V> using int_c = std::integral_constant<int, V>;
+
+// Stored position of 16-byte chunk c of code row r in LDS: XOR-swizzled by
+// bits 1..3 of the row, so that the 16-byte reads of any 16 consecutive rows
+// (same logical chunk; rows alternate between the two 128-byte halves of a
+// 256-byte bank window) fall in 16 distinct 16-byte slots.
+__device__ __forceinline__ int code_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// e8m0 block scale as the fp32 factor of the conversion (s = 0: 2^-127, a
+// denormal; s = 255, NaN, is handled by the caller).
+__device__ __forceinline__ float scale_factor(uint32_t s) { return __uint_as_float(s == 0 ? 0x00400000u : (s << 23)); }
+
+// Byte p of a word of e2m1 codes (low nibble first) times the scale -> two
+// bf16 (low nibble in the low half).  p must fold to a constant.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t codes, float scale, int p) {
+  bf16x2_t r;
+  if (p == 0) r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  else if (p == 1) r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  else if (p == 2) r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  else r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <bool GATED, int NJ, bool FAST>
+__global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
+  constexpr int BN = 64 * NJ;
+  constexpr int CPR = BK / 8;               // 16-byte chunks per A row
+  constexpr int SEG_ROWS = 1024 / (2 * BK); // A rows per 1 KB copy segment
+  constexpr int RA = BM * CPR / kThreads;   // A copy instructions per wavefront and tile
+  constexpr int RC = BN * kCodeRowBytes / 1024 / 4;  // code copy instructions per wavefront and group
+  static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
+  static_assert(BN * kCodeRowBytes % 4096 == 0, "code copy rounds");
+  constexpr int KK = BK / 16;  // MFMA steps per tile
+  static_assert(KK == 4, "a lane's 16-byte code piece covers the 4 steps of a tile");
+  constexpr int NM = 4 * NJ;   // MFMAs per step
+  constexpr int kScaleDw = 3;  // FAST: aligned dwords holding a row's 8 scale bytes of a group
+  constexpr int RS = (BN * kScaleDw + kThreads - 1) / kThreads;  // scale copy rounds per wavefront and group
+
+  // A stages are separate variables (the compiler tells copies into one from
+  // reads of the other only by the variable they address); the steady loop
+  // is unrolled by 2 so that their indices are compile-time constants.
+  __shared__ uint16_t lds_a0[BM * BK], lds_a1[BM * BK];
+  __shared__ uint16_t lds_code[2][BN * kCodeRowBytes / 2];
+  __shared__ uint32_t lds_scale[2][FAST ? RS * kThreads : 1];  // row r: bytes 12 r .. 12 r + 11
+  auto stage_a = [&](int st) __attribute__((always_inline)) -> uint16_t* { return st == 0 ? lds_a0 : lds_a1; };
+
+  int m_tile, n_tile;
+  if (!block_tile<kGroupM>(a, m_tile, n_tile)) return;
+  const int4 desc = reinterpret_cast<const int4*>(a.tile_desc)[m_tile];
+  const int e = desc.x;
+  const int N = a.N;
+  const int K = a.K;
+  const int n0 = n_tile * (GATED ? BN / 2 : BN);
+  if (n0 >= N) return;
+  const int r0 = desc.y;
+  const int r_end = desc.z;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int fr = lane & 31, fk = lane >> 5;
+
+  // B row r of the block is weight row n0 + 32 (r / 64) + r % 32 of the gate
+  // (r % 64 < 32) or up tensor in the gate|up stage, n0 + r otherwise.  Rows
+  // past N use row n0 (their outputs are dropped).
+  auto clamp_row = [&](int wrow) __attribute__((always_inline)) { return wrow < N ? wrow : n0; };
+
+  // ---- copy coordinates (as the dense kernel: in round i wavefront wv fills
+  // the 1 KB LDS segment 4 i + wv, lane l its 16-byte slot l).
+  const int ld_sub = lane / CPR;
+  const int ld_phys = lane % CPR;
+  // element offset of each copied A row (the A operand is under 2^31
+  // elements; the library checks)
+  uint32_t a_row[RA];
+#pragma unroll
+  for (int i = 0; i < RA; ++i) {
+    const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int gr = r0 + r < r_end ? r0 + r : r0;
+    a_row[i] = (uint32_t)(a.row_token ? a.row_token[gr] : gr) * (uint32_t)a.lda;
+  }
+  // The expert's code and scale tensors (gate, up); byte offsets within one
+  // expert fit 32 bits (the library rejects larger experts).
+  const uint8_t* const code_gate = a.c0 + (size_t)e * N * (K / 2);
+  const uint8_t* const code_up = GATED ? a.c1 + (size_t)e * N * (K / 2) : code_gate;
+  const uint8_t* const scale_gate = a.s0 + (size_t)e * N * (K / 32);
+  const uint8_t* const scale_up = GATED ? a.s1 + (size_t)e * N * (K / 32) : scale_gate;
+  // Code copy round i: lane l copies stored chunk l % 8 of B row
+  // 32 i + code_r (code_r = 8 wv + l / 8 < 32), i.e. weight row
+  // n0 + 32 (i / 2) + code_r of the gate (i even) or up (i odd) tensor in the
+  // gate|up stage, n0 + 32 i + code_r otherwise.  Bits 1..3 of the B row do
+  // not depend on i, nor does the logical chunk the slot holds.
+  const int code_r = 8 * wv + (lane >> 3);
+  const uint32_t code_lane = 16u * (uint32_t)code_chunk(code_r, lane & 7);
+  // this lane's fragment rows: B row wn 32 NJ + 32 j + fr of the block, i.e.
+  // weight row n0 + 64 wn + 32 (j / 2) + fr of the gate (j even) or up tensor
+  // in the gate|up stage, n0 + 32 NJ wn + 32 j + fr otherwise
+  auto frag_row = [&](int j) __attribute__((always_inline)) {
+    return GATED ? n0 + 64 * wn + 32 * (j / 2) + fr : n0 + 32 * NJ * wn + 32 * j + fr;
+  };
+  const int code_off0 = (wn * 32 * NJ + fr) * (kCodeRowBytes / 2);  // uint16 offset of fragment row j = 0
+  const int code_x = (wn * 32 * NJ + fr) >> 1 & 7;  // row hash of the fragment rows (32 j keeps it)
+
+  const int ktiles = (K + BK - 1) / BK;
+  const int tail_tile = (K % BK) != 0 ? ktiles - 1 : -1;
+  const int code_bytes = K / 2;
+
+  auto copy_a = [&](int kt, uint16_t* As, int i) __attribute__((always_inline)) {
+    const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int chunk = (swz<BK>(row, ld_phys) - row * BK) >> 3;  // logical chunk of this slot
+    const int k = min(kt * BK + 8 * chunk, K - 8);
+    __builtin_amdgcn_global_load_lds(a.a + (a_row[i] + (uint32_t)k), As + (4 * i + wv) * 512, 16, 0, 0);
+  };
+  auto issue_a = [&](int kt, int sa) __attribute__((always_inline)) {
+    uint16_t* As = stage_a(sa);
+#pragma unroll
+    for (int i = 0; i < RA; ++i) copy_a(kt, As, i);
+  };
+  // codes of group g into buffer g % 2 (pieces past the row end copy the
+  // row's first piece; the tiles that would use them mask them)
+  auto issue_codes = [&](int g) __attribute__((always_inline)) {
+    uint16_t* Cs = lds_code[g & 1];
+    const uint32_t base = kCodeRowBytes * g;
+    const uint32_t piece = base + code_lane + 16 <= (uint32_t)code_bytes ? base + code_lane : 0u;
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      const int wrow = clamp_row(GATED ? n0 + 32 * (i / 2) + code_r : n0 + 32 * i + code_r);
+      const uint8_t* src = (GATED && (i & 1)) ? code_up : code_gate;
+      __builtin_amdgcn_global_load_lds(src + ((uint32_t)wrow * (uint32_t)(K / 2) + piece), Cs + (4 * i + wv) * 512, 16, 0, 0);
+    }
+  };
+  // FAST: the 8 scale bytes of group g of every B row, as the 3 aligned
+  // dwords that hold them, into scale buffer g % 2 (dword q of the buffer is
+  // dword q % 3 of row q / 3; rows past BN repeat row BN - 1 into padding).
+  // Dwords past the end of the tensor are clamped to its last one (their
+  // bytes belong to no block of K).
+  auto issue_scales = [&](int g) __attribute__((always_inline)) {
+    uint32_t* Ss = lds_scale[g & 1];
+    const uintptr_t end_gate = reinterpret_cast<uintptr_t>(a.s0) + (size_t)a.E * N * (K / 32) - 4;
+    const uintptr_t end_up = GATED ? reinterpret_cast<uintptr_t>(a.s1) + (size_t)a.E * N * (K / 32) - 4 : end_gate;
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int q = 64 * (4 * i + wv) + lane;
+      const int r = min(q / kScaleDw, BN - 1);
+      const bool up = GATED && (r & 63) >= 32;
+      const int wrow = clamp_row(GATED ? n0 + 32 * (r >> 6) + (r & 31) : n0 + r);
+      const uintptr_t row = reinterpret_cast<uintptr_t>(up ? scale_up : scale_gate) + (size_t)wrow * (K / 32) + 8 * g;
+      const uintptr_t dw = min((row & ~(uintptr_t)3) + 4 * (q % kScaleDw), up ? end_up : end_gate);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dw), Ss + 64 * (4 * i + wv), 4, 0, 0);
+    }
+  };
+  // scale bytes of tile kt for this lane's half: FAST from the scale buffer,
+  // else from the tensors into registers a tile ahead (a half past K loads
+  // the row's last scale; take_scales replaces it)
+  uint32_t sraw[NJ];
+  auto load_scales = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (FAST) {
+      const uint8_t* Sb = reinterpret_cast<const uint8_t*>(lds_scale[(kt / kTilesPerGroup) & 1]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int wrow = clamp_row(frag_row(j));
+        const uintptr_t row = reinterpret_cast<uintptr_t>((GATED && (j & 1)) ? scale_up : scale_gate) + (size_t)wrow * (K / 32);
+        const int r = wn * 32 * NJ + 32 * j + fr;
+        sraw[j] = Sb[kScaleDw * 4 * r + (int)(row & 3) + 2 * (kt % kTilesPerGroup) + fk];
+      }
+    } else {
+      const int cb = min(2 * kt + fk, K / 32 - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        sraw[j] = ((GATED && (j & 1)) ? scale_up : scale_gate)[(uint32_t)clamp_row(frag_row(j)) * (uint32_t)(K / 32) + cb];
+    }
+  };
+  float scf[NJ];      // scale factors of the current tile
+  uint32_t nan_j = 0; // bit j: scale byte 255 (NaN block) in the current tile
+  // scales of tile kt from sraw (a half past K: 127; its codes are zero)
+  auto take_scales = [&](int kt) __attribute__((always_inline)) {
+    const bool past = !FAST && 2 * kt + fk >= K / 32;
+    nan_j = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t sb = past ? 127u : sraw[j];
+      scf[j] = scale_factor(sb);
+      nan_j |= (sb == 255u ? 1u : 0u) << j;
+    }
+  };
+  // this lane's code pieces of tile kt (zero for a half past K)
+  u32x4_t cw[NJ];
+  auto read_codes = [&](int kt, bool check_k) __attribute__((always_inline)) {
+    const uint16_t* Cs = lds_code[(kt / kTilesPerGroup) & 1];
+    const int c = code_chunk(0, 2 * (kt % kTilesPerGroup) + fk) ^ code_x;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cw[j] = *reinterpret_cast<const u32x4_t*>(Cs + code_off0 + 32 * j * (kCodeRowBytes / 2) + 8 * c);
+    if (check_k && kt * BK + 32 * fk >= K) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) cw[j] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  // zero the A chunks of the tile past K (the last tile only)
+  auto zero_tail_a = [&](int kt, int sa) __attribute__((always_inline)) {
+    uint16_t* As = stage_a(sa);
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
+      const int chunk = (swz<BK>(row, ld_phys) - row * BK) >> 3;
+      if (kt * BK + 8 * chunk >= K)
+        *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+
+  f32x16_t acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  bf16x8_t fa[2][4];
+  u32x4_t fbw[2][NJ];
+  // A fragment of M block i, step s, from stage As
+  auto load_fa = [&](const uint16_t* As, int s, int buf, int i) __attribute__((always_inline)) {
+    fa[buf][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(As + swz<BK>(wm * 128 + 32 * i + fr, 4 * fk + s)));
+  };
+  // part p (2 codes -> 2 bf16) of B fragment j of step s; step 0 also marks
+  // NaN blocks (one NaN element makes every output of the column NaN, as
+  // the NaN weights would)
+  auto cvt_part = [&](int s, int buf, int j, int p) __attribute__((always_inline)) {
+    const uint32_t w = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
+    uint32_t v = cvt_fp4_pair(w, scf[j], p);
+    if (s == 0 && p == 0) v = (nan_j >> j) & 1 ? 0x7fc07fc0u : v;
+    if (p == 0) fbw[buf][j].x = v;
+    else if (p == 1) fbw[buf][j].y = v;
+    else if (p == 2) fbw[buf][j].z = v;
+    else fbw[buf][j].w = v;
+  };
+  auto mfma_m = [&](int cur, int m) __attribute__((always_inline)) {
+    const int i = m / NJ, j = m % NJ;
+    acc[i][j] = mfma_32x32x16(fa[cur][i], __builtin_bit_cast(bf16x8_t, fbw[cur][j]), acc[i][j]);
+  };
+
+  // ---- prologue: A of tiles 0 and 1, code (and FAST: scale) groups 0 and 1,
+  // (else: scales of tiles 0 and 1)
+  issue_a(0, 0);
+  if (ktiles > 1) issue_a(1, 1);
+  issue_codes(0);
+  if (kCodeRowBytes < code_bytes) issue_codes(1);
+  if constexpr (FAST) {
+    issue_scales(0);
+    if (kCodeRowBytes < code_bytes) issue_scales(1);
+    wait_vmcnt<0>();
+    barrier_lds();
+    load_scales(0);
+    wait_lgkmcnt0();
+    take_scales(0);
+  } else {
+    load_scales(0);
+    wait_vmcnt<0>();
+    take_scales(0);
+    if (ktiles > 1) load_scales(1);
+  }
+  barrier_lds();
+  if (tail_tile == 0) {
+    zero_tail_a(0, 0);
+    barrier_lds();
+  }
+  read_codes(0, true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_fa(lds_a0, 0, 0, i);
+  wait_lgkmcnt0();
+#pragma unroll
+  for (int m = 0; m < NM; ++m) cvt_part(0, 0, m / 4, m % 4);
+
+  // One K tile.  Steps 0..2: the MFMAs of step s alternate with the A
+  // fragment reads and B fragment conversions of step s + 1.  Step 3 starts
+  // with the tile boundary (all copies landed, barrier: tile kt+1 is in LDS
+  // and every wavefront is done reading tile kt), reads tile kt+1's codes and
+  // scales, then alternates its MFMAs with the copies of A(kt+2) into the
+  // stage tile kt used and with tile kt+1's first fragments.
+  // MODE kSteady: tile kt+1 exists and is no tail tile (copies past the last
+  // tile are clamped to it, into a stage nobody reads again); kLast: tile kt
+  // is the last one; kGeneral: run-time checks.
+  auto tile_step = [&](int kt, auto mode_tag, auto phase_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool STEADY = MODE == kSteady;
+    constexpr int PH = decltype(phase_tag)::value;  // kt % 2 if >= 0
+    const int sa = PH >= 0 ? PH : kt & 1;
+    const int sa1 = PH >= 0 ? PH ^ 1 : (kt + 1) & 1;
+#pragma unroll
+    for (int s = 0; s < KK; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      wait_lgkmcnt0();
+      if (s + 1 < KK) {
+        const uint16_t* As = stage_a(sa);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mfma_m(cur, m);
+          if (m < 4) load_fa(As, s + 1, nxt, m);
+          cvt_part(s + 1, nxt, m / 4, m % 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
+      if (MODE == kLast || (MODE == kGeneral && kt + 1 >= ktiles)) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) mfma_m(cur, m);
+        continue;
+      }
+      wait_vmcnt<0>();
+      barrier_lds();
+      if (!STEADY && kt + 1 == tail_tile) {
+        zero_tail_a(kt + 1, sa1);
+        barrier_lds();
+      }
+      read_codes(kt + 1, !STEADY);
+      if constexpr (FAST) {
+        load_scales(kt + 1);  // LDS reads; converted once they have landed
+      } else {
+        take_scales(kt + 1);
+        if (STEADY || kt + 2 < ktiles) load_scales(kt + 2);
+      }
+      const int g1 = (kt + 1) / kTilesPerGroup + 1;
+      if ((kt + 1) % kTilesPerGroup == 0 && kCodeRowBytes * g1 < code_bytes) {
+        issue_codes(g1);
+        if constexpr (FAST) issue_scales(g1);
+      }
+      const bool more_a = STEADY || kt + 2 < ktiles;
+      const int kt2 = min(kt + 2, ktiles - 1);
+      uint16_t* As = stage_a(sa);
+      const uint16_t* As1 = stage_a(sa1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (STEADY) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mfma_m(cur, m);
+          if (m < RA) copy_a(kt2, As, m);
+          if (m < 4) load_fa(As1, 0, nxt, m);
+          if (m == NM / 2 - 1) {
+            wait_lgkmcnt0();
+            if constexpr (FAST) take_scales(kt + 1);
+          }
+          if (m >= NM / 2) {
+            cvt_part(0, nxt, (2 * (m - NM / 2)) / 4, (2 * (m - NM / 2)) % 4);
+            cvt_part(0, nxt, (2 * (m - NM / 2) + 1) / 4, (2 * (m - NM / 2) + 1) % 4);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int m = NM; m < RA; ++m) copy_a(kt2, As, m);
+      } else {
+        if (more_a) issue_a(kt + 2, sa);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_fa(As1, 0, nxt, i);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) mfma_m(cur, m);
+        wait_lgkmcnt0();
+        if constexpr (FAST) take_scales(kt + 1);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) cvt_part(0, nxt, m / 4, m % 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int kt = 0;
+  if constexpr (FAST) {
+    // every tile but the last ends with a steady boundary; the steady steps
+    // come in pairs (constant stage indices), kt is even after the loop
+    const int nb = ktiles - 1;
+    for (; kt + 2 <= nb; kt += 2) {
+      tile_step(kt, int_c<kSteady>{}, int_c<0>{});
+      tile_step(kt + 1, int_c<kSteady>{}, int_c<1>{});
+    }
+    if (kt < nb) {
+      tile_step(kt, int_c<kSteady>{}, int_c<0>{});
+      ++kt;
+    }
+    if (kt & 1) tile_step(kt, int_c<kLast>{}, int_c<1>{});
+    else tile_step(kt, int_c<kLast>{}, int_c<0>{});
+  } else {
+    const int steady_end = ktiles - 2 - (tail_tile >= 0 ? 1 : 0);
+    for (; kt + 2 <= steady_end; kt += 2) {
+      tile_step(kt, int_c<kSteady>{}, int_c<0>{});
+      tile_step(kt + 1, int_c<kSteady>{}, int_c<1>{});
+    }
+    for (; kt < ktiles; ++kt) tile_step(kt, int_c<kGeneral>{}, int_c<-1>{});
+  }
+
+  store_tile<GATED, NJ>(a, acc, e, false, N, n0, r0, r_end, wm, wn, lane);
+}
+
+// The FAST kernel applies: K % 64 == 0 and the scale tensor [E, N, K / 32]
+// 4-byte aligned in base and size (its dwords can then be copied whole).
+bool fast_shape(const Layer& L, int K, int N, const uint8_t* scales) {
+  const size_t bytes = (size_t)L.E * N * (K / 32);
+  return K % BK == 0 && reinterpret_cast<uintptr_t>(scales) % 4 == 0 && bytes % 4 == 0;
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_mxfp4(const Layer& L, const Work& W, hipStream_t s) {
+  MfmaArgs m = base_args(L, W);
+  m.a = static_cast<const uint16_t*>(L.x);
+  m.lda = L.d;
+  m.row_token = W.row_token;
+  m.c0 = L.wg_codes; m.s0 = L.wg_scales; m.c1 = L.wu_codes; m.s1 = L.wu_scales;
+  m.bias0 = static_cast<const uint16_t*>(L.bg);
+  m.bias1 = static_cast<const uint16_t*>(L.bu);
+  m.N = L.F; m.K = L.d; m.N_sh = L.F; m.K_sh = L.d;
+  m.out = static_cast<uint16_t*>(W.h);
+  m.ldo = L.F_max();
+  m.n_tiles = (L.F + 127) / 128;
+  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  if (fast_shape(L, L.d, L.F, L.wg_scales) && fast_shape(L, L.d, L.F, L.wu_scales))
+    mxfp4_gemm_kernel<true, 4, true><<<grid, kThreads, 0, s>>>(m);
+  else
+    mxfp4_gemm_kernel<true, 4, false><<<grid, kThreads, 0, s>>>(m);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mxfp4(const Layer& L, const Work& W, hipStream_t s) {
+  MfmaArgs m = base_args(L, W);
+  m.a = static_cast<const uint16_t*>(W.h);
+  m.lda = L.F_max();
+  m.row_token = nullptr;
+  m.c0 = L.wd_codes; m.s0 = L.wd_scales;
+  m.bias0 = static_cast<const uint16_t*>(L.bd);
+  m.N = L.d; m.K = L.F; m.N_sh = L.d; m.K_sh = L.F;
+  m.out = static_cast<uint16_t*>(W.y);
+  m.ldo = L.d;
+  // column tiles of 256 or 192, whichever copies fewer A bytes in total
+  const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
+  const bool narrow = t192 * (256 + 48) < t256 * (256 + 64);
+  m.n_tiles = narrow ? t192 : t256;
+  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  const bool fast = fast_shape(L, L.F, L.d, L.wd_scales);
+  if (narrow) {
+    if (fast) mxfp4_gemm_kernel<false, 3, true><<<grid, kThreads, 0, s>>>(m);
+    else mxfp4_gemm_kernel<false, 3, false><<<grid, kThreads, 0, s>>>(m);
+  } else {
+    if (fast) mxfp4_gemm_kernel<false, 4, true><<<grid, kThreads, 0, s>>>(m);
+    else mxfp4_gemm_kernel<false, 4, false><<<grid, kThreads, 0, s>>>(m);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

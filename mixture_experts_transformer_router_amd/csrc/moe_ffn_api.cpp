@@ -75,6 +75,14 @@ moe_status check_common(const Layer& L) {
   if (L.dt != MOE_F32 && L.dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", L.dt);
   const int q = L.wfmt == WF_MXFP4 ? 32 : 8;
   if (L.d % q || L.F % q) return fail(MOE_ERR_UNSUPPORTED, "d = %d and d_ff = %d must be multiples of %d", L.d, L.F, q);
+  if (L.wfmt == WF_MXFP4) {
+    // the MXFP4 kernels address one expert's codes and the activation rows
+    // with 32-bit offsets
+    if ((unsigned long long)L.d * L.F / 2 >= (1ull << 32))
+      return fail(MOE_ERR_UNSUPPORTED, "d * d_ff = %lld >= 2^33 with MXFP4 weights", (long long)L.d * L.F);
+    if ((unsigned long long)L.rows_all() * (L.d > L.F ? L.d : L.F) >= (1ull << 32))
+      return fail(MOE_ERR_UNSUPPORTED, "T * k * max(d, d_ff) >= 2^32 with MXFP4 weights");
+  }
   if (L.act != MOE_ACT_CLIPPED_SWIGLU && L.act != MOE_ACT_SILU) return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", L.act);
   if (L.act == MOE_ACT_CLIPPED_SWIGLU) {
     if (!(L.limit > 0.f) || !std::isfinite(L.limit)) return fail(MOE_ERR_INVALID_ARG, "limit = %g must be finite and > 0", (double)L.limit);
@@ -133,20 +141,23 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   // Expert stages: weight streaming on MFMA for a few tokens (every expert
   // then holds at most kDecodeMaxTokens rows), grouped MFMA GEMMs for bf16 /
   // MXFP4 otherwise, vector-ALU tiles for fp32.
-  enum { kDecode, kMfma, kTiled } path;
+  enum { kDecode, kMfma, kMxfp4, kTiled } path;
   if (L.dt == MOE_F32) path = kTiled;
-  else if (L.wfmt == WF_BF16 && L.T <= kDecodeMaxTokens) path = kDecode;
+  else if (L.wfmt == WF_MXFP4) path = kMxfp4;
+  else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     e = path == kDecode ? launch_gate_up_decode(L, W, s)
-        : path == kMfma ? launch_gate_up_mfma(L, W, s) : launch_gate_up(L, W, s);
+        : path == kMfma ? launch_gate_up_mfma(L, W, s)
+        : path == kMxfp4 ? launch_gate_up_mxfp4(L, W, s) : launch_gate_up(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
     StageTimer tm(s, MOE_STAGE_DOWN);
     e = path == kDecode ? launch_down_decode(L, W, s)
-        : path == kMfma ? launch_down_mfma(L, W, s) : launch_down(L, W, s);
+        : path == kMfma ? launch_down_mfma(L, W, s)
+        : path == kMxfp4 ? launch_down_mxfp4(L, W, s) : launch_down(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
   {

@@ -105,6 +105,8 @@ hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_gate_up_mxfp4(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down_mxfp4(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
 
 }  // namespace moe

@@ -143,3 +143,6 @@ def test_mxfp4_argument_checks(lib):
     assert call(d=48) == M.MOE_ERR_UNSUPPORTED
     assert call(F=40) == M.MOE_ERR_UNSUPPORTED
     assert call(codes=None) == M.MOE_ERR_INVALID_ARG
+    # one expert's codes must stay under 2^32 bytes (32-bit offsets in the kernels)
+    assert call(d=65536, F=131072) == M.MOE_ERR_UNSUPPORTED
+    assert b"2^33" in lib.moe_last_error_detail()

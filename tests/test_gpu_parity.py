@@ -13,7 +13,8 @@ from mixture_experts_transformer_router_amd import layer as LY
 from mixture_experts_transformer_router_amd import moe_ffn
 from mixture_experts_transformer_router_amd import workloads as W
 
-from parity_util import check_layer
+from oracle import moe_oracle as O
+from parity_util import cfg_of, check_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +101,38 @@ def test_all_tokens_on_one_expert():
     a["router_b"] = I.f32_to_bf16_bits(b)
     rep = _run_and_check(w, a=a)
     assert rep["tokens_checked"] == 300
+
+
+def test_mxfp4_nan_scale_gives_nan_exactly_where_the_block_is_used():
+    # e8m0 byte 255 is NaN (OCP MX v1.0): a NaN gate block makes every output
+    # of the tokens routed to that expert NaN; a NaN down block only the one
+    # output column of those tokens.  Everything else must stay finite and
+    # match the oracle under the GPU's own routing.
+    w = W.GPTOSS_MXFP4.scaled(T=150, d=256, d_ff=160, E=8, k=2, name="mxfp4_nan_scale")
+    a = I.make_inputs(w)
+    a["w_gate_scales"] = a["w_gate_scales"].copy()
+    a["w_gate_scales"][3, 5, 1] = 255     # expert 3, gate row 5, elements 32..63
+    a["w_down_scales"] = a["w_down_scales"].copy()
+    a["w_down_scales"][6, 10, 4] = 255    # expert 6, output column 10, elements 128..159
+    _say(f"[case] {w.name} T={w.T} d={w.d} F={w.d_ff} E={w.E} k={w.k} seed={w.seed}")
+    t = LY.to_device(a, DEV)
+    out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, r = LY.run(w, t, out=out, routing=True)
+    torch.cuda.synchronize()
+    cfg = cfg_of(w)
+    g_idx = r["topk_idx"].cpu().numpy().astype(np.int64)
+    logits, _, _ = O.route(a, cfg)
+    ref = O.experts_forward(a, cfg, g_idx, O.forced_weights(logits, g_idx, cfg))
+    got = out.float().cpu().numpy().astype(np.float64)
+    nan_ref = np.isnan(ref)
+    rows_all_nan = nan_ref.all(axis=1)
+    assert rows_all_nan.any(), "no token routed to expert 3"
+    assert (nan_ref[~rows_all_nan, 10]).any(), "no token routed to expert 6 alone"
+    np.testing.assert_array_equal(np.isnan(got), nan_ref)
+    fin = ~nan_ref
+    err = np.abs(got[fin] - ref[fin]).max()
+    assert err <= 2e-2 * np.abs(ref[fin]).max(), err
+    _say(f"[ok] {w.name}: nan rows {int(rows_all_nan.sum())}, max err {err:.3e}")
 
 
 def test_exact_logit_ties_lowest_index_wins():
