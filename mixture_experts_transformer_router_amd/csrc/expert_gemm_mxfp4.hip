@@ -48,7 +48,7 @@ constexpr int BK = 64;                   // K elements per A stage and per decod
 constexpr int kTilesPerGroup = 4;        // K tiles per code group (128 code bytes of a row)
 constexpr int kCodeRowBytes = 128;
 // kinds of K-tile step (see tile_step)
-constexpr int kSteady = 0, kGeneral = 1, kLast = 2;
+constexpr int kSteady = 0, kGeneral = 1, kLast = 2, kFinal = 3;
 template <int V> using int_c = std::integral_constant<int, V>;
 
 // Stored position of 16-byte chunk c of code row r in LDS: XOR-swizzled by
@@ -289,9 +289,12 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   };
 
   // ---- prologue: A of tiles 0 and 1, code (and FAST: scale) groups 0 and 1,
-  // (else: scales of tiles 0 and 1)
-  issue_a(0, 0);
-  if (ktiles > 1) issue_a(1, 1);
+  // (else: scales of tiles 0 and 1).  Tile kt uses A stage (kt + off) % 2;
+  // FAST kernels pick off so that the last tile always uses stage 1 (every
+  // step after the steady loop then has compile-time stages).
+  const int off = FAST ? (ktiles & 1) : 0;
+  issue_a(0, off);
+  if (ktiles > 1) issue_a(1, off ^ 1);
   issue_codes(0);
   if (kCodeRowBytes < code_bytes) issue_codes(1);
   if constexpr (FAST) {
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   }
   read_codes(0, true);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_fa(lds_a0, 0, 0, i);
+  for (int i = 0; i < 4; ++i) load_fa(stage_a(off), 0, 0, i);
   wait_lgkmcnt0();
 #pragma unroll
   for (int m = 0; m < NM; ++m) cvt_part(0, 0, m / 4, m % 4);
@@ -327,11 +330,13 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   // scales, then alternates its MFMAs with the copies of A(kt+2) into the
   // stage tile kt used and with tile kt+1's first fragments.
   // MODE kSteady: tile kt+1 exists and is no tail tile (copies past the last
-  // tile are clamped to it, into a stage nobody reads again); kLast: tile kt
-  // is the last one; kGeneral: run-time checks.
+  // tile are clamped to it, into a stage nobody reads again); kFinal: tile
+  // kt+1 is the last one (no copies); kLast: tile kt is the last one;
+  // kGeneral: run-time checks.
   auto tile_step = [&](int kt, auto mode_tag, auto phase_tag) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_tag)::value;
-    constexpr bool STEADY = MODE == kSteady;
+    constexpr bool STEADY = MODE == kSteady || MODE == kFinal;
+    constexpr bool COPIES = MODE != kFinal;
     constexpr int PH = decltype(phase_tag)::value;  // kt % 2 if >= 0
     const int sa = PH >= 0 ? PH : kt & 1;
     const int sa1 = PH >= 0 ? PH ^ 1 : (kt + 1) & 1;
@@ -367,10 +372,10 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
         load_scales(kt + 1);  // LDS reads; converted once they have landed
       } else {
         take_scales(kt + 1);
-        if (STEADY || kt + 2 < ktiles) load_scales(kt + 2);
+        if (COPIES && (STEADY || kt + 2 < ktiles)) load_scales(kt + 2);
       }
       const int g1 = (kt + 1) / kTilesPerGroup + 1;
-      if ((kt + 1) % kTilesPerGroup == 0 && kCodeRowBytes * g1 < code_bytes) {
+      if (COPIES && (kt + 1) % kTilesPerGroup == 0 && kCodeRowBytes * g1 < code_bytes) {
         issue_codes(g1);
         if constexpr (FAST) issue_scales(g1);
       }
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           mfma_m(cur, m);
-          if (m < RA) copy_a(kt2, As, m);
+          if (COPIES && m < RA) copy_a(kt2, As, m);
           if (m < 4) load_fa(As1, 0, nxt, m);
           if (m == NM / 2 - 1) {
             wait_lgkmcnt0();
@@ -396,7 +401,8 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int m = NM; m < RA; ++m) copy_a(kt2, As, m);
+        for (int m = NM; m < RA; ++m)
+          if (COPIES) copy_a(kt2, As, m);
       } else {
         if (more_a) issue_a(kt + 2, sa);
 #pragma unroll
@@ -413,19 +419,20 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   };
   int kt = 0;
   if constexpr (FAST) {
-    // every tile but the last ends with a steady boundary; the steady steps
-    // come in pairs (constant stage indices), kt is even after the loop
-    const int nb = ktiles - 1;
-    for (; kt + 2 <= nb; kt += 2) {
+    // stages: tile kt in (kt + off) % 2, the last tile in stage 1.  An odd
+    // ktiles starts with one steady step in stage 1; then steady pairs up
+    // to tile ktiles - 3, the final boundary (tile ktiles - 2, stage 0) and
+    // the last tile.
+    if (off && ktiles >= 2) {
+      tile_step(0, int_c<kSteady>{}, int_c<1>{});
+      kt = 1;
+    }
+    for (; kt + 2 <= ktiles - 2; kt += 2) {
       tile_step(kt, int_c<kSteady>{}, int_c<0>{});
       tile_step(kt + 1, int_c<kSteady>{}, int_c<1>{});
     }
-    if (kt < nb) {
-      tile_step(kt, int_c<kSteady>{}, int_c<0>{});
-      ++kt;
-    }
-    if (kt & 1) tile_step(kt, int_c<kLast>{}, int_c<1>{});
-    else tile_step(kt, int_c<kLast>{}, int_c<0>{});
+    if (ktiles >= 2) tile_step(ktiles - 2, int_c<kFinal>{}, int_c<0>{});
+    tile_step(ktiles - 1, int_c<kLast>{}, int_c<1>{});
   } else {
     const int steady_end = ktiles - 2 - (tail_tile >= 0 ? 1 : 0);
     for (; kt + 2 <= steady_end; kt += 2) {

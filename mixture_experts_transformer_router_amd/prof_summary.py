@@ -31,7 +31,7 @@ DEFAULT_COPY_BYTES = 1 << 28
 
 
 def short_name(name: str) -> str:
-    """moe::(anonymous namespace)::mfma_gemm_kernel<1, true, 4, 32, 5>(...) -> mfma_gemm_kernel<1, true, 4, 32, 5>"""
+    """moe::(anonymous namespace)::mfma_gemm_kernel<true, 4, 64, 2, 2>(...) -> mfma_gemm_kernel<true, 4, 64, 2, 2>"""
     n = re.sub(r"\(.*$", "", name.replace("(anonymous namespace)::", ""))
     n = n.replace("void ", "").replace("moe::", "")
     return n.strip()
@@ -93,7 +93,8 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources each timed kernel family is built from
 KERNEL_SOURCES = {
     "decode_kernel": ["expert_decode.hip"],
-    "mfma_gemm_kernel": ["expert_gemm_mfma.hip"],
+    "mfma_gemm_kernel": ["expert_gemm_mfma.hip", "gemm_common.h"],
+    "mxfp4_gemm_kernel": ["expert_gemm_mxfp4.hip", "gemm_common.h"],
 }
 COMMON_SOURCES = ["device_common.h", "moe_internal.h"]
 
