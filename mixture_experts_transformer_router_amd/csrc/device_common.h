@@ -36,10 +36,11 @@ template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, siz
 // Logistic function with the hardware exp2 and reciprocal (about 2 ulp).
 __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-// v clipped to [lo, hi]; NaN stays NaN (the hardware min / max / median
-// return the other operand for a NaN input).
+// v clipped to [lo, hi]; NaN stays NaN: IEEE 754-2019 maximum / minimum
+// (gfx950 v_maximum3_f32 / v_minimum3_f32; the older min / max / median
+// instructions return the other operand for a NaN input).
 __device__ __forceinline__ float clip_nan(float v, float lo, float hi) {
-  return __builtin_isnan(v) ? v : __builtin_amdgcn_fmed3f(v, lo, hi);
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, lo), hi);
 }
 
 // Expert activation.  act 0: clipped SwiGLU (gate clipped to [0, limit], up to

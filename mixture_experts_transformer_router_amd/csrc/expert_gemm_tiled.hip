@@ -1,6 +1,5 @@
-// Grouped expert GEMMs on the vector ALUs, for every storage format
-// (fp32, bf16, MXFP4).  This is the path for fp32 layers and the reference
-// shape of the two expert stages:
+// Grouped expert GEMMs on the vector ALUs for fp32 layers (fp32 data,
+// fp32 accumulation):
 //
 //   gate|up:  for sorted row r of expert e with token t = row_token[r]
 //             g = x[t] . Wg[e][f] + bg[e][f],  u = x[t] . Wu[e][f] + bu[e][f],
@@ -35,10 +34,6 @@ struct GemmArgs {
   const int32_t* row_token;  // gate|up: token of each sorted row; down: nullptr
   const void* w0;            // dense weights [E, N, K] (down, or gate)
   const void* w1;            // dense up weights (gate|up only)
-  const uint8_t* c0;         // MXFP4 codes / scales of w0, w1
-  const uint8_t* s0;
-  const uint8_t* c1;
-  const uint8_t* s1;
   const void* bias0;         // [E, N] or nullptr
   const void* bias1;
   const void* sh_w0;         // shared expert weights [N_sh, K_sh] or nullptr
@@ -54,29 +49,7 @@ struct GemmArgs {
   float alpha, limit;
 };
 
-__device__ __forceinline__ float e2m1(uint32_t c) {
-  const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
-  float v = mag[c & 7u];
-  return (c & 8u) ? -v : v;
-}
-
-// Weight element (n, kk) of expert e.
-template <int WF, typename TA>
-__device__ __forceinline__ float load_w(const void* w, const uint8_t* codes, const uint8_t* scales,
-                                        int e, int n, int kk, int N, int K) {
-  if constexpr (WF == WF_MXFP4) {
-    const size_t row = (size_t)e * N + n;
-    const uint32_t byte = codes[row * (K / 2) + kk / 2];
-    const uint32_t c = (kk & 1) ? (byte >> 4) : (byte & 15u);
-    const int s = scales[row * (K / 32) + kk / 32];
-    if (s == 255) return __uint_as_float(0x7fc00000u);
-    return ldexpf(e2m1(c), s - 127);
-  } else {
-    return load_f32(static_cast<const TA*>(w), ((size_t)e * N + n) * K + kk);
-  }
-}
-
-template <typename TA, int WF, bool GATED>
+template <typename TA, bool GATED>
 __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(GemmArgs a) {
   __shared__ float As[BK][BM + 1];
   __shared__ float Bs0[BK][BN + 1];
@@ -128,8 +101,8 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(GemmArgs a) {
         Bs0[lk + q][lr] = ok ? load_f32(static_cast<const TA*>(w0), (size_t)n * K + kk) : 0.f;
         if constexpr (GATED) Bs1[lk + q][lr] = ok ? load_f32(static_cast<const TA*>(w1), (size_t)n * K + kk) : 0.f;
       } else {
-        Bs0[lk + q][lr] = ok ? load_w<WF, TA>(w0, a.c0, a.s0, we, n, kk, N, K) : 0.f;
-        if constexpr (GATED) Bs1[lk + q][lr] = ok ? load_w<WF, TA>(w1, a.c1, a.s1, we, n, kk, N, K) : 0.f;
+        Bs0[lk + q][lr] = ok ? load_f32(static_cast<const TA*>(w0), ((size_t)we * N + n) * K + kk) : 0.f;
+        if constexpr (GATED) Bs1[lk + q][lr] = ok ? load_f32(static_cast<const TA*>(w1), ((size_t)we * N + n) * K + kk) : 0.f;
       }
     }
     __syncthreads();
@@ -175,10 +148,10 @@ __global__ __launch_bounds__(kThreads) void tiled_gemm_kernel(GemmArgs a) {
   }
 }
 
-template <typename TA, int WF, bool GATED>
+template <typename TA, bool GATED>
 hipError_t launch_t(const GemmArgs& a, int rows_all, int n_max, hipStream_t s) {
   dim3 grid((rows_all + BM - 1) / BM + a.E_all, (n_max + BN - 1) / BN);
-  tiled_gemm_kernel<TA, WF, GATED><<<grid, kThreads, 0, s>>>(a);
+  tiled_gemm_kernel<TA, GATED><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -200,29 +173,26 @@ hipError_t launch_gate_up(const Layer& L, const Work& W, hipStream_t s) {
   GemmArgs g = common_args(L, W);
   g.a = L.x; g.lda = L.d; g.row_token = W.row_token;
   g.w0 = L.wg; g.w1 = L.wu;
-  g.c0 = L.wg_codes; g.s0 = L.wg_scales; g.c1 = L.wu_codes; g.s1 = L.wu_scales;
   g.bias0 = L.bg; g.bias1 = L.bu;
   g.sh_w0 = L.sh_wg; g.sh_w1 = L.sh_wu;
   g.N = L.F; g.K = L.d; g.N_sh = L.F_sh; g.K_sh = L.d;
   g.out = W.h; g.ldo = L.F_max();
   const int rows = L.rows_all(), nmax = L.F_max();
-  if (L.dt == MOE_F32) return launch_t<float, WF_F32, true>(g, rows, nmax, s);
-  if (L.wfmt == WF_MXFP4) return launch_t<uint16_t, WF_MXFP4, true>(g, rows, nmax, s);
-  return launch_t<uint16_t, WF_BF16, true>(g, rows, nmax, s);
+  if (L.dt != MOE_F32) return hipErrorInvalidValue;  // bf16 and MXFP4 layers take the MFMA kernels
+  return launch_t<float, true>(g, rows, nmax, s);
 }
 
 hipError_t launch_down(const Layer& L, const Work& W, hipStream_t s) {
   GemmArgs g = common_args(L, W);
   g.a = W.h; g.lda = L.F_max(); g.row_token = nullptr;
-  g.w0 = L.wd; g.c0 = L.wd_codes; g.s0 = L.wd_scales;
+  g.w0 = L.wd;
   g.bias0 = L.bd;
   g.sh_w0 = L.sh_wd;
   g.N = L.d; g.K = L.F; g.N_sh = L.d; g.K_sh = L.F_sh;
   g.out = W.y; g.ldo = L.d;
   const int rows = L.rows_all();
-  if (L.dt == MOE_F32) return launch_t<float, WF_F32, false>(g, rows, L.d, s);
-  if (L.wfmt == WF_MXFP4) return launch_t<uint16_t, WF_MXFP4, false>(g, rows, L.d, s);
-  return launch_t<uint16_t, WF_BF16, false>(g, rows, L.d, s);
+  if (L.dt != MOE_F32) return hipErrorInvalidValue;
+  return launch_t<float, false>(g, rows, L.d, s);
 }
 
 }  // namespace moe

@@ -97,8 +97,7 @@ __device__ __forceinline__ float quad_xor2(float v) {
 }
 
 // The expert activation with its kind fixed at compile time (no per-element
-// branch); the clamps are v_med3_f32 plus a NaN select (the C ABI guarantees
-// limit > 0).
+// branch); the clamps keep NaN (clip_nan; the C ABI guarantees limit > 0).
 // act 0: clipped SwiGLU, act 1: SiLU-GLU, as expert_act().
 template <int ACT>
 __device__ __forceinline__ float expert_act_t(float g, float u, float alpha, float limit) {
