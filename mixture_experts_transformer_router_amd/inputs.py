@@ -15,6 +15,7 @@ Layout of every array (row-major, contiguous):
   w_down       [E, d, d_ff]      expert down projection, [out, in]
   b_down       [E, d]
   shared_w_gate/shared_w_up [d_ff_shared, d], shared_w_down [d, d_ff_shared]
+  norm_w       [d]               RMSNorm scale of a MoE block (block workloads)
 
 bf16 arrays are stored as numpy uint16 bit patterns; f32 arrays as float32.
 MXFP4 weights replace w_* by (codes, scales):
@@ -24,8 +25,8 @@ MXFP4 weights replace w_* by (codes, scales):
            consecutive input-dim elements.
 
 Draw order from numpy.random.default_rng(seed) (PCG64): x, router_w,
-router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, shared gate/up/down;
-weights drawn one expert at a time.  Weights ~ N(0, 1/d_in) (std d_in^-1/2),
+router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, shared gate/up/down,
+norm_w; weights drawn one expert at a time.  norm_w ~ 1 + N(0, 0.1^2).  Weights ~ N(0, 1/d_in) (std d_in^-1/2),
 biases ~ N(0, 0.02^2), x ~ N(0, 1).  The router bias is zero, normal, or
 log Zipf(s) over expert rank (b_e = -s*ln(e+1)), per workload.
 """
@@ -118,5 +119,10 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         out["shared_w_gate"] = _normal(rng, (Fs, d), d ** -0.5, dt)
         out["shared_w_up"] = _normal(rng, (Fs, d), d ** -0.5, dt)
         out["shared_w_down"] = _normal(rng, (d, Fs), Fs ** -0.5, dt)
+    if w.block:
+        # RMSNorm scale, drawn last so that the layer's other arrays are those
+        # of the same workload without the block
+        g = np.float32(1.0) + np.float32(0.1) * rng.standard_normal(size=d, dtype=np.float32)
+        out["norm_w"] = f32_to_bf16_bits(g) if dt == "bf16" else g
     return out
 

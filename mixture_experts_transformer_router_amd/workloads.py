@@ -1,4 +1,4 @@
-"""The five MoE-FFN layer workloads this library is tested and measured on.
+"""The MoE-FFN layer workloads this library is tested and measured on.
 
 Each workload fixes the layer's shapes, its routing flavour and the recipe of
 its seeded synthetic inputs.  Shapes follow the pages:
@@ -44,6 +44,10 @@ class Workload:
     routed_scaling_factor: float = 1.0
     score: str = "softmax"     # "softmax" | "sigmoid"
     d_ff_shared: int = 0       # 0 = no shared expert
+    # MoE block (glm4_moe_lite.go, MoEBlock.Forward after attention):
+    # out = x + layer(RMSNorm(x; gamma, norm_eps))
+    block: bool = False
+    norm_eps: float = 1e-5
     # input recipe
     router_bias: str = "normal"   # "normal" | "zero" | "zipf" | "none"
     expert_bias: bool = True
@@ -88,4 +92,12 @@ GLM4_MOE_LITE = Workload(
     router_bias="none", expert_bias=False)
 
 ALL = (TINY_F32, GPTOSS_DECODE, GPTOSS_PREFILL, GPTOSS_MXFP4, GLM4_MOE_LITE)
-BY_NAME = {w.name: w for w in ALL}
+
+# The same layers as MoE blocks: RMSNorm in front, residual added
+# (glm4_moe_lite.go, MoEBlock.Forward; Config.RMSNormEps).
+GLM4_MOE_LITE_BLOCK = GLM4_MOE_LITE.scaled(name="glm4moelite_block_T2048_d2048_F1536_E64s1_k6_g8tg4",
+                                           block=True)
+GPTOSS_DECODE_BLOCK = GPTOSS_DECODE.scaled(name="gptoss20b_block_decode_T8_d2880_E32_k4_bf16", block=True)
+BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK)
+
+BY_NAME = {w.name: w for w in ALL + BLOCKS}

@@ -43,6 +43,10 @@ reason in the design notes of this repository):
   * The shared expert is a SiLU-gated MLP without bias, weight 1, added after
     the routed sum ([GLM] SharedExperts.Forward, MoE.Forward).
   * Permutation: pairs p = t*k + j sorted by (expert, p) (a stable sort).
+  * MoE block ([GLM] MoEBlock.Forward, the half after attention): the layer
+    sees RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma (nn.RMSNorm with
+    Config.RMSNormEps; the pages do not print its formula, this is the plain
+    definition) and its output is added to x.
 """
 from __future__ import annotations
 
@@ -270,6 +274,30 @@ class ExpertWeights:
 
 
 # ----------------------------------------------------------------------------
+# MoE block: RMSNorm before the layer, residual after it.
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis ([GLM] MoEBlock.Forward applies
+    PostAttentionLayerNorm, an nn.RMSNorm with Config.RMSNormEps, to the MoE
+    input):  y = x / sqrt(mean(x^2) + eps) * gamma."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma
+
+
+def layer_input(arrays: dict, cfg: dict, tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """The rows the MoE layer works on, float64: x, or RMSNorm(x) with the
+    block's gamma (arrays["norm_w"]) when cfg["block"] is set."""
+    dt = cfg["dtype"]
+    x = to_f64(arrays["x"], dt)
+    if tokens is not None:
+        x = x[tokens]
+    if cfg.get("block"):
+        x = rms_norm(x, to_f64(arrays["norm_w"], dt), float(cfg["norm_eps"]))
+    return x
+
+
+# ----------------------------------------------------------------------------
 # Routing of a whole layer, permutation, and the layer forward.
 
 
@@ -278,11 +306,10 @@ def route(arrays: dict, cfg: dict, tokens: Optional[np.ndarray] = None):
 
     cfg keys: dtype, k, routing ("gptoss" | "grouped"); for grouped routing
     also n_group, topk_group, norm_topk_prob, routed_scaling_factor, score;
-    optional e_score_bias (float array [E])."""
+    optional e_score_bias (float array [E]); block and norm_eps for a MoE
+    block (the router sees RMSNorm(x))."""
     dt = cfg["dtype"]
-    x = to_f64(arrays["x"], dt)
-    if tokens is not None:
-        x = x[tokens]
+    x = layer_input(arrays, cfg, tokens)
     l = router_logits(x, to_f64(arrays["router_w"], dt), to_f64(arrays.get("router_b"), dt))
     if cfg.get("routing", "gptoss") == "gptoss":
         idx, w = gptoss_route(l, cfg["k"])
@@ -326,11 +353,11 @@ def experts_forward(arrays: dict, cfg: dict, idx: np.ndarray, w: np.ndarray,
         out[t] = sum_{j = 0..k-1} w[t, j] * FFN_{idx[t, j]}(x_t)   (+ shared(x_t))
 
     ([GLM] MoE.Forward: sum over the k expert outputs weighted by the gate
-    scores, then the shared experts added).  idx/w are [len(tokens), k]."""
+    scores, then the shared experts added).  idx/w are [len(tokens), k].
+    For a MoE block (cfg["block"]) the experts see RMSNorm(x) and the result
+    is added to x ([GLM] MoEBlock.Forward)."""
     dt = cfg["dtype"]
-    x = to_f64(arrays["x"], dt)
-    if tokens is not None:
-        x = x[tokens]
+    x = layer_input(arrays, cfg, tokens)
     n, k = idx.shape
     W = ExpertWeights(arrays, dt, cfg.get("weights", "dense"))
     act, alpha, limit = cfg.get("act", "clipped_swiglu"), cfg.get("alpha", 1.702), cfg.get("limit", 7.0)
@@ -344,6 +371,9 @@ def experts_forward(arrays: dict, cfg: dict, idx: np.ndarray, w: np.ndarray,
     sh = W.shared()
     if sh is not None:
         out += expert_mlp(x, *sh, "silu", 0.0, 0.0)
+    if cfg.get("block"):
+        x_in = to_f64(arrays["x"], dt)
+        out = out + (x_in if tokens is None else x_in[tokens])
     return out
 
 

@@ -28,7 +28,7 @@ def cfg_of(w, e_score_bias=None) -> dict:
     c = dict(dtype=w.dtype, weights=w.weights, routing=w.routing, act=w.act, alpha=w.alpha,
              limit=w.limit, k=w.k, E=w.E, n_group=w.n_group, topk_group=w.topk_group,
              norm_topk_prob=w.norm_topk_prob, routed_scaling_factor=w.routed_scaling_factor,
-             score=w.score)
+             score=w.score, block=w.block, norm_eps=w.norm_eps)
     if e_score_bias is not None:
         c["e_score_bias"] = np.asarray(e_score_bias, dtype=np.float64)
     return c

@@ -319,3 +319,67 @@ def test_generator_is_seeded_and_shaped():
     assert a1["x"].shape == (16, 64) and a1["w_down"].shape == (8, 64, 64)
     assert a1["x"].dtype == np.float32
     assert abs(a1["router_w"].std() - 1 / 8) < 0.02
+
+# --------------------------------------------------------------------------- MoE block
+
+
+def test_rms_norm_golden_points():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "rmsnorm_points.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        eps, x, g, y = [part.split() for part in line.split("|")]
+        got = O.rms_norm(np.array([float(v) for v in x]), np.array([float(v) for v in g]), float(eps[0]))
+        np.testing.assert_allclose(got, [float(v) for v in y], rtol=1e-14, atol=1e-15)
+        n += 1
+    assert n == 5
+
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(4)
+    x = rng.normal(0, 3, (7, 37))
+    g = rng.normal(1, 0.1, 37)
+    want = F.rms_norm(_t(x), (37,), weight=_t(g), eps=1e-5).numpy()
+    np.testing.assert_allclose(O.rms_norm(x, g, 1e-5), want, rtol=1e-13)
+
+
+def _small_block():
+    w = W.GLM4_MOE_LITE.scaled(T=40, d=64, d_ff=32, E=8, k=2, n_group=4, topk_group=2, d_ff_shared=16,
+                               block=True, name="pin_block")
+    return w, I.make_inputs(w)
+
+
+def _cfg(w, **over):
+    c = dict(dtype=w.dtype, weights=w.weights, routing=w.routing, act=w.act, alpha=w.alpha, limit=w.limit,
+             k=w.k, E=w.E, n_group=w.n_group, topk_group=w.topk_group, norm_topk_prob=w.norm_topk_prob,
+             routed_scaling_factor=w.routed_scaling_factor, score=w.score, block=w.block, norm_eps=w.norm_eps)
+    c.update(over)
+    return c
+
+
+def test_block_residual_is_the_input_when_the_experts_vanish():
+    # all expert and shared weights zero, no biases: every expert output is 0,
+    # so the block returns its input exactly
+    w, a = _small_block()
+    a = dict(a)
+    for name in ("w_gate", "w_up", "w_down", "shared_w_gate", "shared_w_up", "shared_w_down"):
+        a[name] = np.zeros_like(a[name])
+    out = O.moe_layer(a, _cfg(w))["out"]
+    np.testing.assert_array_equal(out, O.to_f64(a["x"], w.dtype))
+
+
+def test_block_norm_feeds_the_layer():
+    # with eps = 0, RMSNorm(c x) = RMSNorm(x) for c > 0: the MoE part of the
+    # block (output minus input) does not change when x is scaled, while the
+    # plain layer's output does
+    w, a = _small_block()
+    cfg = _cfg(w, norm_eps=0.0)
+    x = O.to_f64(a["x"], w.dtype)
+    a2 = dict(a)
+    a2["x"] = I.f32_to_bf16_bits((4.0 * x).astype(np.float32))   # exact: a power of two
+    m1 = O.moe_layer(a, cfg)["out"] - x
+    m2 = O.moe_layer(a2, cfg)["out"] - 4.0 * x
+    np.testing.assert_allclose(m2, m1, rtol=1e-12, atol=1e-12)
+    plain = _cfg(w, block=False)
+    assert np.abs(O.moe_layer(a2, plain)["out"] - O.moe_layer(a, plain)["out"]).max() > 1e-3
