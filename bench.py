@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE-FFN layer on one MI355X; prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|mxfp4|glm|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
 default workload is the GPT-OSS-20B-shaped decode layer (T=8, d=d_ff=2880,
 E=32, k=4, bf16).  Expert weights rotate over several device copies so that
-successive steps cannot hit the 256 MB last-level cache.
+successive steps cannot hit the 256 MB last-level cache.  The block_*
+workloads run the same layers as MoE blocks (RMSNorm in front, residual
+after).
 
 `value` is tokens/s over the K timed steps.  `roofline` reports the gate|up
 kernel: algorithmic bytes (decode) or flops (prefill) per launch divided by
@@ -37,7 +40,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "mxfp4", "glm", "tiny"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -49,7 +53,8 @@ def parse():
 def workload(name):
     from mixture_experts_transformer_router_amd import workloads as W
     return {"decode": W.GPTOSS_DECODE, "prefill": W.GPTOSS_PREFILL, "mxfp4": W.GPTOSS_MXFP4,
-            "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32}[name]
+            "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
+            "block_glm": W.GLM4_MOE_LITE_BLOCK}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -130,7 +135,8 @@ def main():
     from mixture_experts_transformer_router_amd import moe_ffn
 
     w = workload(args.workload)
-    steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100}[args.workload]
+    steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
+                           "block_decode": 500, "block_glm": 100}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -176,7 +182,7 @@ def main():
 
     gu_ms, gu_n = prof["gate_up"]
     gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
-    if args.workload in ("decode",):
+    if args.workload in ("decode", "block_decode"):
         roof = {"bound": "hbm", "achieved": nbytes / gu_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": flops / gu_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}

@@ -172,6 +172,67 @@ moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const vo
                                    void* out, moe_dtype dt, void* workspace, size_t workspace_bytes,
                                    moe_routing_out* routing, hipStream_t stream);
 
+/* ---- MoE block: RMSNorm in front of the layer, residual after it --------
+ * glm4_moe_lite.go, MoEBlock.Forward (the half after attention): the MoE
+ * input is PostAttentionLayerNorm(h), an RMSNorm with Config.RMSNormEps, and
+ * the block returns h + MoE(...).  With a moe_block the layer computes
+ *
+ *   xn  = x / sqrt(mean(x^2) + eps) * norm_w     (norm_w != NULL; per token,
+ *         over the d channels, fp32, rounded once to dt)
+ *   out = x + layer(xn)                          (residual != 0; the sum is
+ *         taken in fp32 with the combine, then rounded once)
+ *
+ * where layer() is the plain entry point's computation (routing included).
+ * norm_w is a device array [d] of type dt (bf16 for the MXFP4 layer); eps
+ * must be finite and >= 0.  A NULL block is the plain layer. */
+typedef struct {
+  const void* norm_w; /* [d] RMSNorm scale; NULL = no norm */
+  float eps;          /* RMSNorm epsilon (used when norm_w != NULL) */
+  int residual;       /* nonzero: add x to the layer output */
+} moe_block;
+
+/* Workspace bytes of a block call (the normalised rows need T * d elements
+ * more when block->norm_w != NULL).  Same conventions as
+ * moe_ffn_workspace_bytes, which it equals for a NULL block. */
+size_t moe_block_workspace_bytes(const moe_block* block, int T, int d, int d_ff, int E, int k,
+                                 moe_dtype dt, int d_ff_shared);
+
+/* The three layers as blocks: arguments as moe_ffn_forward,
+ * moe_ffn_forward_mxfp4 and moe_ffn_forward_grouped, plus `block`.
+ * Errors as there; in addition MOE_ERR_INVALID_ARG for a negative or
+ * non-finite eps, and MOE_ERR_WORKSPACE when the workspace is smaller than
+ * moe_block_workspace_bytes(). */
+moe_status moe_block_forward(const moe_block* block, const void* x, const void* router_w, const void* router_b,
+                             const void* w_gate, const void* b_gate,
+                             const void* w_up, const void* b_up,
+                             const void* w_down, const void* b_down,
+                             int T, int d, int d_ff, int E, int k, float alpha, float limit,
+                             void* out, moe_dtype dt, void* workspace, size_t workspace_bytes,
+                             moe_routing_out* routing, hipStream_t stream);
+
+moe_status moe_block_forward_mxfp4(const moe_block* block, const void* x, const void* router_w,
+                                   const void* router_b,
+                                   const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                   const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                   const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                   int T, int d, int d_ff, int E, int k, float alpha, float limit,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   moe_routing_out* routing, hipStream_t stream);
+
+moe_status moe_block_forward_grouped(const moe_block* block, const void* x, const void* router_w,
+                                     const void* router_b, const float* e_score_bias,
+                                     const void* w_gate, const void* b_gate,
+                                     const void* w_up, const void* b_up,
+                                     const void* w_down, const void* b_down,
+                                     const void* shared_w_gate, const void* shared_w_up,
+                                     const void* shared_w_down, int d_ff_shared,
+                                     int T, int d, int d_ff, int E, int k,
+                                     int n_group, int topk_group, int norm_topk_prob,
+                                     float routed_scaling_factor, moe_score score,
+                                     moe_act act, float alpha, float limit,
+                                     void* out, moe_dtype dt, void* workspace, size_t workspace_bytes,
+                                     moe_routing_out* routing, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 
@@ -182,7 +243,7 @@ const char* moe_last_error_detail(void);
 /* ---- Opt-in stage timing -------------------------------------------------
  * Stages of one call, in launch order. */
 typedef enum {
-  MOE_STAGE_ROUTE = 0,    /* router logits + top-k + weights */
+  MOE_STAGE_ROUTE = 0,    /* (block RMSNorm +) router logits + top-k + weights */
   MOE_STAGE_PERMUTE = 1,  /* per-expert counts, prefix sums, stable scatter */
   MOE_STAGE_GATE_UP = 2,  /* grouped gate|up GEMM + bias + activation */
   MOE_STAGE_DOWN = 3,     /* grouped down GEMM + bias */

@@ -4,7 +4,9 @@
 //
 // summed in fp32 in increasing j, the shared expert added last, then rounded
 // once to the output type (glm4_moe_lite.go, MoE.Forward: weighted sum over
-// the k expert outputs, then the shared experts added).  Deterministic: no
+// the k expert outputs, then the shared experts added).  In a MoE block the
+// block input x[t] is added after that, before the rounding (MoEBlock.Forward:
+// the block returns its input plus the MoE output).  Deterministic: no
 // atomics; each output element is produced by one thread.
 #include "device_common.h"
 #include "moe_internal.h"
@@ -19,6 +21,7 @@ struct CombineArgs {
   const float* w;
   const int32_t* pos;
   int T, d, k, shared;
+  const void* resid;  // [T, d] rows added last, or nullptr
   void* out;
 };
 
@@ -54,6 +57,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       for (int q = 0; q < VEC; ++q) acc[q] += load_f32(Y, base + q);
     }
     const size_t ob = (size_t)t * a.d + (size_t)v * VEC;
+    if (a.resid) {
+      const TE* R = static_cast<const TE*>(a.resid);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) acc[q] += load_f32(R, ob + q);
+    }
 #pragma unroll
     for (int q = 0; q < VEC; ++q) store_f32(O, ob + q, acc[q]);
   }
@@ -65,6 +73,7 @@ hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s) {
   CombineArgs a;
   a.y = W.y; a.w = W.w; a.pos = W.pos;
   a.T = L.T; a.d = L.d; a.k = L.k; a.shared = L.has_shared() ? 1 : 0;
+  a.resid = L.x_resid;
   a.out = L.out;
   if (L.dt == MOE_F32) combine_kernel<float, 4><<<L.T, kThreads, 0, s>>>(a);
   else combine_kernel<uint16_t, 8><<<L.T, kThreads, 0, s>>>(a);

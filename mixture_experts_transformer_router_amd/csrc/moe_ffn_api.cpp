@@ -102,6 +102,8 @@ moe_status check_common(const Layer& L) {
     if (!L.sh_wu || !L.sh_wd) return fail(MOE_ERR_INVALID_ARG, "shared_w_up and shared_w_down are required with shared_w_gate");
     if (L.F_sh < 1 || L.F_sh % 8) return fail(MOE_ERR_INVALID_ARG, "d_ff_shared = %d must be >= 1 and a multiple of 8", L.F_sh);
   }
+  if (L.norm_w && (!(L.eps >= 0.f) || !std::isfinite(L.eps)))
+    return fail(MOE_ERR_INVALID_ARG, "RMSNorm eps = %g must be finite and >= 0", (double)L.eps);
   if (L.T == 0) return MOE_OK;
   if (!L.x || !L.router_w || !L.out) return fail(MOE_ERR_INVALID_ARG, "x, router_w and out are required");
   if (L.wfmt == WF_MXFP4) {
@@ -130,7 +132,13 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   hipError_t e;
   {
     StageTimer tm(s, MOE_STAGE_ROUTE);
-    e = launch_route(L, W, s);
+    e = hipSuccess;
+    if (L.norm_w) {
+      // block prologue: the layer works on RMSNorm(x) from here on
+      e = launch_rmsnorm(L, W, s);
+      L.x = W.xn;
+    }
+    if (e == hipSuccess) e = launch_route(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "route launch: %s", hipGetErrorString(e));
   {
@@ -196,6 +204,7 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   W->pos = static_cast<int32_t*>(take(P * 4));
   W->h = take(rows * (size_t)L.F_max() * L.elt());
   W->y = take(rows * (size_t)L.d * L.elt());
+  W->xn = take(L.norm_w ? (size_t)L.T * L.d * L.elt() : 0);
   return off;
 }
 
@@ -203,9 +212,23 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
 
 using moe::Layer;
 
+namespace {
+void apply_block(Layer& L, const moe_block* b) {
+  if (!b) return;
+  L.norm_w = b->norm_w;
+  L.eps = b->eps;
+  L.x_resid = b->residual ? L.x : nullptr;
+}
+}  // namespace
+
 extern "C" {
 
 size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int d_ff_shared) {
+  return moe_block_workspace_bytes(nullptr, T, d, d_ff, E, k, dt, d_ff_shared);
+}
+
+size_t moe_block_workspace_bytes(const moe_block* block, int T, int d, int d_ff, int E, int k, moe_dtype dt,
+                                 int d_ff_shared) {
   if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E || d_ff_shared < 0) return (size_t)-1;
   if ((long long)T * k >= (1ll << 26)) return (size_t)-1;
   if (T == 0) return 0;
@@ -214,6 +237,7 @@ size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype d
   L.F_sh = d_ff_shared;
   static const char dummy = 0;
   if (d_ff_shared > 0) L.sh_wg = &dummy;
+  if (block && block->norm_w) L.norm_w = &dummy;
   moe::Work W;
   return moe::carve_workspace(L, nullptr, &W);
 }
@@ -223,6 +247,15 @@ moe_status moe_ffn_forward(const void* x, const void* router_w, const void* rout
                            const void* w_down, const void* b_down, int T, int d, int d_ff, int E, int k,
                            float alpha, float limit, void* out, moe_dtype dt, void* workspace,
                            size_t workspace_bytes, moe_routing_out* routing, hipStream_t stream) {
+  return moe_block_forward(nullptr, x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, T, d,
+                           d_ff, E, k, alpha, limit, out, dt, workspace, workspace_bytes, routing, stream);
+}
+
+moe_status moe_block_forward(const moe_block* block, const void* x, const void* router_w, const void* router_b,
+                             const void* w_gate, const void* b_gate, const void* w_up, const void* b_up,
+                             const void* w_down, const void* b_down, int T, int d, int d_ff, int E, int k,
+                             float alpha, float limit, void* out, moe_dtype dt, void* workspace,
+                             size_t workspace_bytes, moe_routing_out* routing, hipStream_t stream) {
   Layer L;
   L.x = x; L.router_w = router_w; L.router_b = router_b;
   L.wg = w_gate; L.bg = b_gate; L.wu = w_up; L.bu = b_up; L.wd = w_down; L.bd = b_down;
@@ -231,6 +264,7 @@ moe_status moe_ffn_forward(const void* x, const void* router_w, const void* rout
   L.dt = dt; L.wfmt = dt == MOE_F32 ? moe::WF_F32 : moe::WF_BF16;
   L.out = out;
   if (routing) L.routing = *routing;
+  apply_block(L, block);
   return moe::run(L, workspace, workspace_bytes, stream);
 }
 
@@ -241,6 +275,18 @@ moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void
                                  int T, int d, int d_ff, int E, int k, float alpha, float limit, void* out,
                                  void* workspace, size_t workspace_bytes, moe_routing_out* routing,
                                  hipStream_t stream) {
+  return moe_block_forward_mxfp4(nullptr, x, router_w, router_b, w_gate_codes, w_gate_scales, b_gate, w_up_codes,
+                                 w_up_scales, b_up, w_down_codes, w_down_scales, b_down, T, d, d_ff, E, k, alpha,
+                                 limit, out, workspace, workspace_bytes, routing, stream);
+}
+
+moe_status moe_block_forward_mxfp4(const moe_block* block, const void* x, const void* router_w,
+                                   const void* router_b, const uint8_t* w_gate_codes, const uint8_t* w_gate_scales,
+                                   const void* b_gate, const uint8_t* w_up_codes, const uint8_t* w_up_scales,
+                                   const void* b_up, const uint8_t* w_down_codes, const uint8_t* w_down_scales,
+                                   const void* b_down, int T, int d, int d_ff, int E, int k, float alpha,
+                                   float limit, void* out, void* workspace, size_t workspace_bytes,
+                                   moe_routing_out* routing, hipStream_t stream) {
   Layer L;
   L.x = x; L.router_w = router_w; L.router_b = router_b;
   L.wg_codes = w_gate_codes; L.wg_scales = w_gate_scales; L.bg = b_gate;
@@ -251,6 +297,7 @@ moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void
   L.dt = MOE_BF16; L.wfmt = moe::WF_MXFP4;
   L.out = out;
   if (routing) L.routing = *routing;
+  apply_block(L, block);
   return moe::run(L, workspace, workspace_bytes, stream);
 }
 
@@ -263,6 +310,21 @@ moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const vo
                                    moe_score score, moe_act act, float alpha, float limit, void* out,
                                    moe_dtype dt, void* workspace, size_t workspace_bytes,
                                    moe_routing_out* routing, hipStream_t stream) {
+  return moe_block_forward_grouped(nullptr, x, router_w, router_b, e_score_bias, w_gate, b_gate, w_up, b_up,
+                                   w_down, b_down, shared_w_gate, shared_w_up, shared_w_down, d_ff_shared, T, d,
+                                   d_ff, E, k, n_group, topk_group, norm_topk_prob, routed_scaling_factor, score,
+                                   act, alpha, limit, out, dt, workspace, workspace_bytes, routing, stream);
+}
+
+moe_status moe_block_forward_grouped(const moe_block* block, const void* x, const void* router_w,
+                                     const void* router_b, const float* e_score_bias, const void* w_gate,
+                                     const void* b_gate, const void* w_up, const void* b_up, const void* w_down,
+                                     const void* b_down, const void* shared_w_gate, const void* shared_w_up,
+                                     const void* shared_w_down, int d_ff_shared, int T, int d, int d_ff, int E,
+                                     int k, int n_group, int topk_group, int norm_topk_prob,
+                                     float routed_scaling_factor, moe_score score, moe_act act, float alpha,
+                                     float limit, void* out, moe_dtype dt, void* workspace,
+                                     size_t workspace_bytes, moe_routing_out* routing, hipStream_t stream) {
   Layer L;
   L.x = x; L.router_w = router_w; L.router_b = router_b; L.e_bias = e_score_bias;
   L.wg = w_gate; L.bg = b_gate; L.wu = w_up; L.bu = b_up; L.wd = w_down; L.bd = b_down;
@@ -275,6 +337,7 @@ moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const vo
   L.dt = dt; L.wfmt = dt == MOE_F32 ? moe::WF_F32 : moe::WF_BF16;
   L.out = out;
   if (routing) L.routing = *routing;
+  apply_block(L, block);
   return moe::run(L, workspace, workspace_bytes, stream);
 }
 

@@ -64,6 +64,12 @@ struct Layer {
   int wfmt = WF_BF16;
   void* out = nullptr;
   moe_routing_out routing{nullptr, nullptr, nullptr, nullptr};
+  // MoE block: RMSNorm scale (nullptr: none) and epsilon; x_resid: the rows
+  // added to the output (nullptr: no residual).  After the norm, x points at
+  // the normalised rows and x_resid still at the caller's x.
+  const void* norm_w = nullptr;
+  float eps = 0.f;
+  const void* x_resid = nullptr;
 
   bool has_shared() const { return sh_wg != nullptr; }
   int n_experts_all() const { return E + (has_shared() ? 1 : 0); }
@@ -88,6 +94,7 @@ struct Work {
   int32_t* pos = nullptr;          // [T*k] sorted row of each pair
   void* h = nullptr;               // [rows_all, F_max] hidden activation (dt)
   void* y = nullptr;               // [rows_all, d] expert outputs (dt)
+  void* xn = nullptr;              // block with a norm: [T, d] normalised rows (dt)
 };
 
 // Byte size of the workspace and the layout of its buffers (ws == nullptr:
@@ -108,5 +115,6 @@ hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_gate_up_mxfp4(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_mxfp4(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_rmsnorm(const Layer& L, const Work& W, hipStream_t s);
 
 }  // namespace moe

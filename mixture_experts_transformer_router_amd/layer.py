@@ -22,15 +22,22 @@ def to_device(arrays: dict, device="cuda") -> dict:
     return out
 
 
+def block_of(w: Workload, t: dict):
+    """The moe_block of a block workload (None for a plain layer)."""
+    return moe_ffn.make_block(t["norm_w"], w.norm_eps, True) if w.block else None
+
+
 def workspace_for(w: Workload, device="cuda") -> torch.Tensor:
     dt = moe_ffn.MOE_F32 if w.dtype == "f32" else moe_ffn.MOE_BF16
-    n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared)
+    blk = moe_ffn.MoeBlock(1, w.norm_eps, 1) if w.block else None  # sizes only
+    n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared, block=blk)
     return moe_ffn.alloc_workspace(n, device)
 
 
 def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=None,
         e_score_bias=None):
-    """One layer forward of workload `w` on device tensors `t`."""
+    """One layer (or block) forward of workload `w` on device tensors `t`."""
+    block = block_of(w, t)
     if w.routing == "grouped":
         return moe_ffn.forward_grouped(
             t["x"], t["router_w"], t.get("router_b"), t.get("w_gate"), t.get("b_gate"), t.get("w_up"),
@@ -41,14 +48,14 @@ def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=No
             alpha=w.alpha, limit=w.limit, e_score_bias=e_score_bias,
             shared_w_gate=t.get("shared_w_gate"), shared_w_up=t.get("shared_w_up"),
             shared_w_down=t.get("shared_w_down"), out=out, workspace=workspace, routing=routing,
-            stream=stream)
+            stream=stream, block=block)
     if w.weights == "mxfp4":
         return moe_ffn.forward_mxfp4(
             t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),
             t["w_up_codes"], t["w_up_scales"], t.get("b_up"), t["w_down_codes"], t["w_down_scales"],
             t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
-            routing=routing, stream=stream)
+            routing=routing, stream=stream, block=block)
     return moe_ffn.forward(
         t["x"], t["router_w"], t.get("router_b"), t["w_gate"], t.get("b_gate"), t["w_up"], t.get("b_up"),
         t["w_down"], t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
-        routing=routing, stream=stream)
+        routing=routing, stream=stream, block=block)

@@ -9,6 +9,8 @@ stream.  The entry points keep the C names:
     forward_mxfp4(...)    -> moe_ffn_forward_mxfp4   (MXFP4 expert weights)
     forward_grouped(...)  -> moe_ffn_forward_grouped (GLM group-limited routing, shared expert)
     workspace_bytes(...)  -> moe_ffn_workspace_bytes
+    each with block=MoeBlock(...) -> the moe_block_* entry point of the same
+    layer (RMSNorm in front, residual after) and moe_block_workspace_bytes
 
 If the shared library has not been built, loading raises MoeLibraryMissing;
 there is no other implementation to fall back to.
@@ -32,7 +34,8 @@ STAGES = ("route", "permute", "gate_up", "down", "combine")
 
 EXPORTED = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp4",
             "moe_ffn_forward_grouped", "moe_status_string", "moe_last_error_detail",
-            "moe_ffn_profile_enable", "moe_ffn_profile_read")
+            "moe_ffn_profile_enable", "moe_ffn_profile_read", "moe_block_workspace_bytes",
+            "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -43,6 +46,16 @@ class MoeError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(msg)
         self.status = status
+
+
+class MoeBlock(ctypes.Structure):
+    """moe_block: RMSNorm scale (device pointer or None), epsilon, residual flag."""
+    _fields_ = [("norm_w", ctypes.c_void_p), ("eps", ctypes.c_float), ("residual", ctypes.c_int)]
+
+
+def make_block(norm_w: Optional[torch.Tensor], eps: float = 1e-5, residual: bool = True) -> MoeBlock:
+    """A moe_block for `norm_w` (a device tensor [d], kept alive by the caller)."""
+    return MoeBlock(None if norm_w is None else norm_w.data_ptr(), eps, int(bool(residual)))
 
 
 class RoutingOut(ctypes.Structure):
@@ -81,6 +94,12 @@ def load() -> ctypes.CDLL:
     L.moe_ffn_forward_grouped.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                           _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F,
                                           _P, _I, _P, _Z, _P, _P]
+    for name in ("moe_ffn_forward", "moe_ffn_forward_mxfp4", "moe_ffn_forward_grouped"):
+        blk = getattr(L, name.replace("moe_ffn_", "moe_block_"))
+        blk.restype = _I
+        blk.argtypes = [_P] + getattr(L, name).argtypes
+    L.moe_block_workspace_bytes.restype = _Z
+    L.moe_block_workspace_bytes.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [_I]
     L.moe_last_error_detail.restype = ctypes.c_char_p
@@ -121,8 +140,11 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
-def workspace_bytes(T, d, d_ff, E, k, dtype=MOE_BF16, d_ff_shared=0) -> int:
-    n = load().moe_ffn_workspace_bytes(T, d, d_ff, E, k, dtype, d_ff_shared)
+def workspace_bytes(T, d, d_ff, E, k, dtype=MOE_BF16, d_ff_shared=0, block: Optional[MoeBlock] = None) -> int:
+    if block is None:
+        n = load().moe_ffn_workspace_bytes(T, d, d_ff, E, k, dtype, d_ff_shared)
+    else:
+        n = load().moe_block_workspace_bytes(ctypes.byref(block), T, d, d_ff, E, k, dtype, d_ff_shared)
     if n == ctypes.c_size_t(-1).value:
         raise MoeError(MOE_ERR_UNSUPPORTED, "sizes outside the library's limits")
     return n
@@ -144,17 +166,27 @@ def _routing(T, k, E, device, want):
     return r, s
 
 
+def _entry(name: str, block: Optional[MoeBlock]):
+    """The plain entry point, or its moe_block_* twin with the block prepended."""
+    L = load()
+    if block is None:
+        return getattr(L, name)
+    f = getattr(L, name.replace("moe_ffn_", "moe_block_"))
+    return lambda *args: f(ctypes.byref(block), *args)
+
+
 def forward(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, k,
-            alpha=1.702, limit=7.0, out=None, workspace=None, routing=False, stream=None):
-    """moe_ffn_forward.  Shapes: x [T,d], router_w [E,d], w_gate/w_up [E,d_ff,d],
-    w_down [E,d,d_ff], biases [E], [E,d_ff], [E,d] or None."""
+            alpha=1.702, limit=7.0, out=None, workspace=None, routing=False, stream=None, block=None):
+    """moe_ffn_forward (moe_block_forward with `block`).  Shapes: x [T,d], router_w [E,d],
+    w_gate/w_up [E,d_ff,d], w_down [E,d,d_ff], biases [E], [E,d_ff], [E,d] or None."""
     T, d = x.shape
     E, d_ff = w_gate.shape[0], w_gate.shape[1]
     dt = _dt(x)
     out = torch.empty_like(x) if out is None else out
-    ws = workspace if workspace is not None else alloc_workspace(workspace_bytes(T, d, d_ff, E, k, dt), x.device)
+    ws = workspace if workspace is not None else alloc_workspace(
+        workspace_bytes(T, d, d_ff, E, k, dt, block=block), x.device)
     r, rs = _routing(T, k, E, x.device, routing)
-    st = load().moe_ffn_forward(
+    st = _entry("moe_ffn_forward", block)(
         _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w_gate), _ptr(b_gate), _ptr(w_up), _ptr(b_up),
         _ptr(w_down), _ptr(b_down), T, d, d_ff, E, k, alpha, limit, _ptr(out), dt,
         _ptr(ws), ws.numel(), ctypes.byref(rs) if rs is not None else None, _stream(stream))
@@ -164,14 +196,16 @@ def forward(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, k
 
 def forward_mxfp4(x, router_w, router_b, w_gate_codes, w_gate_scales, b_gate, w_up_codes, w_up_scales,
                   b_up, w_down_codes, w_down_scales, b_down, k, alpha=1.702, limit=7.0, out=None,
-                  workspace=None, routing=False, stream=None):
-    """moe_ffn_forward_mxfp4.  codes uint8 [E,rows,cols/2], scales uint8 [E,rows,cols/32]."""
+                  workspace=None, routing=False, stream=None, block=None):
+    """moe_ffn_forward_mxfp4 (moe_block_forward_mxfp4 with `block`).  codes uint8
+    [E,rows,cols/2], scales uint8 [E,rows,cols/32]."""
     T, d = x.shape
     E, d_ff = w_gate_codes.shape[0], w_gate_codes.shape[1]
     out = torch.empty_like(x) if out is None else out
-    ws = workspace if workspace is not None else alloc_workspace(workspace_bytes(T, d, d_ff, E, k, MOE_BF16), x.device)
+    ws = workspace if workspace is not None else alloc_workspace(
+        workspace_bytes(T, d, d_ff, E, k, MOE_BF16, block=block), x.device)
     r, rs = _routing(T, k, E, x.device, routing)
-    st = load().moe_ffn_forward_mxfp4(
+    st = _entry("moe_ffn_forward_mxfp4", block)(
         _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w_gate_codes), _ptr(w_gate_scales), _ptr(b_gate),
         _ptr(w_up_codes), _ptr(w_up_scales), _ptr(b_up), _ptr(w_down_codes), _ptr(w_down_scales), _ptr(b_down),
         T, d, d_ff, E, k, alpha, limit, _ptr(out), _ptr(ws), ws.numel(),
@@ -184,16 +218,18 @@ def forward_grouped(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b
                     n_group, topk_group, norm_topk_prob, routed_scaling_factor,
                     score=MOE_SCORE_SOFTMAX, act=MOE_ACT_SILU, alpha=1.702, limit=7.0,
                     e_score_bias=None, shared_w_gate=None, shared_w_up=None, shared_w_down=None,
-                    out=None, workspace=None, routing=False, stream=None):
-    """moe_ffn_forward_grouped.  Shared expert weights [d_ff_shared, d] x2 and [d, d_ff_shared]."""
+                    out=None, workspace=None, routing=False, stream=None, block=None):
+    """moe_ffn_forward_grouped (moe_block_forward_grouped with `block`).  Shared expert
+    weights [d_ff_shared, d] x2 and [d, d_ff_shared]."""
     T, d = x.shape
     E, d_ff = w_gate.shape[0], w_gate.shape[1]
     dt = _dt(x)
     Fs = shared_w_gate.shape[0] if shared_w_gate is not None else 0
     out = torch.empty_like(x) if out is None else out
-    ws = workspace if workspace is not None else alloc_workspace(workspace_bytes(T, d, d_ff, E, k, dt, Fs), x.device)
+    ws = workspace if workspace is not None else alloc_workspace(
+        workspace_bytes(T, d, d_ff, E, k, dt, Fs, block=block), x.device)
     r, rs = _routing(T, k, E, x.device, routing)
-    st = load().moe_ffn_forward_grouped(
+    st = _entry("moe_ffn_forward_grouped", block)(
         _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(e_score_bias), _ptr(w_gate), _ptr(b_gate),
         _ptr(w_up), _ptr(b_up), _ptr(w_down), _ptr(b_down), _ptr(shared_w_gate), _ptr(shared_w_up),
         _ptr(shared_w_down), Fs, T, d, d_ff, E, k, n_group, topk_group, int(bool(norm_topk_prob)),
@@ -215,14 +251,17 @@ def profile_read():
     return {STAGES[i]: (ms[i], n[i]) for i in range(5)}
 
 
-def bind(fn_name: str, *args):
+def bind(fn_name: str, *args, block: Optional[MoeBlock] = None):
     """Pre-marshal one call: returns a no-argument callable that invokes the
-    named C entry point with the given (already converted) arguments and
-    raises on a non-zero status.  Used where Python overhead must stay out of
-    a timed loop; the arguments must stay alive as long as the callable."""
+    named C entry point (its moe_block_* twin with `block`) with the given
+    (already converted) arguments and raises on a non-zero status.  Used where
+    Python overhead must stay out of a timed loop; the arguments must stay
+    alive as long as the callable."""
     L = load()
-    f = getattr(L, fn_name)
+    f = getattr(L, fn_name if block is None else fn_name.replace("moe_ffn_", "moe_block_"))
     conv = [a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args]
+    if block is not None:
+        conv = [ctypes.byref(block)] + conv
 
     def call():
         st = f(*conv)
@@ -233,10 +272,12 @@ def bind(fn_name: str, *args):
 
 def bound_layer_call(w, t: dict, out: torch.Tensor, workspace: torch.Tensor, stream=None,
                      routing: Optional[RoutingOut] = None):
-    """bind() for a workload description `w` and its device tensors `t`."""
+    """bind() for a workload description `w` and its device tensors `t`
+    (a block workload passes t["norm_w"] in a moe_block)."""
     s = _stream(stream)
     rp = ctypes.byref(routing) if routing is not None else None
     g = t.get
+    blk = make_block(t["norm_w"], w.norm_eps, True) if getattr(w, "block", False) else None
     if w.routing == "grouped":
         Fs = g("shared_w_gate").shape[0] if g("shared_w_gate") is not None else 0
         return bind("moe_ffn_forward_grouped", g("x"), g("router_w"), g("router_b"), None, g("w_gate"),
@@ -245,12 +286,14 @@ def bound_layer_call(w, t: dict, out: torch.Tensor, workspace: torch.Tensor, str
                     w.topk_group, int(w.norm_topk_prob), w.routed_scaling_factor,
                     MOE_SCORE_SOFTMAX if w.score == "softmax" else MOE_SCORE_SIGMOID,
                     MOE_ACT_SILU if w.act == "silu" else MOE_ACT_CLIPPED_SWIGLU, w.alpha, w.limit,
-                    out, MOE_F32 if w.dtype == "f32" else MOE_BF16, workspace, workspace.numel(), rp, s)
+                    out, MOE_F32 if w.dtype == "f32" else MOE_BF16, workspace, workspace.numel(), rp, s,
+                    block=blk)
     if w.weights == "mxfp4":
         return bind("moe_ffn_forward_mxfp4", g("x"), g("router_w"), g("router_b"), g("w_gate_codes"),
                     g("w_gate_scales"), g("b_gate"), g("w_up_codes"), g("w_up_scales"), g("b_up"),
                     g("w_down_codes"), g("w_down_scales"), g("b_down"), w.T, w.d, w.d_ff, w.E, w.k,
-                    w.alpha, w.limit, out, workspace, workspace.numel(), rp, s)
+                    w.alpha, w.limit, out, workspace, workspace.numel(), rp, s, block=blk)
     return bind("moe_ffn_forward", g("x"), g("router_w"), g("router_b"), g("w_gate"), g("b_gate"),
                 g("w_up"), g("b_up"), g("w_down"), g("b_down"), w.T, w.d, w.d_ff, w.E, w.k, w.alpha,
-                w.limit, out, MOE_F32 if w.dtype == "f32" else MOE_BF16, workspace, workspace.numel(), rp, s)
+                w.limit, out, MOE_F32 if w.dtype == "f32" else MOE_BF16, workspace, workspace.numel(), rp, s,
+                block=blk)

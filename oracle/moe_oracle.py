@@ -46,7 +46,9 @@ reason in the design notes of this repository):
   * MoE block ([GLM] MoEBlock.Forward, the half after attention): the layer
     sees RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma (nn.RMSNorm with
     Config.RMSNormEps; the pages do not print its formula, this is the plain
-    definition) and its output is added to x.
+    definition) and its output is added to x.  The norm's output is an array
+    of the layer's element type (MLX arrays keep their dtype), so the layer
+    sees it rounded to nearest-even bf16 (fp32).
 """
 from __future__ import annotations
 
@@ -285,15 +287,31 @@ def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(ms + eps) * gamma
 
 
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (8 significant bits), ties to even,
+    rounded once from float64 (no float32 step).  For finite values in the
+    normal range of bf16 (all this oracle rounds)."""
+    m, e = np.frexp(np.asarray(v, dtype=np.float64))   # v = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0), e - 8)        # numpy rounds halves to even
+
+
+def round_to(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Nearest value of the element type (ties to even), as float64."""
+    if dtype == "bf16":
+        return round_bf16(v)
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
 def layer_input(arrays: dict, cfg: dict, tokens: Optional[np.ndarray] = None) -> np.ndarray:
-    """The rows the MoE layer works on, float64: x, or RMSNorm(x) with the
-    block's gamma (arrays["norm_w"]) when cfg["block"] is set."""
+    """The rows the MoE layer works on, float64: x, or for a block
+    (cfg["block"]) RMSNorm(x) with the block's gamma (arrays["norm_w"]),
+    rounded to the layer's element type."""
     dt = cfg["dtype"]
     x = to_f64(arrays["x"], dt)
     if tokens is not None:
         x = x[tokens]
     if cfg.get("block"):
-        x = rms_norm(x, to_f64(arrays["norm_w"], dt), float(cfg["norm_eps"]))
+        x = round_to(rms_norm(x, to_f64(arrays["norm_w"], dt), float(cfg["norm_eps"])), dt)
     return x
 
 

@@ -146,3 +146,29 @@ def test_mxfp4_argument_checks(lib):
     # one expert's codes must stay under 2^32 bytes (32-bit offsets in the kernels)
     assert call(d=65536, F=131072) == M.MOE_ERR_UNSUPPORTED
     assert b"2^33" in lib.moe_last_error_detail()
+
+def test_block_workspace_and_argument_checks(lib):
+    n = lib.moe_ffn_workspace_bytes
+    nb = lib.moe_block_workspace_bytes
+    with_norm = M.MoeBlock(FAKE, 1e-5, 1)
+    residual_only = M.MoeBlock(None, 0.0, 1)
+    assert nb(None, 64, 256, 128, 8, 2, M.MOE_BF16, 0) == n(64, 256, 128, 8, 2, M.MOE_BF16, 0)
+    assert nb(ctypes.byref(residual_only), 64, 256, 128, 8, 2, M.MOE_BF16, 0) == n(64, 256, 128, 8, 2, M.MOE_BF16, 0)
+    # the normalised rows: T * d elements more
+    assert nb(ctypes.byref(with_norm), 64, 256, 128, 8, 2, M.MOE_BF16, 0) >= n(64, 256, 128, 8, 2, M.MOE_BF16, 0) + 64 * 256 * 2
+
+    def call(block, wsb=None):
+        need = nb(ctypes.byref(block), 16, 64, 64, 8, 2, M.MOE_BF16, 0)
+        return lib.moe_block_forward(ctypes.byref(block), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                                     16, 64, 64, 8, 2, 1.702, 7.0, FAKE2, M.MOE_BF16, FAKE + (1 << 36),
+                                     need if wsb is None else wsb, None, None)
+    assert call(M.MoeBlock(FAKE, -1e-5, 1)) == M.MOE_ERR_INVALID_ARG
+    assert b"eps" in lib.moe_last_error_detail()
+    assert call(M.MoeBlock(FAKE, float("nan"), 0)) == M.MOE_ERR_INVALID_ARG
+    assert call(M.MoeBlock(FAKE, float("inf"), 0)) == M.MOE_ERR_INVALID_ARG
+    # a workspace sized for the plain layer is too small once the norm needs its rows
+    plain = n(16, 64, 64, 8, 2, M.MOE_BF16, 0)
+    assert call(M.MoeBlock(FAKE, 1e-5, 1), wsb=plain) == M.MOE_ERR_WORKSPACE
+    # T = 0 is a no-op for blocks too
+    assert lib.moe_block_forward(ctypes.byref(with_norm), None, None, None, None, None, None, None, None, None,
+                                 0, 64, 64, 8, 2, 1.702, 7.0, None, M.MOE_BF16, 0, 0, None, None) == M.MOE_OK

@@ -2,6 +2,7 @@
 
 Each case prints its name, shape and seed before touching the GPU.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -186,3 +187,54 @@ def test_zero_tokens_is_noop_and_errors_leave_out_untouched():
     empty = moe_ffn.forward(t["x"][:0], t["router_w"], t["router_b"], t["w_gate"], t["b_gate"], t["w_up"],
                             t["b_up"], t["w_down"], t["b_down"], k=2)
     assert empty.shape == (0, w.d)
+
+# --- MoE blocks: RMSNorm in front of the layer, residual after it -------------------
+
+BLOCK_SMALL = [
+    # every expert path: weight streaming (T <= 16), bf16 MFMA with ragged K,
+    # MXFP4, fp32, grouped routing with a shared expert
+    W.GPTOSS_DECODE.scaled(T=7, d=520, d_ff=72, E=8, k=3, block=True, name="block_decode_T7"),
+    W.GPTOSS_PREFILL.scaled(T=300, d=1000, d_ff=712, E=8, k=2, block=True, name="block_prefill_ragged_k"),
+    W.GPTOSS_MXFP4.scaled(T=150, d=256, d_ff=160, E=8, k=2, block=True, name="block_mxfp4_small"),
+    W.TINY_F32.scaled(T=40, d=96, d_ff=80, E=16, k=3, block=True, name="block_f32"),
+    W.GLM4_MOE_LITE.scaled(T=300, d=256, d_ff=192, E=64, k=6, d_ff_shared=128, block=True,
+                           name="block_glm_small"),
+    # rows longer than the norm kernel keeps in registers (two passes over x)
+    W.GPTOSS_DECODE.scaled(T=4, d=16400, d_ff=16, E=4, k=2, block=True, name="block_bf16_d16400"),
+    W.TINY_F32.scaled(T=6, d=8200, d_ff=16, E=4, k=2, block=True, name="block_f32_d8200"),
+]
+BLOCK_CASES = list(W.BLOCKS) + BLOCK_SMALL
+
+
+@pytest.mark.parametrize("w", BLOCK_CASES, ids=[w.name for w in BLOCK_CASES])
+def test_block(w):
+    _run_and_check(w, n_out_tokens=256 if w.T > 256 else w.T)
+
+
+def test_block_residual_only_and_norm_only():
+    # residual without a norm = the plain layer plus x; a norm without the
+    # residual = the full block minus x (each up to the roundings of the two
+    # ways of computing it)
+    w = W.GLM4_MOE_LITE.scaled(T=200, d=256, d_ff=192, E=16, k=4, n_group=4, topk_group=2, d_ff_shared=64,
+                               block=True, name="block_parts")
+    _say(f"[case] {w.name}")
+    a = I.make_inputs(w)
+    t = LY.to_device(a, DEV)
+    plain = LY.run(dataclasses.replace(w, block=False), t)
+    full = LY.run(w, t)
+    x = t["x"].float()
+
+    def grouped(block):
+        return moe_ffn.forward_grouped(
+            t["x"], t["router_w"], None, t["w_gate"], None, t["w_up"], None, t["w_down"], None, w.k, w.n_group,
+            w.topk_group, w.norm_topk_prob, w.routed_scaling_factor, act=moe_ffn.MOE_ACT_SILU,
+            shared_w_gate=t["shared_w_gate"], shared_w_up=t["shared_w_up"], shared_w_down=t["shared_w_down"],
+            block=block)
+    res_only = grouped(moe_ffn.make_block(None, 0.0, True))
+    norm_only = grouped(moe_ffn.make_block(t["norm_w"], w.norm_eps, False))
+    torch.cuda.synchronize()
+    scale = float((x + plain.float()).abs().max())
+    assert float((res_only.float() - (x + plain.float())).abs().max()) <= 2 ** -7 * scale
+    scale = float(full.float().abs().max())
+    assert float((norm_only.float() - (full.float() - x)).abs().max()) <= 2 ** -7 * scale
+    assert float((norm_only.float() - plain.float()).abs().max()) > 1e-2  # the norm changes the layer

@@ -383,3 +383,16 @@ def test_block_norm_feeds_the_layer():
     np.testing.assert_allclose(m2, m1, rtol=1e-12, atol=1e-12)
     plain = _cfg(w, block=False)
     assert np.abs(O.moe_layer(a2, plain)["out"] - O.moe_layer(a, plain)["out"]).max() > 1e-3
+
+
+def test_round_bf16_matches_torch_and_breaks_ties_to_even():
+    # values exact in fp32: torch's fp32 -> bf16 conversion is a single rounding
+    rng = np.random.default_rng(9)
+    v = rng.normal(0, 3, 20000).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(v.astype(np.float64)), want)
+    h = 2.0 ** -8   # half a bf16 ulp at 1
+    cases = [(1 + h, 1.0), (1 + 3 * h, 1 + 4 * h), (-(1 + h), -1.0), (1 + h + 2.0 ** -30, 1 + 2 * h),
+             (1 - 2.0 ** -30, 1.0), (0.0, 0.0), (3.0, 3.0)]
+    for x, y in cases:   # the fourth is above the tie: one rounding from fp64 goes up
+        assert O.round_bf16(np.array([x]))[0] == y, (x, y)
