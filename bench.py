@@ -2,7 +2,7 @@
 """Benchmark of the MoE-FFN layer on one MI355X; prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm]
+                    [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm"])
+                    choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm",
+                             "dense_block"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -54,7 +55,7 @@ def workload(name):
     from mixture_experts_transformer_router_amd import workloads as W
     return {"decode": W.GPTOSS_DECODE, "prefill": W.GPTOSS_PREFILL, "mxfp4": W.GPTOSS_MXFP4,
             "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
-            "block_glm": W.GLM4_MOE_LITE_BLOCK}[name]
+            "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -136,7 +137,7 @@ def main():
 
     w = workload(args.workload)
     steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
-                           "block_decode": 500, "block_glm": 100}[args.workload]
+                           "block_decode": 500, "block_glm": 100, "dense_block": 100}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)

@@ -98,6 +98,14 @@ ALL = (TINY_F32, GPTOSS_DECODE, GPTOSS_PREFILL, GPTOSS_MXFP4, GLM4_MOE_LITE)
 GLM4_MOE_LITE_BLOCK = GLM4_MOE_LITE.scaled(name="glm4moelite_block_T2048_d2048_F1536_E64s1_k6_g8tg4",
                                            block=True)
 GPTOSS_DECODE_BLOCK = GPTOSS_DECODE.scaled(name="gptoss20b_block_decode_T8_d2880_E32_k4_bf16", block=True)
-BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK)
+# A dense block of the first_k_dense_replace layers (glm4_moe_lite.go, DenseBlock
+# and DenseMLP: down(silu(gate(x)) * up(x)), no router) is the E = k = 1 case
+# of the grouped layer: one expert, softmax over one logit = weight 1.  The
+# dense intermediate size (8192 here) is not on the pages.
+GLM4_DENSE_BLOCK = Workload(
+    name="glm4_dense_block_T2048_d2048_F8192", T=2048, d=2048, d_ff=8192, E=1, k=1,
+    dtype="bf16", routing="grouped", act="silu", n_group=1, topk_group=1, norm_topk_prob=False,
+    routed_scaling_factor=1.0, score="softmax", router_bias="none", expert_bias=False, block=True)
+BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK, GLM4_DENSE_BLOCK)
 
 BY_NAME = {w.name: w for w in ALL + BLOCKS}

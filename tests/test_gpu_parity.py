@@ -199,6 +199,8 @@ BLOCK_SMALL = [
     W.TINY_F32.scaled(T=40, d=96, d_ff=80, E=16, k=3, block=True, name="block_f32"),
     W.GLM4_MOE_LITE.scaled(T=300, d=256, d_ff=192, E=64, k=6, d_ff_shared=128, block=True,
                            name="block_glm_small"),
+    W.GLM4_DENSE_BLOCK.scaled(T=100, d=256, d_ff=520, name="dense_block_small"),
+    W.GLM4_DENSE_BLOCK.scaled(T=9, d=256, d_ff=136, name="dense_block_T9"),
     # rows longer than the norm kernel keeps in registers (two passes over x)
     W.GPTOSS_DECODE.scaled(T=4, d=16400, d_ff=16, E=4, k=2, block=True, name="block_bf16_d16400"),
     W.TINY_F32.scaled(T=6, d=8200, d_ff=16, E=4, k=2, block=True, name="block_f32_d8200"),
