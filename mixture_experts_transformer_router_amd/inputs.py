@@ -23,6 +23,11 @@ MXFP4 weights replace w_* by (codes, scales):
            element 2i+1 in the high nibble; nibble = e2m1 code (bit 3 = sign)
   *_scales uint8 [E, rows, cols/32]: e8m0 exponent byte of each block of 32
            consecutive input-dim elements.
+Affine group-quantized weights (weights "affine4" / "affine8") replace w_* by
+  *_q        uint8 [E, rows, cols * bits / 8]: unsigned codes (4 bits: element
+             2i in the low nibble; 8 bits: one byte per element)
+  *_qscales, *_qbiases  bf16 [E, rows, cols / group] (group 32 for 4 bits,
+             64 for 8 bits): w = scale * q + bias.
 
 Draw order from numpy.random.default_rng(seed) (PCG64): x, router_w,
 router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, shared gate/up/down,
@@ -58,6 +63,25 @@ def _stacked_normal(rng, E, rows, cols, std, dtype):
     for e in range(E):
         out[e] = _normal(rng, (rows, cols), std, dtype)
     return out
+
+
+def _affine(rng, E, rows, cols, bits, group, std):
+    """Affine group-quantized weights: uniform codes over [0, 2^bits), a
+    bf16 scale and bias per group of `group` elements of a row, chosen so that
+    scale * q + bias has standard deviation ~std and mean ~0."""
+    levels = 1 << bits
+    q_std = ((levels * levels - 1) / 12.0) ** 0.5
+    codes = np.empty((E, rows, cols * bits // 8), dtype=np.uint8)
+    scales = np.empty((E, rows, cols // group), dtype=np.uint16)
+    biases = np.empty((E, rows, cols // group), dtype=np.uint16)
+    for e in range(E):
+        q = rng.integers(0, levels, size=(rows, cols), dtype=np.uint8)
+        codes[e] = q if bits == 8 else (q[:, 0::2] | (q[:, 1::2] << np.uint8(4)))
+        sc = (std / q_std) * (1.0 + 0.1 * rng.standard_normal(size=(rows, cols // group), dtype=np.float32))
+        bi = -sc * ((levels - 1) / 2.0) + 0.1 * std * rng.standard_normal(size=sc.shape, dtype=np.float32)
+        scales[e] = f32_to_bf16_bits(sc.astype(np.float32))
+        biases[e] = f32_to_bf16_bits(bi.astype(np.float32))
+    return codes, scales, biases
 
 
 def _mxfp4(rng, E, rows, cols, lo, hi):
@@ -110,6 +134,16 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         out["w_up_codes"], out["w_up_scales"] = _mxfp4(rng, E, F, d, lo, hi)
         out["b_up"] = bias(E, F)
         out["w_down_codes"], out["w_down_scales"] = _mxfp4(rng, E, d, F, lo, hi)
+        out["b_down"] = bias(E, d)
+    elif w.weights in ("affine4", "affine8"):
+        assert dt == "bf16"
+        bits = 4 if w.weights == "affine4" else 8
+        group = 32 if bits == 4 else 64
+        out["w_gate_q"], out["w_gate_qscales"], out["w_gate_qbiases"] = _affine(rng, E, F, d, bits, group, d ** -0.5)
+        out["b_gate"] = bias(E, F)
+        out["w_up_q"], out["w_up_qscales"], out["w_up_qbiases"] = _affine(rng, E, F, d, bits, group, d ** -0.5)
+        out["b_up"] = bias(E, F)
+        out["w_down_q"], out["w_down_qscales"], out["w_down_qbiases"] = _affine(rng, E, d, F, bits, group, F ** -0.5)
         out["b_down"] = bias(E, d)
     else:
         raise ValueError(w.weights)

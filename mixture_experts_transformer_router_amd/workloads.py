@@ -32,7 +32,7 @@ class Workload:
     E: int
     k: int
     dtype: str                 # "f32" | "bf16" (activations, dense weights, biases, out)
-    weights: str = "dense"     # "dense" | "mxfp4"
+    weights: str = "dense"     # "dense" | "mxfp4" | "affine4" (groups of 32) | "affine8" (groups of 64)
     routing: str = "gptoss"    # "gptoss" (top-k over logits, softmax over selected) | "grouped"
     act: str = "clipped_swiglu"  # "clipped_swiglu" | "silu"
     alpha: float = 1.702
@@ -93,6 +93,15 @@ GLM4_MOE_LITE = Workload(
 
 ALL = (TINY_F32, GPTOSS_DECODE, GPTOSS_PREFILL, GPTOSS_MXFP4, GLM4_MOE_LITE)
 
+# GLM4-MoE-Lite with affine group-quantized routed experts (glm4_moe_lite.go:
+# SwitchMLP through GatherQMM; quantizationParams INT4 = groups of 32 x 4 bits,
+# INT8 = groups of 64 x 8 bits, mode affine).  The shared expert stays bf16.
+GLM4_MOE_LITE_INT4 = GLM4_MOE_LITE.scaled(name="glm4moelite_int4g32_T2048_d2048_F1536_E64s1_k6_g8tg4",
+                                          weights="affine4")
+GLM4_MOE_LITE_INT8 = GLM4_MOE_LITE.scaled(name="glm4moelite_int8g64_T2048_d2048_F1536_E64s1_k6_g8tg4",
+                                          weights="affine8")
+QUANTIZED = (GLM4_MOE_LITE_INT4, GLM4_MOE_LITE_INT8)
+
 # The same layers as MoE blocks: RMSNorm in front, residual added
 # (glm4_moe_lite.go, MoEBlock.Forward; Config.RMSNormEps).
 GLM4_MOE_LITE_BLOCK = GLM4_MOE_LITE.scaled(name="glm4moelite_block_T2048_d2048_F1536_E64s1_k6_g8tg4",
@@ -108,4 +117,4 @@ GLM4_DENSE_BLOCK = Workload(
     routed_scaling_factor=1.0, score="softmax", router_bias="none", expert_bias=False, block=True)
 BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK, GLM4_DENSE_BLOCK)
 
-BY_NAME = {w.name: w for w in ALL + BLOCKS}
+BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED}

@@ -21,6 +21,11 @@ MoE layers of GPT-OSS and GLM4-MoE-Lite):
   [OCP-MX]  OCP Microscaling Formats (MX) v1.0 specification (not on the
             pages; it defines the e2m1 element and e8m0 scale the MXFP4 name
             on [GGUF] refers to).
+  [GLM-Q]   the same glm4_moe_lite.go page on quantized experts:
+            SwitchMLP (GatherQMM with weight, scales and biases, group size,
+            bits, mode), supportsGatherQMM (affine, 4 or 8 bits),
+            quantizationParams (INT4: groups of 32, 4 bits, affine; INT8:
+            groups of 64, 8 bits, affine), loadExpertWeight.
 
 Readings taken where the pages are silent or disagree (each is listed with its
 reason in the design notes of this repository):
@@ -96,6 +101,31 @@ def e8m0_value(scale: np.ndarray) -> np.ndarray:
     s = np.asarray(scale, dtype=np.int64)
     v = np.ldexp(1.0, (s - 127).astype(np.int32))
     return np.where(s == 255, np.nan, v)
+
+
+def affine_decode(q: np.ndarray, scales: np.ndarray, biases: np.ndarray, bits: int, group: int) -> np.ndarray:
+    """Decode one affine group-quantized matrix ([GLM-Q]; the pages name the
+    mode, the bits, the group size and the scale / bias arrays but print no
+    formula -- this is the plain affine reading):
+        w[r, c] = scales[r, c // group] * q[r, c] + biases[r, c // group]
+    with unsigned codes q in [0, 2^bits).  q is stored as uint8 [rows,
+    cols * bits / 8]: 8 bits one byte per element; 4 bits element 2i in the
+    low nibble and 2i+1 in the high nibble.  scales and biases are float64
+    [rows, cols / group]."""
+    q = np.asarray(q, dtype=np.uint8)
+    if bits == 8:
+        elem = q.astype(np.float64)
+    elif bits == 4:
+        rows, half = q.shape
+        elem = np.empty((rows, 2 * half), dtype=np.float64)
+        elem[:, 0::2] = q & 0x0F
+        elem[:, 1::2] = q >> 4
+    else:
+        raise ValueError(bits)
+    s = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=1)
+    b = np.repeat(np.asarray(biases, dtype=np.float64), group, axis=1)
+    assert s.shape == elem.shape
+    return s * elem + b
 
 
 def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -256,6 +286,11 @@ class ExpertWeights:
     def _mat(self, name: str, e: int) -> np.ndarray:
         if self.weights == "mxfp4":
             return mxfp4_decode(self.a[name + "_codes"][e], self.a[name + "_scales"][e])
+        if self.weights in ("affine4", "affine8"):
+            bits = 4 if self.weights == "affine4" else 8
+            group = 32 if bits == 4 else 64
+            return affine_decode(self.a[name + "_q"][e], to_f64(self.a[name + "_qscales"][e], self.dtype),
+                                 to_f64(self.a[name + "_qbiases"][e], self.dtype), bits, group)
         return to_f64(self.a[name][e], self.dtype)
 
     def _vec(self, name: str, e: int):

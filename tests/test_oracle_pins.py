@@ -396,3 +396,41 @@ def test_round_bf16_matches_torch_and_breaks_ties_to_even():
              (1 - 2.0 ** -30, 1.0), (0.0, 0.0), (3.0, 3.0)]
     for x, y in cases:   # the fourth is above the tie: one rounding from fp64 goes up
         assert O.round_bf16(np.array([x]))[0] == y, (x, y)
+
+
+# --------------------------------------------------------------------------- affine experts
+
+
+def test_affine_decode_golden_points():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "affine_points.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        bits, group, codes, sc, bi, want = [part.split() for part in line.split("|")]
+        q = np.array([[int(c, 16) for c in codes]], dtype=np.uint8)
+        got = O.affine_decode(q, np.array([[float(v) for v in sc]]), np.array([[float(v) for v in bi]]),
+                              int(bits[0]), int(group[0]))
+        np.testing.assert_array_equal(got, [[float(v) for v in want]])
+        n += 1
+    assert n == 3
+
+
+def test_affine_layer_equals_the_dense_layer_of_its_weights():
+    # decoded affine weights are bf16 x small integer + bf16: exact in float32, so a float32
+    # dense layer holding them is the same layer, through the pinned dense path
+    for weights in ("affine4", "affine8"):
+        w = W.GLM4_MOE_LITE.scaled(T=24, d=128, d_ff=64, E=8, k=2, n_group=4, topk_group=2, d_ff_shared=0,
+                                   weights=weights, name="pin_affine")
+        a = I.make_inputs(w)
+        ew = O.ExpertWeights(a, "bf16", weights)
+        dense = {k: v for k, v in a.items() if not k.startswith(("w_gate", "w_up", "w_down"))}
+        for name, pos in (("w_gate", 0), ("w_up", 2), ("w_down", 4)):
+            m = np.stack([ew.expert(e)[pos] for e in range(w.E)])
+            assert np.array_equal(m.astype(np.float32).astype(np.float64), m)
+            dense[name] = m.astype(np.float32)
+        for key in ("x", "router_w"):
+            dense[key] = O.to_f64(a[key], "bf16").astype(np.float32)
+        c = _cfg(w)
+        cd = dict(c, dtype="f32", weights="dense")
+        np.testing.assert_array_equal(O.moe_layer(a, c)["out"], O.moe_layer(dense, cd)["out"])
