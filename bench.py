@@ -2,7 +2,8 @@
 """Benchmark of the MoE-FFN layer on one MI355X; prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block]
+                    [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block|
+                                glm_int4|glm_int8]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
@@ -42,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm",
-                             "dense_block"])
+                             "dense_block", "glm_int4", "glm_int8"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -55,7 +56,8 @@ def workload(name):
     from mixture_experts_transformer_router_amd import workloads as W
     return {"decode": W.GPTOSS_DECODE, "prefill": W.GPTOSS_PREFILL, "mxfp4": W.GPTOSS_MXFP4,
             "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
-            "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK}[name]
+            "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK,
+            "glm_int4": W.GLM4_MOE_LITE_INT4, "glm_int8": W.GLM4_MOE_LITE_INT8}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -68,6 +70,9 @@ def algorithmic_gate_up(w, counts):
     active = [e for e, c in enumerate(counts) if c > 0]
     if w.weights == "mxfp4":
         wbytes_per_expert = 2 * (w.d_ff * w.d // 2 + w.d_ff * w.d // 32)
+    elif w.weights in ("affine4", "affine8"):
+        bits, group = (4, 32) if w.weights == "affine4" else (8, 64)
+        wbytes_per_expert = 2 * (w.d_ff * w.d * bits // 8 + 2 * 2 * w.d_ff * w.d // group)
     else:
         wbytes_per_expert = 2 * w.d_ff * w.d * eb
     bias = 2 * w.d_ff * eb if w.expert_bias else 0
@@ -91,7 +96,8 @@ def recorded_traffic(w, workload_name):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload_name)
-    if not rec or rec.get("source_sha256") != PS.source_digest(rec["kernel"]):
+    digest = PS.source_digest(rec["kernel"]) if rec else None
+    if digest is None or rec.get("source_sha256") != digest:
         return None
     return rec["bytes"]
 
@@ -137,7 +143,8 @@ def main():
 
     w = workload(args.workload)
     steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
-                           "block_decode": 500, "block_glm": 100, "dense_block": 100}[args.workload]
+                           "block_decode": 500, "block_glm": 100, "dense_block": 100, "glm_int4": 100,
+                           "glm_int8": 100}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)

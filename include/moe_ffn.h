@@ -233,6 +233,45 @@ moe_status moe_block_forward_grouped(const moe_block* block, const void* x, cons
                                      void* out, moe_dtype dt, void* workspace, size_t workspace_bytes,
                                      moe_routing_out* routing, hipStream_t stream);
 
+/* ---- Affine group-quantized routed experts -------------------------------
+ * glm4_moe_lite.go runs quantized experts through GatherQMM on (weight,
+ * scales, biases) with the affine mode of quantizationParams: INT4 = 4-bit
+ * codes in groups of 32, INT8 = 8-bit codes in groups of 64 (SwitchMLP,
+ * supportsGatherQMM, quantizationParams, loadExpertWeight).  The weight is
+ *   w[e][n][k] = scales[e][n][k / G] * q[e][n][k] + biases[e][n][k / G]
+ * with unsigned codes q in [0, 2^bits).  Layouts (rows, cols) as the dense
+ * weights, (d_ff, d) for gate and up, (d, d_ff) for down:
+ *   *_q       uint8 [E, rows, cols * bits / 8]: 8 bits one byte per element;
+ *             4 bits element 2i in the low nibble, 2i+1 in the high nibble;
+ *   *_scales, *_biases  bf16 [E, rows, cols / G].
+ * The decoded weight is rounded once to bf16 before the products. */
+typedef struct {
+  int bits; /* 4 (groups of 32) or 8 (groups of 64) */
+  const uint8_t* gate_q; const void* gate_scales; const void* gate_biases;
+  const uint8_t* up_q;   const void* up_scales;   const void* up_biases;
+  const uint8_t* down_q; const void* down_scales; const void* down_biases;
+} moe_affine_experts;
+
+/* The GLM4-MoE-style layer (moe_ffn_forward_grouped's routing, activation,
+ * shared expert, expert biases) with affine group-quantized routed experts;
+ * x, router, biases, shared expert and out are bf16; `block` as in
+ * moe_block_forward_grouped (NULL: the plain layer).  Requires bits 4 or 8,
+ * d and d_ff multiples of the group size (MOE_ERR_UNSUPPORTED), every
+ * code / scale / bias pointer (MOE_ERR_INVALID_ARG), and the size limits of
+ * the MXFP4 layer for the codes (d * d_ff * bits / 8 < 2^32). */
+moe_status moe_block_forward_grouped_affine(const moe_block* block, const moe_affine_experts* experts,
+                                            const void* x, const void* router_w, const void* router_b,
+                                            const float* e_score_bias,
+                                            const void* b_gate, const void* b_up, const void* b_down,
+                                            const void* shared_w_gate, const void* shared_w_up,
+                                            const void* shared_w_down, int d_ff_shared,
+                                            int T, int d, int d_ff, int E, int k,
+                                            int n_group, int topk_group, int norm_topk_prob,
+                                            float routed_scaling_factor, moe_score score,
+                                            moe_act act, float alpha, float limit,
+                                            void* out, void* workspace, size_t workspace_bytes,
+                                            moe_routing_out* routing, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 

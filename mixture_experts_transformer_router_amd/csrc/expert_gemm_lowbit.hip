@@ -1,35 +1,43 @@
-// Grouped expert GEMMs with MXFP4 weights on bf16 MFMA.
+// Grouped expert GEMMs with low-bit expert weights on bf16 MFMA.
 //
 //   gate|up:  h[r][f] = act(x[t] . Wg[e][f] + bg[e][f], x[t] . Wu[e][f] + bu[e][f])
 //   down:     y[r][n] = h[r] . Wd[e][n] + bd[e][n]
-//   with W[e][n][k] = e2m1(code[e][n][k]) * 2^(scale[e][n][k / 32] - 127)
+//   MXFP4:    W[e][n][k] = e2m1(code[e][n][k]) * 2^(scale[e][n][k / 32] - 127)
+//   affine:   W[e][n][k] = scale[e][n][k / G] * q[e][n][k] + bias[e][n][k / G]
+//             (4-bit codes with G = 32, 8-bit codes with G = 64)
 //
 // (MaxText GPT-OSS weight mapping "MOE EXPERTS"; the weight format of the
-// MXFP4 GPT-OSS checkpoints; OCP Microscaling Formats v1.0 for e2m1 / e8m0.)
+// MXFP4 GPT-OSS checkpoints; OCP Microscaling Formats v1.0 for e2m1 / e8m0;
+// glm4_moe_lite.go SwitchMLP / quantizationParams for the affine experts.)
+//
+// MXFP4 products e2m1 * 2^s are bf16 numbers, so those operands are exact;
+// affine weights are computed in fp32 (one fma) and rounded once to bf16.
 //
 // Same tile geometry, tile order and epilogue as the dense bf16 kernel, but
 // the weights stay 4-bit until they reach registers: the codes are copied
 // into LDS (a quarter of the bf16 bytes), each wavefront reads its own code
-// fragments from there and gfx950's v_cvt_scalef32_pk_bf16_fp4 turns them,
-// with the block scale, into the bf16 B operands of the MFMAs, in the shadow
-// of the previous step's MFMAs.  Every product e2m1 * 2^s is a bf16 number,
-// so the decoded operands are exact.
+// fragments from there and converts them into the bf16 B operands of the
+// MFMAs, in the shadow of the previous step's MFMAs: gfx950's
+// v_cvt_scalef32_pk_bf16_fp4 for MXFP4; byte-to-float conversions, one fma
+// with the group's scale and bias, and a bf16 pack for affine codes.
 //
 // K permutation.  v_mfma_f32_32x32x16_bf16 takes 8 k values from each lane
 // half h = lane / 32.  Within a 64-wide K tile, half h of step s (0..3) holds
 // k = 32 h + 8 s .. +7 for both operands (the MFMA sums over k in any order as
 // long as A and B agree): a lane's B codes for the whole tile are then one
-// 16-byte piece of its weight row (32 codes, one e8m0 scale), and its A
-// fragment of step s is 16-byte chunk 4 h + s of its LDS row.
+// 16-byte (4-bit) or 32-byte (8-bit) piece of its weight row under one scale
+// (and bias), and its A fragment of step s is 16-byte chunk 4 h + s of its
+// LDS row.
 //
-// Codes of 4 K tiles (128 bytes of each weight row) are copied as one group,
+// 128 bytes of each weight row's codes (4 K tiles of 4-bit, 2 of 8-bit codes)
+// are copied as one group,
 // 8 rows x 128 B per 1 KB instruction, into one of two group buffers; the
 // copies of group g + 1 are issued when tile 4 g starts, into the buffer that
 // group g - 1 used.  FAST kernels (K % 64 == 0, scale tensors 4-byte aligned
-// in base and size) copy the 8 scale bytes of each row and group the same way
-// (as the 3 aligned dwords that hold them) and run every K tile but the last
-// with the same branch-free step; the general kernel loads each lane's scale
-// bytes into registers a tile ahead and handles a K tail.
+// in base and size) copy the scales of each row and group like the codes (as
+// the aligned dwords that hold them; affine: scales and biases) and run every
+// K tile but the last with the same branch-free step.  The general kernel
+// loads each lane's scales into registers a tile ahead and handles a K tail.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -45,8 +53,9 @@ using namespace gemm;
 
 constexpr int kGroupM = MOE_MX_GROUP_M;  // row tiles walked together within an XCD
 constexpr int BK = 64;                   // K elements per A stage and per decode tile
-constexpr int kTilesPerGroup = 4;        // K tiles per code group (128 code bytes of a row)
-constexpr int kCodeRowBytes = 128;
+constexpr int kCodeRowBytes = 128;       // bytes of a weight row's codes per copy group
+// weight formats
+constexpr int kFmtMx4 = 0, kFmtAff4 = 1, kFmtAff8 = 2;
 // kinds of K-tile step (see tile_step)
 constexpr int kSteady = 0, kGeneral = 1, kLast = 2, kFinal = 3;
 template <int V> using int_c = std::integral_constant<int, V>;
@@ -73,8 +82,25 @@ __device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t codes, float scale, in
   return __builtin_bit_cast(uint32_t, r);
 }
 
-template <bool GATED, int NJ, bool FAST>
-__global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
+// bf16 pair (lo in the low half) of two fp32 values, one v_cvt_pk_bf16_f32
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+// byte b of w as a float (v_cvt_f32_ubyte<b>); b must fold to a constant
+__device__ __forceinline__ float ubyte(uint32_t w, int b) { return static_cast<float>((w >> (8 * b)) & 0xffu); }
+
+template <int FMT, bool GATED, int NJ, bool FAST>
+__global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
+  constexpr bool MX = FMT == kFmtMx4;
+  constexpr int CB = FMT == kFmtAff8 ? 8 : 4;      // code bits
+  constexpr int kTilesPerGroup = kCodeRowBytes / (BK * CB / 8);  // 4 (4-bit) or 2 (8-bit)
+  constexpr int QG = MX ? 32 : (CB == 4 ? 32 : 64);  // elements per scale
+  constexpr bool SCALE_LDS = FAST;                 // scales (and biases) copied into LDS per group
+  constexpr int NT = MX ? 1 : 2;                   // scale tables: MXFP4 scales; affine scales and biases
+  constexpr int EB = MX ? 1 : 2;                   // bytes per table element (e8m0 byte / bf16)
+  constexpr int SBY = EB * BK * kTilesPerGroup / QG;  // bytes of one row and code group in one table
+  constexpr int kScaleDw = (SBY + 3) / 4 + 1;      // aligned dwords that hold them (2-byte aligned start)
   constexpr int BN = 64 * NJ;
   constexpr int CPR = BK / 8;               // 16-byte chunks per A row
   constexpr int SEG_ROWS = 1024 / (2 * BK); // A rows per 1 KB copy segment
@@ -85,21 +111,22 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   constexpr int KK = BK / 16;  // MFMA steps per tile
   static_assert(KK == 4, "a lane's 16-byte code piece covers the 4 steps of a tile");
   constexpr int NM = 4 * NJ;   // MFMAs per step
-  constexpr int kScaleDw = 3;  // FAST: aligned dwords holding a row's 8 scale bytes of a group
-  constexpr int RS = (BN * kScaleDw + kThreads - 1) / kThreads;  // scale copy rounds per wavefront and group
+  constexpr int RS = (BN * kScaleDw + kThreads - 1) / kThreads;  // copy rounds per wavefront, group and table
 
   // A stages are separate variables (the compiler tells copies into one from
   // reads of the other only by the variable they address); the steady loop
   // is unrolled by 2 so that their indices are compile-time constants.
   __shared__ uint16_t lds_a0[BM * BK], lds_a1[BM * BK];
   __shared__ uint16_t lds_code[2][BN * kCodeRowBytes / 2];
-  __shared__ uint32_t lds_scale[2][FAST ? RS * kThreads : 1];  // row r: bytes 12 r .. 12 r + 11
+  // scale tables of two code groups; table t, row r: bytes 4 kScaleDw r .. + 4 kScaleDw - 1
+  __shared__ uint32_t lds_scale[2][NT][SCALE_LDS ? RS * kThreads : 1];
   auto stage_a = [&](int st) __attribute__((always_inline)) -> uint16_t* { return st == 0 ? lds_a0 : lds_a1; };
 
   int m_tile, n_tile;
   if (!block_tile<kGroupM>(a, m_tile, n_tile)) return;
   const int4 desc = reinterpret_cast<const int4*>(a.tile_desc)[m_tile];
   const int e = desc.x;
+  if (e >= a.E) return;  // a shared expert's tiles are left to the dense kernel
   const int N = a.N;
   const int K = a.K;
   const int n0 = n_tile * (GATED ? BN / 2 : BN);
@@ -131,10 +158,16 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   }
   // The expert's code and scale tensors (gate, up); byte offsets within one
   // expert fit 32 bits (the library rejects larger experts).
-  const uint8_t* const code_gate = a.c0 + (size_t)e * N * (K / 2);
-  const uint8_t* const code_up = GATED ? a.c1 + (size_t)e * N * (K / 2) : code_gate;
-  const uint8_t* const scale_gate = a.s0 + (size_t)e * N * (K / 32);
-  const uint8_t* const scale_up = GATED ? a.s1 + (size_t)e * N * (K / 32) : scale_gate;
+  const int code_bytes = K * CB / 8;  // of one weight row
+  const uint8_t* const code_gate = a.c0 + (size_t)e * N * code_bytes;
+  const uint8_t* const code_up = GATED ? a.c1 + (size_t)e * N * code_bytes : code_gate;
+  const uint8_t* const scale_gate = MX ? a.s0 + (size_t)e * N * (K / 32) : nullptr;
+  const uint8_t* const scale_up = MX && GATED ? a.s1 + (size_t)e * N * (K / 32) : scale_gate;
+  // affine: bf16 scales and biases [E, N, K / QG]
+  const uint16_t* const qs_gate = MX ? nullptr : reinterpret_cast<const uint16_t*>(a.s0) + (size_t)e * N * (K / QG);
+  const uint16_t* const qs_up = !MX && GATED ? reinterpret_cast<const uint16_t*>(a.s1) + (size_t)e * N * (K / QG) : qs_gate;
+  const uint16_t* const qb_gate = MX ? nullptr : a.qb0 + (size_t)e * N * (K / QG);
+  const uint16_t* const qb_up = !MX && GATED ? a.qb1 + (size_t)e * N * (K / QG) : qb_gate;
   // Code copy round i: lane l copies stored chunk l % 8 of B row
   // 32 i + code_r (code_r = 8 wv + l / 8 < 32), i.e. weight row
   // n0 + 32 (i / 2) + code_r of the gate (i even) or up (i odd) tensor in the
@@ -153,7 +186,6 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
 
   const int ktiles = (K + BK - 1) / BK;
   const int tail_tile = (K % BK) != 0 ? ktiles - 1 : -1;
-  const int code_bytes = K / 2;
 
   auto copy_a = [&](int kt, uint16_t* As, int i) __attribute__((always_inline)) {
     const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
@@ -176,42 +208,81 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
     for (int i = 0; i < RC; ++i) {
       const int wrow = clamp_row(GATED ? n0 + 32 * (i / 2) + code_r : n0 + 32 * i + code_r);
       const uint8_t* src = (GATED && (i & 1)) ? code_up : code_gate;
-      __builtin_amdgcn_global_load_lds(src + ((uint32_t)wrow * (uint32_t)(K / 2) + piece), Cs + (4 * i + wv) * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + ((uint32_t)wrow * (uint32_t)code_bytes + piece), Cs + (4 * i + wv) * 512, 16, 0, 0);
     }
   };
-  // FAST: the 8 scale bytes of group g of every B row, as the 3 aligned
-  // dwords that hold them, into scale buffer g % 2 (dword q of the buffer is
-  // dword q % 3 of row q / 3; rows past BN repeat row BN - 1 into padding).
-  // Dwords past the end of the tensor are clamped to its last one (their
-  // bytes belong to no block of K).
+  // Tensor t of the scale tables (MXFP4: e8m0 scales; affine: scales, then
+  // biases) of the gate (or down) and up weights, with the expert's offset.
+  auto table = [&](int t, bool up) __attribute__((always_inline)) -> uintptr_t {
+    const uint8_t* base = t == 0 ? (up ? a.s1 : a.s0) : reinterpret_cast<const uint8_t*>(up ? a.qb1 : a.qb0);
+    return reinterpret_cast<uintptr_t>(base) + (size_t)e * N * (K / QG) * EB;
+  };
+  // FAST: the SBY bytes of code group g of every B row in each table, as the
+  // kScaleDw aligned dwords that hold them, into scale buffer g % 2 (dword q
+  // of a table is dword q % kScaleDw of row q / kScaleDw; rows past BN repeat
+  // row BN - 1 into padding).  Dwords past the end of a tensor are clamped to
+  // its last one (their bytes belong to no group of K).
   auto issue_scales = [&](int g) __attribute__((always_inline)) {
-    uint32_t* Ss = lds_scale[g & 1];
-    const uintptr_t end_gate = reinterpret_cast<uintptr_t>(a.s0) + (size_t)a.E * N * (K / 32) - 4;
-    const uintptr_t end_up = GATED ? reinterpret_cast<uintptr_t>(a.s1) + (size_t)a.E * N * (K / 32) - 4 : end_gate;
+    const size_t tensor_bytes = (size_t)a.E * N * (K / QG) * EB;
 #pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      const int q = 64 * (4 * i + wv) + lane;
-      const int r = min(q / kScaleDw, BN - 1);
-      const bool up = GATED && (r & 63) >= 32;
-      const int wrow = clamp_row(GATED ? n0 + 32 * (r >> 6) + (r & 31) : n0 + r);
-      const uintptr_t row = reinterpret_cast<uintptr_t>(up ? scale_up : scale_gate) + (size_t)wrow * (K / 32) + 8 * g;
-      const uintptr_t dw = min((row & ~(uintptr_t)3) + 4 * (q % kScaleDw), up ? end_up : end_gate);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dw), Ss + 64 * (4 * i + wv), 4, 0, 0);
+    for (int t = 0; t < NT; ++t) {
+      uint32_t* Ss = lds_scale[g & 1][t];
+      const uintptr_t t_gate = table(t, false), t_up = GATED ? table(t, true) : t_gate;
+      const uintptr_t end_gate = t_gate - (size_t)e * N * (K / QG) * EB + tensor_bytes - 4;
+      const uintptr_t end_up = t_up - (size_t)e * N * (K / QG) * EB + tensor_bytes - 4;
+#pragma unroll
+      for (int i = 0; i < RS; ++i) {
+        const int q = 64 * (4 * i + wv) + lane;
+        const int r = min(q / kScaleDw, BN - 1);
+        const bool up = GATED && (r & 63) >= 32;
+        const int wrow = clamp_row(GATED ? n0 + 32 * (r >> 6) + (r & 31) : n0 + r);
+        const uintptr_t row = (up ? t_up : t_gate) + (size_t)wrow * (K / QG) * EB + (size_t)SBY * g;
+        const uintptr_t dw = min((row & ~(uintptr_t)3) + 4 * (q % kScaleDw), up ? end_up : end_gate);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dw), Ss + 64 * (4 * i + wv), 4, 0, 0);
+      }
     }
   };
-  // scale bytes of tile kt for this lane's half: FAST from the scale buffer,
-  // else from the tensors into registers a tile ahead (a half past K loads
-  // the row's last scale; take_scales replaces it)
-  uint32_t sraw[NJ];
-  auto load_scales = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (FAST) {
-      const uint8_t* Sb = reinterpret_cast<const uint8_t*>(lds_scale[(kt / kTilesPerGroup) & 1]);
+  // FAST: byte offset of this lane's fragment row j in scale table t (the
+  // row's piece starts (row address & 3) bytes into its first dword)
+  int sc_at[SCALE_LDS ? NT : 1][NJ];
+  if constexpr (SCALE_LDS) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int wrow = clamp_row(frag_row(j));
-        const uintptr_t row = reinterpret_cast<uintptr_t>((GATED && (j & 1)) ? scale_up : scale_gate) + (size_t)wrow * (K / 32);
-        const int r = wn * 32 * NJ + 32 * j + fr;
-        sraw[j] = Sb[kScaleDw * 4 * r + (int)(row & 3) + 2 * (kt % kTilesPerGroup) + fk];
+        const uintptr_t row = table(t, GATED && (j & 1)) + (size_t)clamp_row(frag_row(j)) * (K / QG) * EB;
+        sc_at[t][j] = kScaleDw * 4 * (wn * 32 * NJ + 32 * j + fr) + (int)(row & 3);
+      }
+  }
+  // scales of tile kt for this lane's half: FAST from the scale buffer,
+  // else from the tensors into registers a tile ahead (a half past K loads
+  // the row's last scale; take_scales replaces it).  Affine: the bf16 scale
+  // in the low and the bf16 bias in the high half of sraw.
+  uint32_t sraw[NJ];
+  auto load_scales = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (SCALE_LDS) {
+      // element (BK (kt % TPG) + 32 fk) / QG of the row's group piece, behind
+      // the piece's offset within its first aligned dword
+      const int el = (BK * (kt % kTilesPerGroup) + 32 * fk) / QG;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint8_t* Sb = reinterpret_cast<const uint8_t*>(lds_scale[(kt / kTilesPerGroup) & 1][t]);
+          const int at = sc_at[t][j] + EB * el;
+          const uint32_t x = EB == 1 ? (uint32_t)Sb[at] : (uint32_t)*reinterpret_cast<const uint16_t*>(Sb + at);
+          v |= x << (16 * t);
+        }
+        sraw[j] = v;
+      }
+    } else if constexpr (!MX) {
+      const int gi = min((BK * kt + 32 * fk) / QG, K / QG - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t at = (uint32_t)clamp_row(frag_row(j)) * (uint32_t)(K / QG) + gi;
+        const bool up = GATED && (j & 1);
+        sraw[j] = (uint32_t)(up ? qs_up : qs_gate)[at] | ((uint32_t)(up ? qb_up : qb_gate)[at] << 16);
       }
     } else {
       const int cb = min(2 * kt + fk, K / 32 - 1);
@@ -221,28 +292,53 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
     }
   };
   float scf[NJ];      // scale factors of the current tile
-  uint32_t nan_j = 0; // bit j: scale byte 255 (NaN block) in the current tile
-  // scales of tile kt from sraw (a half past K: 127; its codes are zero)
+  float sbi[MX ? 1 : NJ];  // affine: biases of the current tile
+  uint32_t nan_j = 0; // MXFP4, bit j: scale byte 255 (NaN block) in the current tile
+  // scales of tile kt from sraw (a half past K: MXFP4 127, affine scale and
+  // bias 0, with zero codes either way)
   auto take_scales = [&](int kt) __attribute__((always_inline)) {
-    const bool past = !FAST && 2 * kt + fk >= K / 32;
-    nan_j = 0;
+    const bool past = !FAST && BK * kt + 32 * fk >= K;
+    if constexpr (MX) {
+      nan_j = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint32_t sb = past ? 127u : sraw[j];
-      scf[j] = scale_factor(sb);
-      nan_j |= (sb == 255u ? 1u : 0u) << j;
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t sb = past ? 127u : sraw[j];
+        scf[j] = scale_factor(sb);
+        nan_j |= (sb == 255u ? 1u : 0u) << j;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        scf[j] = past ? 0.f : bf16_to_f32(static_cast<uint16_t>(sraw[j] & 0xffffu));
+        sbi[j] = past ? 0.f : bf16_to_f32(static_cast<uint16_t>(sraw[j] >> 16));
+      }
     }
   };
-  // this lane's code pieces of tile kt (zero for a half past K)
-  u32x4_t cw[NJ];
+  // this lane's code pieces of tile kt (zero for a half past K): 16 bytes
+  // (4-bit codes) in cw, 32 bytes (8-bit codes) in cw and cw2
+  u32x4_t cw[NJ], cw2[CB == 8 ? NJ : 1];
   auto read_codes = [&](int kt, bool check_k) __attribute__((always_inline)) {
     const uint16_t* Cs = lds_code[(kt / kTilesPerGroup) & 1];
-    const int c = code_chunk(0, 2 * (kt % kTilesPerGroup) + fk) ^ code_x;
+    if constexpr (CB == 4) {
+      const int c = code_chunk(0, 2 * (kt % kTilesPerGroup) + fk) ^ code_x;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) cw[j] = *reinterpret_cast<const u32x4_t*>(Cs + code_off0 + 32 * j * (kCodeRowBytes / 2) + 8 * c);
+      for (int j = 0; j < NJ; ++j)
+        cw[j] = *reinterpret_cast<const u32x4_t*>(Cs + code_off0 + 32 * j * (kCodeRowBytes / 2) + 8 * c);
+    } else {
+      const int c0 = code_chunk(0, 4 * (kt % kTilesPerGroup) + 2 * fk) ^ code_x;
+      const int c1 = code_chunk(0, 4 * (kt % kTilesPerGroup) + 2 * fk + 1) ^ code_x;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        cw[j] = *reinterpret_cast<const u32x4_t*>(Cs + code_off0 + 32 * j * (kCodeRowBytes / 2) + 8 * c0);
+        cw2[j] = *reinterpret_cast<const u32x4_t*>(Cs + code_off0 + 32 * j * (kCodeRowBytes / 2) + 8 * c1);
+      }
+    }
     if (check_k && kt * BK + 32 * fk >= K) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) cw[j] = u32x4_t{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NJ; ++j) {
+        cw[j] = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (CB == 8) cw2[j] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
   };
   // zero the A chunks of the tile past K (the last tile only)
@@ -275,9 +371,23 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   // NaN blocks (one NaN element makes every output of the column NaN, as
   // the NaN weights would)
   auto cvt_part = [&](int s, int buf, int j, int p) __attribute__((always_inline)) {
-    const uint32_t w = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
-    uint32_t v = cvt_fp4_pair(w, scf[j], p);
-    if (s == 0 && p == 0) v = (nan_j >> j) & 1 ? 0x7fc07fc0u : v;
+    uint32_t v;
+    if constexpr (MX) {
+      const uint32_t w = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
+      v = cvt_fp4_pair(w, scf[j], p);
+      if (s == 0 && p == 0) v = (nan_j >> j) & 1 ? 0x7fc07fc0u : v;
+    } else if constexpr (CB == 4) {
+      // elements 2p, 2p + 1: the low and high nibble of byte p of word s,
+      // i.e. byte p of the word's low and high nibbles spread to bytes
+      const uint32_t w = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
+      const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+      v = pack2(fmaf(scf[j], ubyte(lo, p), sbi[j]), fmaf(scf[j], ubyte(hi, p), sbi[j]));
+    } else {
+      // elements 2p, 2p + 1: bytes 2 (p % 2), +1 of word p / 2 of step s's 8 bytes
+      const u32x4_t& c = s < 2 ? cw[j] : cw2[j];
+      const uint32_t w = (s & 1) == 0 ? (p < 2 ? c.x : c.y) : (p < 2 ? c.z : c.w);
+      v = pack2(fmaf(scf[j], ubyte(w, 2 * (p & 1)), sbi[j]), fmaf(scf[j], ubyte(w, 2 * (p & 1) + 1), sbi[j]));
+    }
     if (p == 0) fbw[buf][j].x = v;
     else if (p == 1) fbw[buf][j].y = v;
     else if (p == 2) fbw[buf][j].z = v;
@@ -297,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   if (ktiles > 1) issue_a(1, off ^ 1);
   issue_codes(0);
   if (kCodeRowBytes < code_bytes) issue_codes(1);
-  if constexpr (FAST) {
+  if constexpr (SCALE_LDS) {
     issue_scales(0);
     if (kCodeRowBytes < code_bytes) issue_scales(1);
     wait_vmcnt<0>();
@@ -368,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
         barrier_lds();
       }
       read_codes(kt + 1, !STEADY);
-      if constexpr (FAST) {
+      if constexpr (SCALE_LDS) {
         load_scales(kt + 1);  // LDS reads; converted once they have landed
       } else {
         take_scales(kt + 1);
@@ -377,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
       const int g1 = (kt + 1) / kTilesPerGroup + 1;
       if (COPIES && (kt + 1) % kTilesPerGroup == 0 && kCodeRowBytes * g1 < code_bytes) {
         issue_codes(g1);
-        if constexpr (FAST) issue_scales(g1);
+        if constexpr (SCALE_LDS) issue_scales(g1);
       }
       const bool more_a = STEADY || kt + 2 < ktiles;
       const int kt2 = min(kt + 2, ktiles - 1);
@@ -392,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
           if (m < 4) load_fa(As1, 0, nxt, m);
           if (m == NM / 2 - 1) {
             wait_lgkmcnt0();
-            if constexpr (FAST) take_scales(kt + 1);
+            if constexpr (SCALE_LDS) take_scales(kt + 1);
           }
           if (m >= NM / 2) {
             cvt_part(0, nxt, (2 * (m - NM / 2)) / 4, (2 * (m - NM / 2)) % 4);
@@ -410,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) mfma_m(cur, m);
         wait_lgkmcnt0();
-        if constexpr (FAST) take_scales(kt + 1);
+        if constexpr (SCALE_LDS) take_scales(kt + 1);
 #pragma unroll
         for (int m = 0; m < NM; ++m) cvt_part(0, nxt, m / 4, m % 4);
       }
@@ -445,21 +555,39 @@ __global__ __launch_bounds__(kThreads, 1) void mxfp4_gemm_kernel(MfmaArgs a) {
   store_tile<GATED, NJ>(a, acc, e, false, N, n0, r0, r_end, wm, wn, lane);
 }
 
-// The FAST kernel applies: K % 64 == 0 and the scale tensor [E, N, K / 32]
-// 4-byte aligned in base and size (its dwords can then be copied whole).
-bool fast_shape(const Layer& L, int K, int N, const uint8_t* scales) {
-  const size_t bytes = (size_t)L.E * N * (K / 32);
-  return K % BK == 0 && reinterpret_cast<uintptr_t>(scales) % 4 == 0 && bytes % 4 == 0;
+// The FAST kernel applies when K % 64 == 0 and the scale tensors (MXFP4:
+// e8m0 [E, N, K / 32]; affine: bf16 scales and biases [E, N, K / G]) are
+// 4-byte aligned in base and size: their dwords are then copied whole.
+bool fast_shape(const Layer& L, int K, int N, const void* scales, const void* biases) {
+  if (K % BK) return false;
+  const bool mx = L.wfmt == WF_MXFP4;
+  const size_t bytes = (size_t)L.E * N * (K / (L.wfmt == WF_AFF8 ? 64 : 32)) * (mx ? 1 : 2);
+  const auto aligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 4 == 0; };
+  return bytes % 4 == 0 && aligned(scales) && (mx || aligned(biases));
+}
+
+template <int FMT, bool GATED, int NJ>
+void launch_fmt(const MfmaArgs& m, dim3 grid, bool fast, hipStream_t s) {
+  if (fast) lowbit_gemm_kernel<FMT, GATED, NJ, true><<<grid, kThreads, 0, s>>>(m);
+  else lowbit_gemm_kernel<FMT, GATED, NJ, false><<<grid, kThreads, 0, s>>>(m);
+}
+
+template <bool GATED, int NJ>
+void launch_any(const Layer& L, const MfmaArgs& m, dim3 grid, bool fast, hipStream_t s) {
+  if (L.wfmt == WF_MXFP4) launch_fmt<kFmtMx4, GATED, NJ>(m, grid, fast, s);
+  else if (L.wfmt == WF_AFF4) launch_fmt<kFmtAff4, GATED, NJ>(m, grid, fast, s);
+  else launch_fmt<kFmtAff8, GATED, NJ>(m, grid, fast, s);
 }
 
 }  // namespace
 
-hipError_t launch_gate_up_mxfp4(const Layer& L, const Work& W, hipStream_t s) {
+hipError_t launch_gate_up_lowbit(const Layer& L, const Work& W, hipStream_t s) {
   MfmaArgs m = base_args(L, W);
   m.a = static_cast<const uint16_t*>(L.x);
   m.lda = L.d;
   m.row_token = W.row_token;
   m.c0 = L.wg_codes; m.s0 = L.wg_scales; m.c1 = L.wu_codes; m.s1 = L.wu_scales;
+  m.qb0 = static_cast<const uint16_t*>(L.wg_qbias); m.qb1 = static_cast<const uint16_t*>(L.wu_qbias);
   m.bias0 = static_cast<const uint16_t*>(L.bg);
   m.bias1 = static_cast<const uint16_t*>(L.bu);
   m.N = L.F; m.K = L.d; m.N_sh = L.F; m.K_sh = L.d;
@@ -467,19 +595,18 @@ hipError_t launch_gate_up_mxfp4(const Layer& L, const Work& W, hipStream_t s) {
   m.ldo = L.F_max();
   m.n_tiles = (L.F + 127) / 128;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
-  if (fast_shape(L, L.d, L.F, L.wg_scales) && fast_shape(L, L.d, L.F, L.wu_scales))
-    mxfp4_gemm_kernel<true, 4, true><<<grid, kThreads, 0, s>>>(m);
-  else
-    mxfp4_gemm_kernel<true, 4, false><<<grid, kThreads, 0, s>>>(m);
+  const bool fast = fast_shape(L, L.d, L.F, L.wg_scales, L.wg_qbias) && fast_shape(L, L.d, L.F, L.wu_scales, L.wu_qbias);
+  launch_any<true, 4>(L, m, grid, fast, s);
   return hipGetLastError();
 }
 
-hipError_t launch_down_mxfp4(const Layer& L, const Work& W, hipStream_t s) {
+hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s) {
   MfmaArgs m = base_args(L, W);
   m.a = static_cast<const uint16_t*>(W.h);
   m.lda = L.F_max();
   m.row_token = nullptr;
   m.c0 = L.wd_codes; m.s0 = L.wd_scales;
+  m.qb0 = static_cast<const uint16_t*>(L.wd_qbias);
   m.bias0 = static_cast<const uint16_t*>(L.bd);
   m.N = L.d; m.K = L.F; m.N_sh = L.d; m.K_sh = L.F;
   m.out = static_cast<uint16_t*>(W.y);
@@ -489,14 +616,9 @@ hipError_t launch_down_mxfp4(const Layer& L, const Work& W, hipStream_t s) {
   const bool narrow = t192 * (256 + 48) < t256 * (256 + 64);
   m.n_tiles = narrow ? t192 : t256;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
-  const bool fast = fast_shape(L, L.F, L.d, L.wd_scales);
-  if (narrow) {
-    if (fast) mxfp4_gemm_kernel<false, 3, true><<<grid, kThreads, 0, s>>>(m);
-    else mxfp4_gemm_kernel<false, 3, false><<<grid, kThreads, 0, s>>>(m);
-  } else {
-    if (fast) mxfp4_gemm_kernel<false, 4, true><<<grid, kThreads, 0, s>>>(m);
-    else mxfp4_gemm_kernel<false, 4, false><<<grid, kThreads, 0, s>>>(m);
-  }
+  const bool fast = fast_shape(L, L.F, L.d, L.wd_scales, L.wd_qbias);
+  if (narrow) launch_any<false, 3>(L, m, grid, fast, s);
+  else launch_any<false, 4>(L, m, grid, fast, s);
   return hipGetLastError();
 }
 

@@ -390,8 +390,10 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
 
 }  // namespace
 
-hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) {
+namespace {
+hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first) {
   MfmaArgs m = base_args(L, W);
+  m.e_first = e_first;
   m.a = static_cast<const uint16_t*>(L.x);
   m.lda = L.d;
   m.row_token = W.row_token;
@@ -410,8 +412,9 @@ hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) {
+hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first) {
   MfmaArgs m = base_args(L, W);
+  m.e_first = e_first;
   m.a = static_cast<const uint16_t*>(W.h);
   m.lda = L.F_max();
   m.row_token = nullptr;
@@ -433,5 +436,13 @@ hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) {
   else mfma_gemm_kernel<false, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
+}  // namespace
+
+hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) { return gate_up_mfma(L, W, s, 0); }
+hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) { return down_mfma(L, W, s, 0); }
+hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t s) {
+  return gate_up_mfma(L, W, s, L.E);
+}
+hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s) { return down_mfma(L, W, s, L.E); }
 
 }  // namespace moe

@@ -28,16 +28,19 @@ struct MfmaArgs {
   const int32_t* row_token;   // gate|up: token of each sorted row; down: nullptr
   const uint16_t* w0;         // dense [E, N, K] (down, or gate)
   const uint16_t* w1;         // dense up
-  const uint8_t* c0;          // MXFP4 codes [E, N, K/2] / scales [E, N, K/32]
-  const uint8_t* s0;
+  const uint8_t* c0;          // low-bit codes [E, N, K * bits / 8]; scales: MXFP4 e8m0 bytes
+  const uint8_t* s0;          // [E, N, K / 32], affine bf16 [E, N, K / group]
   const uint8_t* c1;
   const uint8_t* s1;
+  const uint16_t* qb0;        // affine: bf16 biases [E, N, K / group] of c0 / c1
+  const uint16_t* qb1;
   const uint16_t* bias0;      // [E, N] or nullptr
   const uint16_t* bias1;
   const uint16_t* sh_w0;      // shared expert [N_sh, K_sh] or nullptr
   const uint16_t* sh_w1;
   int N, K, N_sh, K_sh;
   int E, E_all;
+  int e_first;                // tiles of experts below e_first are skipped
   const int32_t* offsets;     // [E_all + 1]
   const int32_t* tile_prefix; // [E_all + 1], 256-row tiles
   const int32_t* tile_desc;   // [tiles][4]: expert, first row, end row
@@ -114,7 +117,8 @@ __device__ __forceinline__ float expert_act_t(float g, float u, float alpha, flo
 // device; every block reads it and the blocks of XCD x take the x-th
 // contiguous share of the tiles, walked kGroupM row tiles at a time, so the
 // blocks resident on one XCD reuse each other's A and B tiles through its L2.
-// Returns false for blocks without a tile.
+// Returns false for blocks without a tile, or whose tile belongs to an expert
+// below a.e_first.
 template <int kGroupM>
 __device__ __forceinline__ bool block_tile(const MfmaArgs& a, int& m_tile, int& n_tile) {
   const int total_m = a.tile_prefix[a.E_all];
@@ -129,7 +133,7 @@ __device__ __forceinline__ bool block_tile(const MfmaArgs& a, int& m_tile, int& 
   const int rr = L - group * kGroupM * a.n_tiles;
   m_tile = first_m + rr % gm;
   n_tile = rr / gm;
-  return true;
+  return a.e_first == 0 || reinterpret_cast<const int4*>(a.tile_desc)[m_tile].x >= a.e_first;
 }
 
 // Epilogue of a 256 x (64 NJ) tile held by 4 wavefronts (2 x 2, each 128 x

@@ -73,15 +73,16 @@ moe_status check_common(const Layer& L) {
   if (L.k > 16) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 16", L.k);
   if ((long long)L.T * L.k >= (1ll << 26)) return fail(MOE_ERR_UNSUPPORTED, "T * k = %lld >= 2^26", (long long)L.T * L.k);
   if (L.dt != MOE_F32 && L.dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", L.dt);
-  const int q = L.wfmt == WF_MXFP4 ? 32 : 8;
+  const int q = L.wfmt == WF_AFF8 ? 64 : lowbit_format(L.wfmt) ? 32 : 8;
   if (L.d % q || L.F % q) return fail(MOE_ERR_UNSUPPORTED, "d = %d and d_ff = %d must be multiples of %d", L.d, L.F, q);
-  if (L.wfmt == WF_MXFP4) {
-    // the MXFP4 kernels address one expert's codes and the activation rows
-    // with 32-bit offsets
-    if ((unsigned long long)L.d * L.F / 2 >= (1ull << 32))
-      return fail(MOE_ERR_UNSUPPORTED, "d * d_ff = %lld >= 2^33 with MXFP4 weights", (long long)L.d * L.F);
+  if (lowbit_format(L.wfmt)) {
+    // the low-bit kernels address one expert's codes and the activation
+    // rows with 32-bit offsets
+    const unsigned long long code_bytes = (unsigned long long)L.d * L.F * (L.wfmt == WF_AFF8 ? 8 : 4) / 8;
+    if (code_bytes >= (1ull << 32))
+      return fail(MOE_ERR_UNSUPPORTED, "d * d_ff = %lld: an expert's codes reach 2^32 bytes", (long long)L.d * L.F);
     if ((unsigned long long)L.rows_all() * (L.d > L.F ? L.d : L.F) >= (1ull << 32))
-      return fail(MOE_ERR_UNSUPPORTED, "T * k * max(d, d_ff) >= 2^32 with MXFP4 weights");
+      return fail(MOE_ERR_UNSUPPORTED, "T * k * max(d, d_ff) >= 2^32 with low-bit weights");
   }
   if (L.act != MOE_ACT_CLIPPED_SWIGLU && L.act != MOE_ACT_SILU) return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", L.act);
   if (L.act == MOE_ACT_CLIPPED_SWIGLU) {
@@ -106,9 +107,11 @@ moe_status check_common(const Layer& L) {
     return fail(MOE_ERR_INVALID_ARG, "RMSNorm eps = %g must be finite and >= 0", (double)L.eps);
   if (L.T == 0) return MOE_OK;
   if (!L.x || !L.router_w || !L.out) return fail(MOE_ERR_INVALID_ARG, "x, router_w and out are required");
-  if (L.wfmt == WF_MXFP4) {
+  if (lowbit_format(L.wfmt)) {
     if (!L.wg_codes || !L.wg_scales || !L.wu_codes || !L.wu_scales || !L.wd_codes || !L.wd_scales)
-      return fail(MOE_ERR_INVALID_ARG, "all MXFP4 codes and scales are required");
+      return fail(MOE_ERR_INVALID_ARG, "all codes and scales are required");
+    if (L.wfmt != WF_MXFP4 && (!L.wg_qbias || !L.wu_qbias || !L.wd_qbias))
+      return fail(MOE_ERR_INVALID_ARG, "all affine biases are required");
   } else if (!L.wg || !L.wu || !L.wd) {
     return fail(MOE_ERR_INVALID_ARG, "w_gate, w_up and w_down are required");
   }
@@ -149,23 +152,28 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   // Expert stages: weight streaming on MFMA for a few tokens (every expert
   // then holds at most kDecodeMaxTokens rows), grouped MFMA GEMMs for bf16 /
   // MXFP4 otherwise, vector-ALU tiles for fp32.
-  enum { kDecode, kMfma, kMxfp4, kTiled } path;
+  enum { kDecode, kMfma, kLowbit, kTiled } path;
   if (L.dt == MOE_F32) path = kTiled;
-  else if (L.wfmt == WF_MXFP4) path = kMxfp4;
+  else if (lowbit_format(L.wfmt)) path = kLowbit;
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
+  // low-bit routed experts with a (bf16) shared expert: the dense GEMM takes
+  // the shared expert's tiles
+  const bool shared_dense = path == kLowbit && L.has_shared();
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     e = path == kDecode ? launch_gate_up_decode(L, W, s)
         : path == kMfma ? launch_gate_up_mfma(L, W, s)
-        : path == kMxfp4 ? launch_gate_up_mxfp4(L, W, s) : launch_gate_up(L, W, s);
+        : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
+    if (e == hipSuccess && shared_dense) e = launch_gate_up_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
     StageTimer tm(s, MOE_STAGE_DOWN);
     e = path == kDecode ? launch_down_decode(L, W, s)
         : path == kMfma ? launch_down_mfma(L, W, s)
-        : path == kMxfp4 ? launch_down_mxfp4(L, W, s) : launch_down(L, W, s);
+        : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
+    if (e == hipSuccess && shared_dense) e = launch_down_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
   {
@@ -335,6 +343,41 @@ moe_status moe_block_forward_grouped(const moe_block* block, const void* x, cons
   L.rsf = routed_scaling_factor; L.score = score;
   L.act = act; L.alpha = alpha; L.limit = limit;
   L.dt = dt; L.wfmt = dt == MOE_F32 ? moe::WF_F32 : moe::WF_BF16;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  apply_block(L, block);
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_block_forward_grouped_affine(const moe_block* block, const moe_affine_experts* experts,
+                                            const void* x, const void* router_w, const void* router_b,
+                                            const float* e_score_bias, const void* b_gate, const void* b_up,
+                                            const void* b_down, const void* shared_w_gate, const void* shared_w_up,
+                                            const void* shared_w_down, int d_ff_shared, int T, int d, int d_ff,
+                                            int E, int k, int n_group, int topk_group, int norm_topk_prob,
+                                            float routed_scaling_factor, moe_score score, moe_act act, float alpha,
+                                            float limit, void* out, void* workspace, size_t workspace_bytes,
+                                            moe_routing_out* routing, hipStream_t stream) {
+  moe::g_detail[0] = '\0';
+  if (!experts) return moe::fail(MOE_ERR_INVALID_ARG, "experts is required");
+  if (experts->bits != 4 && experts->bits != 8)
+    return moe::fail(MOE_ERR_UNSUPPORTED, "affine experts with %d bits (4 or 8 supported)", experts->bits);
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b; L.e_bias = e_score_bias;
+  L.wg_codes = experts->gate_q; L.wg_scales = static_cast<const uint8_t*>(experts->gate_scales);
+  L.wg_qbias = experts->gate_biases;
+  L.wu_codes = experts->up_q; L.wu_scales = static_cast<const uint8_t*>(experts->up_scales);
+  L.wu_qbias = experts->up_biases;
+  L.wd_codes = experts->down_q; L.wd_scales = static_cast<const uint8_t*>(experts->down_scales);
+  L.wd_qbias = experts->down_biases;
+  L.bg = b_gate; L.bu = b_up; L.bd = b_down;
+  L.sh_wg = shared_w_gate; L.sh_wu = shared_w_up; L.sh_wd = shared_w_down;
+  L.F_sh = shared_w_gate ? d_ff_shared : 0;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.grouped = 1; L.n_group = n_group; L.topk_group = topk_group; L.norm = norm_topk_prob ? 1 : 0;
+  L.rsf = routed_scaling_factor; L.score = score;
+  L.act = act; L.alpha = alpha; L.limit = limit;
+  L.dt = MOE_BF16; L.wfmt = experts->bits == 4 ? moe::WF_AFF4 : moe::WF_AFF8;
   L.out = out;
   if (routing) L.routing = *routing;
   apply_block(L, block);

@@ -10,7 +10,10 @@
 namespace moe {
 
 // Storage format of the expert weights.
-enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2 };
+// WF_AFF4 / WF_AFF8: affine group-quantized codes (4 bits, groups of 32 /
+// 8 bits, groups of 64) with bf16 scales and biases.
+enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2, WF_AFF4 = 3, WF_AFF8 = 4 };
+inline bool lowbit_format(int wfmt) { return wfmt >= WF_MXFP4; }
 
 // Tokens handled by one block of the permute kernel.  Router blocks cover
 // route_block_tokens() tokens, a divisor of this.
@@ -49,7 +52,10 @@ struct Layer {
   const uint8_t* wu_codes = nullptr;
   const uint8_t* wu_scales = nullptr;
   const uint8_t* wd_codes = nullptr;
-  const uint8_t* wd_scales = nullptr;
+  const uint8_t* wd_scales = nullptr;     // MXFP4: e8m0 bytes; affine: bf16 scales
+  const void* wg_qbias = nullptr;         // affine: bf16 biases of the codes
+  const void* wu_qbias = nullptr;
+  const void* wd_qbias = nullptr;
   const void* sh_wg = nullptr;
   const void* sh_wu = nullptr;
   const void* sh_wd = nullptr;
@@ -112,8 +118,12 @@ hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s);
-hipError_t launch_gate_up_mxfp4(const Layer& L, const Work& W, hipStream_t s);
-hipError_t launch_down_mxfp4(const Layer& L, const Work& W, hipStream_t s);
+// low-bit expert weights (MXFP4, affine); the shared expert's tiles are skipped
+hipError_t launch_gate_up_lowbit(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s);
+// the dense bf16 GEMMs restricted to the shared expert's tiles
+hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_rmsnorm(const Layer& L, const Work& W, hipStream_t s);
 

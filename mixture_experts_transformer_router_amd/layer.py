@@ -38,6 +38,16 @@ def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=No
         e_score_bias=None):
     """One layer (or block) forward of workload `w` on device tensors `t`."""
     block = block_of(w, t)
+    if w.weights in ("affine4", "affine8"):
+        return moe_ffn.forward_grouped_affine(
+            moe_ffn.make_affine(4 if w.weights == "affine4" else 8, t), t["x"], t["router_w"], t.get("router_b"),
+            w.k, w.n_group, w.topk_group, w.norm_topk_prob, w.routed_scaling_factor, w.d_ff,
+            score=moe_ffn.MOE_SCORE_SOFTMAX if w.score == "softmax" else moe_ffn.MOE_SCORE_SIGMOID,
+            act=moe_ffn.MOE_ACT_SILU if w.act == "silu" else moe_ffn.MOE_ACT_CLIPPED_SWIGLU,
+            alpha=w.alpha, limit=w.limit, e_score_bias=e_score_bias, b_gate=t.get("b_gate"), b_up=t.get("b_up"),
+            b_down=t.get("b_down"), shared_w_gate=t.get("shared_w_gate"), shared_w_up=t.get("shared_w_up"),
+            shared_w_down=t.get("shared_w_down"), E=w.E, out=out, workspace=workspace, routing=routing,
+            stream=stream, block=block)
     if w.routing == "grouped":
         return moe_ffn.forward_grouped(
             t["x"], t["router_w"], t.get("router_b"), t.get("w_gate"), t.get("b_gate"), t.get("w_up"),

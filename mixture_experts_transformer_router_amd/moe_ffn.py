@@ -11,6 +11,8 @@ stream.  The entry points keep the C names:
     workspace_bytes(...)  -> moe_ffn_workspace_bytes
     each with block=MoeBlock(...) -> the moe_block_* entry point of the same
     layer (RMSNorm in front, residual after) and moe_block_workspace_bytes
+    forward_grouped_affine(...) -> moe_block_forward_grouped_affine
+                                   (affine group-quantized routed experts)
 
 If the shared library has not been built, loading raises MoeLibraryMissing;
 there is no other implementation to fall back to.
@@ -35,7 +37,8 @@ STAGES = ("route", "permute", "gate_up", "down", "combine")
 EXPORTED = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp4",
             "moe_ffn_forward_grouped", "moe_status_string", "moe_last_error_detail",
             "moe_ffn_profile_enable", "moe_ffn_profile_read", "moe_block_workspace_bytes",
-            "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped")
+            "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped",
+            "moe_block_forward_grouped_affine")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -56,6 +59,20 @@ class MoeBlock(ctypes.Structure):
 def make_block(norm_w: Optional[torch.Tensor], eps: float = 1e-5, residual: bool = True) -> MoeBlock:
     """A moe_block for `norm_w` (a device tensor [d], kept alive by the caller)."""
     return MoeBlock(None if norm_w is None else norm_w.data_ptr(), eps, int(bool(residual)))
+
+
+class AffineExperts(ctypes.Structure):
+    """moe_affine_experts: bits, then (codes, scales, biases) device pointers of gate, up, down."""
+    _fields_ = [("bits", ctypes.c_int)] + [(f"{w}_{part}", ctypes.c_void_p)
+                                          for w in ("gate", "up", "down") for part in ("q", "scales", "biases")]
+
+
+def make_affine(bits: int, t: dict) -> AffineExperts:
+    """moe_affine_experts from device tensors t["w_gate_q"], t["w_gate_qscales"], ... (kept alive by the caller)."""
+    vals = [bits]
+    for w in ("gate", "up", "down"):
+        vals += [t[f"w_{w}_q"].data_ptr(), t[f"w_{w}_qscales"].data_ptr(), t[f"w_{w}_qbiases"].data_ptr()]
+    return AffineExperts(*vals)
 
 
 class RoutingOut(ctypes.Structure):
@@ -98,6 +115,10 @@ def load() -> ctypes.CDLL:
         blk = getattr(L, name.replace("moe_ffn_", "moe_block_"))
         blk.restype = _I
         blk.argtypes = [_P] + getattr(L, name).argtypes
+    L.moe_block_forward_grouped_affine.restype = _I
+    L.moe_block_forward_grouped_affine.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                                   _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F,
+                                                   _P, _P, _Z, _P, _P]
     L.moe_block_workspace_bytes.restype = _Z
     L.moe_block_workspace_bytes.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -239,6 +260,29 @@ def forward_grouped(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b
     return (out, r) if routing else out
 
 
+def forward_grouped_affine(experts: AffineExperts, x, router_w, router_b, k, n_group, topk_group, norm_topk_prob,
+                           routed_scaling_factor, d_ff, score=MOE_SCORE_SOFTMAX, act=MOE_ACT_SILU, alpha=1.702,
+                           limit=7.0, e_score_bias=None, b_gate=None, b_up=None, b_down=None, shared_w_gate=None,
+                           shared_w_up=None, shared_w_down=None, E=None, out=None, workspace=None, routing=False,
+                           stream=None, block=None):
+    """moe_block_forward_grouped_affine (block None: the plain layer).  `experts` from make_affine."""
+    T, d = x.shape
+    E = router_w.shape[0] if E is None else E
+    Fs = shared_w_gate.shape[0] if shared_w_gate is not None else 0
+    out = torch.empty_like(x) if out is None else out
+    ws = workspace if workspace is not None else alloc_workspace(
+        workspace_bytes(T, d, d_ff, E, k, MOE_BF16, Fs, block=block), x.device)
+    r, rs = _routing(T, k, E, x.device, routing)
+    st = load().moe_block_forward_grouped_affine(
+        ctypes.byref(block) if block is not None else None, ctypes.byref(experts),
+        _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(e_score_bias), _ptr(b_gate), _ptr(b_up), _ptr(b_down),
+        _ptr(shared_w_gate), _ptr(shared_w_up), _ptr(shared_w_down), Fs, T, d, d_ff, E, k, n_group, topk_group,
+        int(bool(norm_topk_prob)), routed_scaling_factor, score, act, alpha, limit, _ptr(out), _ptr(ws),
+        ws.numel(), ctypes.byref(rs) if rs is not None else None, _stream(stream))
+    _check(st)
+    return (out, r) if routing else out
+
+
 def profile_enable(stage_mask: int):
     _check(load().moe_ffn_profile_enable(stage_mask))
 
@@ -278,6 +322,26 @@ def bound_layer_call(w, t: dict, out: torch.Tensor, workspace: torch.Tensor, str
     rp = ctypes.byref(routing) if routing is not None else None
     g = t.get
     blk = make_block(t["norm_w"], w.norm_eps, True) if getattr(w, "block", False) else None
+    if w.weights in ("affine4", "affine8"):
+        aff = make_affine(4 if w.weights == "affine4" else 8, t)
+        Fs = g("shared_w_gate").shape[0] if g("shared_w_gate") is not None else 0
+        L = load()
+        args = [ctypes.byref(blk) if blk is not None else None, ctypes.byref(aff)] + [
+            a.data_ptr() if isinstance(a, torch.Tensor) else a for a in (
+                g("x"), g("router_w"), g("router_b"), None, g("b_gate"), g("b_up"), g("b_down"),
+                g("shared_w_gate"), g("shared_w_up"), g("shared_w_down"), Fs, w.T, w.d, w.d_ff, w.E, w.k,
+                w.n_group, w.topk_group, int(w.norm_topk_prob), w.routed_scaling_factor,
+                MOE_SCORE_SOFTMAX if w.score == "softmax" else MOE_SCORE_SIGMOID,
+                MOE_ACT_SILU if w.act == "silu" else MOE_ACT_CLIPPED_SWIGLU, w.alpha, w.limit, out, workspace,
+                workspace.numel())] + [rp, s]
+        keep = (aff, blk)
+
+        def call():
+            st = L.moe_block_forward_grouped_affine(*args)
+            if st != MOE_OK:
+                _check(st)
+        call.keep = keep
+        return call
     if w.routing == "grouped":
         Fs = g("shared_w_gate").shape[0] if g("shared_w_gate") is not None else 0
         return bind("moe_ffn_forward_grouped", g("x"), g("router_w"), g("router_b"), None, g("w_gate"),

@@ -94,17 +94,23 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode_kernel": ["expert_decode.hip"],
     "mfma_gemm_kernel": ["expert_gemm_mfma.hip", "gemm_common.h"],
-    "mxfp4_gemm_kernel": ["expert_gemm_mxfp4.hip", "gemm_common.h"],
+    "lowbit_gemm_kernel": ["expert_gemm_lowbit.hip", "gemm_common.h"],
 }
 COMMON_SOURCES = ["device_common.h", "moe_internal.h"]
 
 
-def source_digest(kernel: str) -> str:
-    """sha256 over the source files a kernel family is compiled from."""
-    fam = next(k for k in KERNEL_SOURCES if kernel.startswith(k))
+def source_digest(kernel: str):
+    """sha256 over the source files a kernel family is compiled from (None
+    for a kernel this tree no longer builds)."""
+    fam = next((k for k in KERNEL_SOURCES if kernel.startswith(k)), None)
+    if fam is None:
+        return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[fam] + COMMON_SOURCES:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        path = os.path.join(CSRC, f)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
     return h.hexdigest()
 
 

@@ -145,7 +145,7 @@ def test_mxfp4_argument_checks(lib):
     assert call(codes=None) == M.MOE_ERR_INVALID_ARG
     # one expert's codes must stay under 2^32 bytes (32-bit offsets in the kernels)
     assert call(d=65536, F=131072) == M.MOE_ERR_UNSUPPORTED
-    assert b"2^33" in lib.moe_last_error_detail()
+    assert b"2^32" in lib.moe_last_error_detail()
 
 def test_block_workspace_and_argument_checks(lib):
     n = lib.moe_ffn_workspace_bytes
@@ -172,3 +172,21 @@ def test_block_workspace_and_argument_checks(lib):
     # T = 0 is a no-op for blocks too
     assert lib.moe_block_forward(ctypes.byref(with_norm), None, None, None, None, None, None, None, None, None,
                                  0, 64, 64, 8, 2, 1.702, 7.0, None, M.MOE_BF16, 0, 0, None, None) == M.MOE_OK
+
+
+def test_affine_argument_checks(lib):
+    def call(bits=4, d=128, F=64, drop=None, experts=True):
+        ex = M.AffineExperts(bits, *[FAKE] * 9)
+        if drop:
+            setattr(ex, drop, None)
+        need = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0)
+        return lib.moe_block_forward_grouped_affine(
+            None, ctypes.byref(ex) if experts else None, FAKE, FAKE, None, None, None, None, None, None, None,
+            None, 0, 16, d, F, 8, 2, 2, 1, 1, 1.0, 0, 1, 1.702, 7.0, FAKE2, FAKE + (1 << 36), need, None, None)
+    assert call(experts=False) == M.MOE_ERR_INVALID_ARG
+    assert call(bits=5) == M.MOE_ERR_UNSUPPORTED
+    assert call(bits=8, d=96) == M.MOE_ERR_UNSUPPORTED       # 8-bit groups of 64
+    assert call(bits=4, F=48) == M.MOE_ERR_UNSUPPORTED       # 4-bit groups of 32
+    assert call(drop="down_biases") == M.MOE_ERR_INVALID_ARG
+    assert b"biases" in lib.moe_last_error_detail()
+    assert call(drop="up_q") == M.MOE_ERR_INVALID_ARG

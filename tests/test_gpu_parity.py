@@ -240,3 +240,25 @@ def test_block_residual_only_and_norm_only():
     scale = float(full.float().abs().max())
     assert float((norm_only.float() - (full.float() - x)).abs().max()) <= 2 ** -7 * scale
     assert float((norm_only.float() - plain.float()).abs().max()) > 1e-2  # the norm changes the layer
+
+
+# --- affine group-quantized routed experts (INT4 groups of 32, INT8 groups of 64) ----
+
+AFFINE_SMALL = [
+    W.GLM4_MOE_LITE_INT4.scaled(T=300, d=256, d_ff=192, E=64, k=6, d_ff_shared=128, name="int4_small"),
+    W.GLM4_MOE_LITE_INT8.scaled(T=300, d=256, d_ff=192, E=64, k=6, d_ff_shared=128, name="int8_small"),
+    # K = 160 / 96: not a multiple of 64, the general kernel with a K tail
+    W.GLM4_MOE_LITE_INT4.scaled(T=200, d=160, d_ff=96, E=16, k=4, n_group=4, topk_group=2, d_ff_shared=0,
+                                name="int4_ragged_k_no_shared"),
+    W.GLM4_MOE_LITE_INT8.scaled(T=5, d=512, d_ff=128, E=16, k=4, n_group=4, topk_group=2, d_ff_shared=64,
+                                name="int8_T5"),
+    W.GLM4_MOE_LITE_INT4.scaled(T=150, d=256, d_ff=128, E=16, k=4, n_group=4, topk_group=2, d_ff_shared=64,
+                                block=True, name="int4_block"),
+]
+AFFINE_CASES = list(W.QUANTIZED) + AFFINE_SMALL
+
+
+@pytest.mark.parametrize("w", AFFINE_CASES, ids=[w.name for w in AFFINE_CASES])
+def test_affine_experts(w):
+    _run_and_check(w, n_out_tokens=256 if w.T > 256 else w.T)
+
