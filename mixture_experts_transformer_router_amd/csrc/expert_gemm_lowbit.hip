@@ -379,9 +379,14 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
     } else if constexpr (CB == 4) {
       // elements 2p, 2p + 1: the low and high nibble of byte p of word s,
       // i.e. byte p of the word's low and high nibbles spread to bytes
+      // (the high nibbles stay in place, 16 times their value, and take
+      // scale / 16; the masks are opaque so that each byte converts with
+      // one v_cvt_f32_ubyte<p> instead of a field extract and a convert)
       const uint32_t w = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
-      const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-      v = pack2(fmaf(scf[j], ubyte(lo, p), sbi[j]), fmaf(scf[j], ubyte(hi, p), sbi[j]));
+      uint32_t lo, hi16;
+      asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+      asm("v_and_b32 %0, 0xf0f0f0f0, %1" : "=v"(hi16) : "v"(w));
+      v = pack2(fmaf(scf[j], ubyte(lo, p), sbi[j]), fmaf(scf[j] * 0.0625f, ubyte(hi16, p), sbi[j]));
     } else {
       // elements 2p, 2p + 1: bytes 2 (p % 2), +1 of word p / 2 of step s's 8 bytes
       const u32x4_t& c = s < 2 ? cw[j] : cw2[j];
