@@ -21,6 +21,11 @@ MoE layers of GPT-OSS and GLM4-MoE-Lite):
   [OCP-MX]  OCP Microscaling Formats (MX) v1.0 specification (not on the
             pages; it defines the e2m1 element and e8m0 scale the MXFP4 name
             on [GGUF] refers to).
+  [MXFP8]   the same page's quantizationParams names MXFP8 (groups of 32,
+            8 bits) as a quantization mode; [OCP-MX] defines the E4M3
+            element, the e8m0 scale and the conversion of a block of 32
+            values (scale exponent = floor(log2 of the block's largest
+            magnitude) - 8, elements rounded to nearest-even E4M3).
   [GLM-Q]   the same glm4_moe_lite.go page on quantized experts:
             SwitchMLP (GatherQMM with weight, scales and biases, group size,
             bits, mode), supportsGatherQMM (affine, 4 or 8 bits),
@@ -54,6 +59,12 @@ reason in the design notes of this repository):
     definition) and its output is added to x.  The norm's output is an array
     of the layer's element type (MLX arrays keep their dtype), so the layer
     sees it rounded to nearest-even bf16 (fp32).
+  * MXFP8 activations (act_quant = "mxfp8", for MXFP4 experts on the
+    gfx950 scaled MFMA): the rows entering each expert and the hidden
+    activation h, as a bf16 array, are converted to MXFP8 by the [OCP-MX]
+    block conversion along the input dimension; elements beyond the E4M3
+    range saturate to +-448; a block holding a NaN or an infinity gets the
+    NaN scale (255); an all-zero block gets scale byte 0.
 """
 from __future__ import annotations
 
@@ -101,6 +112,72 @@ def e8m0_value(scale: np.ndarray) -> np.ndarray:
     s = np.asarray(scale, dtype=np.int64)
     v = np.ldexp(1.0, (s - 127).astype(np.int32))
     return np.where(s == 255, np.nan, v)
+
+
+def e4m3_value(code: np.ndarray) -> np.ndarray:
+    """Value of an OCP E4M3 code ([OCP-MX]): bit 7 sign, bits 6..3 exponent
+    (bias 7), bits 2..0 mantissa; exponent 0 is subnormal (m/8 * 2^-6);
+    S.1111.111 is NaN; there are no infinities."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int32)))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * v)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of finite float64 values, ties to even; magnitudes
+    at or above the largest normal, 448, give 448 (saturation).  The sign
+    bit is v's sign bit (-0 gives 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    # subnormal range (a < 2^-6): steps of 2^-9, codes 0..8 (8 is 2^-6)
+    q_sub = np.round(a * 512.0)                    # numpy rounds halves to even
+    # normal range: a = f 2^x with f in [0.5, 1); 16 f rounded gives the
+    # implicit bit and 3 mantissa bits (16 carries into the exponent)
+    f, x = np.frexp(a)
+    r = np.round(f * 16.0)
+    q_norm = (x - 1 + 7) * 8 + (r - 8)
+    mag = np.where(a >= 448.0, 0x7E, np.where(a < 2.0 ** -6, q_sub, q_norm))
+    return (mag.astype(np.int64) | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(v: np.ndarray):
+    """MXFP8 conversion of float64 rows [n, K] (K % 32 == 0) in blocks of 32
+    consecutive elements ([OCP-MX] conversion; [MXFP8] group of 32):
+        s = floor(log2(max |v_i|)) - 8   (8 = the E4M3 largest exponent),
+        clamped to the e8m0 range [-127, 127];
+        codes = e4m3_encode(v_i / 2^s), scale byte = s + 127.
+    An all-zero block gets scale byte 0 (zero codes); a block with a NaN or an
+    infinity gets scale byte 255 (NaN) and zero codes.
+    Returns (codes uint8 [n, K], scales uint8 [n, K/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    n, K = v.shape
+    b = v.reshape(n, K // 32, 32)
+    amax = np.max(np.abs(np.where(np.isfinite(b), b, 0.0)), axis=-1)
+    bad = ~np.all(np.isfinite(b), axis=-1)
+    _, x = np.frexp(amax)                              # floor(log2 amax) = x - 1 for amax > 0
+    s = np.clip(x - 1 - 8, -127, 127)
+    s = np.where(amax > 0, s, -127)
+    scaled = np.where(np.isfinite(b), b, 0.0) / np.ldexp(1.0, s.astype(np.int32))[..., None]
+    codes = e4m3_encode(scaled)
+    codes = np.where(bad[..., None], np.uint8(0), codes)
+    scales = np.where(bad, 255, s + 127).astype(np.uint8)
+    return codes.reshape(n, K), scales
+
+
+def mxfp8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of MXFP8 rows: e4m3_value(code) * 2^(scale - 127) per block of
+    32 (scale byte 255: NaN)."""
+    codes = np.asarray(codes)
+    n, K = codes.shape
+    return (e4m3_value(codes).reshape(n, K // 32, 32) * e8m0_value(scales)[..., None]).reshape(n, K)
+
+
+def mxfp8_round(v: np.ndarray) -> np.ndarray:
+    """v as the MXFP8 values it converts to (quantize, then dequantize)."""
+    return mxfp8_dequantize(*mxfp8_quantize(v))
 
 
 def affine_decode(q: np.ndarray, scales: np.ndarray, biases: np.ndarray, bits: int, group: int) -> np.ndarray:
@@ -254,11 +331,18 @@ def activation(g, u, act: str, alpha: float, limit: float):
     raise ValueError(act)
 
 
-def expert_mlp(X: np.ndarray, Wg, bg, Wu, bu, Wd, bd, act: str, alpha: float, limit: float) -> np.ndarray:
+def expert_mlp(X: np.ndarray, Wg, bg, Wu, bu, Wd, bd, act: str, alpha: float, limit: float,
+               act_quant: Optional[str] = None) -> np.ndarray:
     """One expert on the rows of X [n, d]:
         g = X Wg^T + bg ; u = X Wu^T + bu ; h = act(g, u) ; y = h Wd^T + bd
     ([MAXTEXT] "MOE EXPERTS": separate gate_proj / up_proj kernels and biases,
-    mlp2 weight and bias; [GLM] SwitchMLP.Forward: gate, up, activation, down)."""
+    mlp2 weight and bias; [GLM] SwitchMLP.Forward: gate, up, activation, down).
+    act_quant "mxfp8": X and the bf16 array h enter their products as MXFP8
+    values (mxfp8_round)."""
+    if act_quant == "mxfp8":
+        X = mxfp8_round(X)
+    elif act_quant is not None:
+        raise ValueError(act_quant)
     g = X @ Wg.T
     u = X @ Wu.T
     if bg is not None:
@@ -266,6 +350,8 @@ def expert_mlp(X: np.ndarray, Wg, bg, Wu, bu, Wd, bd, act: str, alpha: float, li
     if bu is not None:
         u = u + bu[None, :]
     h = activation(g, u, act, alpha, limit)
+    if act_quant == "mxfp8":
+        h = mxfp8_round(round_bf16(h))
     y = h @ Wd.T
     if bd is not None:
         y = y + bd[None, :]
@@ -417,7 +503,7 @@ def experts_forward(arrays: dict, cfg: dict, idx: np.ndarray, w: np.ndarray,
     y = np.zeros((n, k, x.shape[1]), dtype=np.float64)
     for e in np.unique(idx):
         t_sel, j_sel = np.nonzero(idx == e)
-        y[t_sel, j_sel] = expert_mlp(x[t_sel], *W.expert(int(e)), act, alpha, limit)
+        y[t_sel, j_sel] = expert_mlp(x[t_sel], *W.expert(int(e)), act, alpha, limit, cfg.get("act_quant"))
     out = np.zeros((n, x.shape[1]), dtype=np.float64)
     for j in range(k):
         out += w[:, j:j + 1] * y[:, j]

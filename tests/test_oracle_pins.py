@@ -434,3 +434,104 @@ def test_affine_layer_equals_the_dense_layer_of_its_weights():
         c = _cfg(w)
         cd = dict(c, dtype="f32", weights="dense")
         np.testing.assert_array_equal(O.moe_layer(a, c)["out"], O.moe_layer(dense, cd)["out"])
+
+
+# ---- MXFP8 activations ([OCP-MX] E4M3 elements and block conversion) ----------
+
+def test_e4m3_value_equals_torch_float8_e4m3fn_on_every_code():
+    c = np.arange(256, dtype=np.uint8)
+    got = O.e4m3_value(c)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_encode_equals_torch_round_to_nearest_even():
+    # torch converts float32 to float8_e4m3fn rounding to nearest, ties to even; below 464
+    # (the midpoint of 448 and 480) it never leaves the finite range, so it pins every
+    # rounding decision: the code values, the midpoints between neighbours (ties), points
+    # just beside them, and random values over the whole range including subnormals
+    vals = O.e4m3_value(np.arange(256, dtype=np.uint8))
+    fin = np.sort(np.unique(vals[np.isfinite(vals) & (vals >= 0)]))
+    mids = (fin[:-1] + fin[1:]) / 2
+    rng = np.random.default_rng(5)
+    rand = np.ldexp(rng.uniform(1, 2, 20000), rng.integers(-12, 9, 20000))
+    pts = np.concatenate([fin, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), rand, [448.0, 463.99]])
+    pts = pts[pts < 464].astype(np.float32).astype(np.float64)   # float32-exact inputs for torch
+    pts = np.concatenate([pts, -pts])
+    ref = torch.from_numpy(pts.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(pts), ref)
+    # saturation (a reading): beyond 448 the code stays 448
+    np.testing.assert_array_equal(O.e4m3_encode(np.array([464.0, 480.0, 1e30, -500.0])), [0x7E, 0x7E, 0x7E, 0xFE])
+
+
+def test_mxfp8_golden_points():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "mxfp8_points.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        vals, scale, codes = [part.split() for part in line.split("|")]
+        v = np.zeros((1, 32))
+        for pair in vals:
+            i, x = pair.split(":")
+            v[0, int(i)] = float(x)
+        q, s = O.mxfp8_quantize(v)
+        assert s.shape == (1, 1) and int(s[0, 0]) == int(scale[0]), line
+        for pair in codes:
+            i, c = pair.split(":")
+            assert int(q[0, int(i)]) == int(c, 16), (line, i)
+        n += 1
+    assert n == 11
+
+
+def test_mxfp8_invariants():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((64, 256)) * np.ldexp(1.0, rng.integers(-20, 20, (64, 1)))
+    v = O.round_bf16(v)
+    q, s = O.mxfp8_quantize(v)
+    # blocks are independent and along rows
+    q2, s2 = O.mxfp8_quantize(v[:, 32:64])
+    np.testing.assert_array_equal(q2, q[:, 32:64]); np.testing.assert_array_equal(s2[:, 0], s[:, 1])
+    # scaling by 2^j shifts the scale byte and keeps the codes
+    for j in (-5, 1, 7):
+        qj, sj = O.mxfp8_quantize(np.ldexp(v, j))
+        np.testing.assert_array_equal(qj, q)
+        np.testing.assert_array_equal(sj.astype(int), s.astype(int) + j)
+    # the conversion is idempotent on its own values
+    r = O.mxfp8_dequantize(q, s)
+    qr, sr = O.mxfp8_quantize(r)
+    np.testing.assert_array_equal(O.mxfp8_dequantize(qr, sr), r)
+    # error bound: half an E4M3 step -- 2^-4 relative in the normal range, 2^-10 * 2^s below it --
+    # except the saturated top of each block (at most 448 * 2^s against up to 512 * 2^s)
+    X = np.repeat(np.ldexp(1.0, s.astype(int) - 127), 32, axis=1)
+    sat = np.abs(v) >= 448 * X
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, X * 2.0 ** -10)
+    assert np.all((np.abs(r - v) <= bound) | sat)
+    assert np.all(np.abs(r[sat]) == 448 * X[sat])
+    # the largest element of every block sits in [256, 512) * 2^s before saturation
+    amax = np.abs(v).reshape(64, 8, 32).max(-1)
+    assert np.all((amax >= 256 * X[:, ::32]) & (amax < 512 * X[:, ::32]))
+
+
+def test_mxfp8_layer_rounds_activations_in_both_products():
+    # act_quant only changes what enters the two products: with x and h given as
+    # MXFP8 values the layer is the plain one on those values
+    w = W.GPTOSS_MXFP4.scaled(T=12, d=64, d_ff=64, E=4, k=2, name="pin_mx8")
+    a = I.make_inputs(w)
+    c = _cfg(w)
+    cq = dict(c, act_quant="mxfp8")
+    r, rq = O.moe_layer(a, c), O.moe_layer(a, cq)
+    assert np.array_equal(r["idx"], rq["idx"])                 # routing sees the unquantized x
+    rel = np.abs(r["out"] - rq["out"]).max() / np.abs(r["out"]).max()
+    assert 1e-4 < rel < 0.1                                    # the quantization is visible and small
+    ew = O.ExpertWeights(a, "bf16", "mxfp4")
+    x = O.to_f64(a["x"], "bf16")
+    e = int(rq["idx"][0, 0])
+    Wg, bg, Wu, bu, Wd, bd = ew.expert(e)
+    Xq = O.mxfp8_round(x[:1])
+    g, u = Xq @ Wg.T + bg, Xq @ Wu.T + bu
+    h = O.mxfp8_round(O.round_bf16(O.clipped_swiglu(g, u, 1.702, 7.0)))
+    y = h @ Wd.T + bd
+    np.testing.assert_allclose(O.expert_mlp(x[:1], Wg, bg, Wu, bu, Wd, bd, "clipped_swiglu", 1.702, 7.0, "mxfp8"),
+                               y, rtol=0, atol=0)
