@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block|
-                                glm_int4|glm_int8]
+                                glm_int4|glm_int8|mxfp4_mx8]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
@@ -11,7 +11,9 @@ default workload is the GPT-OSS-20B-shaped decode layer (T=8, d=d_ff=2880,
 E=32, k=4, bf16).  Expert weights rotate over several device copies so that
 successive steps cannot hit the 256 MB last-level cache.  The block_*
 workloads run the same layers as MoE blocks (RMSNorm in front, residual
-after).
+after).  mxfp4_mx8 is the MXFP4 layer with MXFP8 activations on the
+scaled MFMA; its roofline peak is the dense fp8 MFMA rate (the E4M3 operand
+sets the instruction's rate).
 
 `value` is tokens/s over the K timed steps.  `roofline` reports the gate|up
 kernel: algorithmic bytes (decode) or flops (prefill) per launch divided by
@@ -33,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN tokens/s; %HBM BW (T=8) and %MFMA peak (T=8192), E=32 k=4"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 STAGE_GATE_UP = 2
 
 
@@ -43,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm",
-                             "dense_block", "glm_int4", "glm_int8"])
+                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -57,7 +60,8 @@ def workload(name):
     return {"decode": W.GPTOSS_DECODE, "prefill": W.GPTOSS_PREFILL, "mxfp4": W.GPTOSS_MXFP4,
             "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
             "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK,
-            "glm_int4": W.GLM4_MOE_LITE_INT4, "glm_int8": W.GLM4_MOE_LITE_INT8}[name]
+            "glm_int4": W.GLM4_MOE_LITE_INT4, "glm_int8": W.GLM4_MOE_LITE_INT8,
+            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -144,7 +148,7 @@ def main():
     w = workload(args.workload)
     steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
                            "block_decode": 500, "block_glm": 100, "dense_block": 100, "glm_int4": 100,
-                           "glm_int8": 100}[args.workload]
+                           "glm_int8": 100, "mxfp4_mx8": 50}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -193,7 +197,8 @@ def main():
     if args.workload in ("decode", "block_decode"):
         roof = {"bound": "hbm", "achieved": nbytes / gu_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / gu_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        peak = FP8_PEAK_TFLOPS if w.act_quant == "mxfp8" else BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": flops / gu_avg_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(w, args.workload)
     roof["kernel"] = "gate_up"
@@ -214,7 +219,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
+        "dtype": "mxfp8 x mxfp4" if w.act_quant == "mxfp8" else w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "active_experts": n_active, "weight_copies": len(copies), "parallelism": "none"},
         "roofline": roof, "cpu_baseline": cpu,

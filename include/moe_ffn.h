@@ -141,6 +141,50 @@ moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void
                                  void* out, void* workspace, size_t workspace_bytes,
                                  moe_routing_out* routing, hipStream_t stream);
 
+/* GPT-OSS-style MXFP4 layer on the gfx950 scaled MFMA (MXFP8 activations).
+ * Arguments, layouts and routing as moe_ffn_forward_mxfp4; the expert GEMMs
+ * differ: the rows entering gate|up (x) and down (h, after bias and
+ * activation, rounded to bf16) are first converted to MXFP8 as
+ * moe_mxfp8_quantize does (OCP Microscaling Formats v1.0 block conversion;
+ * MXFP8 = 32-element groups of 8 bits in glm4_moe_lite.go
+ * quantizationParams), and v_mfma_scale_f32_32x32x64_f8f6f4 multiplies the
+ * E4M3 activation codes by the e2m1 weight codes with both block scales,
+ * accumulating in fp32.  The result therefore differs from
+ * moe_ffn_forward_mxfp4 by the activation rounding (E4M3 keeps 3 mantissa
+ * bits).  The workspace is moe_ffn_workspace_bytes_mxfp8() bytes.
+ * Requirements beyond moe_ffn_forward_mxfp4 (MOE_ERR_UNSUPPORTED /
+ * MOE_ERR_INVALID_ARG otherwise): d and d_ff multiples of 64,
+ * T * k * max(d, d_ff) rounded up to 128 below 2^32, x 16-byte aligned, the
+ * three scale tensors 4-byte aligned. */
+moe_status moe_ffn_forward_mxfp4_mxfp8(const void* x, const void* router_w, const void* router_b,
+                                       const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                       const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                       const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                       int T, int d, int d_ff, int E, int k, float alpha, float limit, void* out,
+                                       void* workspace, size_t workspace_bytes, moe_routing_out* routing,
+                                       hipStream_t stream);
+
+/* Workspace bytes of moe_ffn_forward_mxfp4_mxfp8 ((size_t)-1 for invalid
+ * sizes, 0 for T == 0).  It adds the MXFP8 copies of x and h to the MXFP4
+ * layer's workspace. */
+size_t moe_ffn_workspace_bytes_mxfp8(int T, int d, int d_ff, int E, int k);
+
+/* MXFP8 conversion of bf16 rows, the activation step of
+ * moe_ffn_forward_mxfp4_mxfp8 (OCP Microscaling Formats v1.0: E4M3 elements,
+ * one e8m0 scale per 32 consecutive elements of a row).
+ *   x      bf16 [rows, cols], device, 16-byte aligned; cols a positive multiple of 32.
+ *   codes  uint8 [rows, cols], device, 16-byte aligned: E4M3 codes.
+ *   scales uint8 [rows, cols/32], device: scale bytes.
+ * Per block of 32 values: s = floor(log2(max |v|)) - 8 clamped to
+ * [-127, 127], scale byte = s + 127, code = v / 2^s rounded to the nearest
+ * E4M3 value, ties to even, magnitudes from 448 up giving 448 (the sign bit
+ * is v's).  An all-zero block gets scale byte 0; a block holding a NaN or an
+ * infinity gets scale byte 255 (NaN) and zero codes.  Enqueued on `stream`;
+ * rows == 0 is a no-op.  The three buffers must not overlap.  Errors:
+ * MOE_ERR_INVALID_ARG (nothing is launched). */
+moe_status moe_mxfp8_quantize(const void* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+
 /* GLM4-MoE-style layer with group-limited routing and optional shared expert
  * (glm4_moe_lite.go: Config, MoEGate.Forward, SharedExperts.Forward, MoE.Forward).
  * Routing per token:

@@ -23,7 +23,7 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16
 }
 
 struct MfmaArgs {
-  const uint16_t* a;          // gate|up: x [T, lda]; down: h [rows, lda]
+  const uint16_t* a;          // gate|up: x [T, lda]; down: h [rows, lda] (MXFP8: E4M3 codes, lda bytes a row)
   int lda;
   const int32_t* row_token;   // gate|up: token of each sorted row; down: nullptr
   const uint16_t* w0;         // dense [E, N, K] (down, or gate)
@@ -32,6 +32,7 @@ struct MfmaArgs {
   const uint8_t* s0;          // [E, N, K / 32], affine bf16 [E, N, K / group]
   const uint8_t* c1;
   const uint8_t* s1;
+  const uint8_t* as;          // MXFP8 activations: e8m0 scales [rows, lda / 32] of the codes at a
   const uint16_t* qb0;        // affine: bf16 biases [E, N, K / group] of c0 / c1
   const uint16_t* qb1;
   const uint16_t* bias0;      // [E, N] or nullptr

@@ -84,6 +84,13 @@ moe_status check_common(const Layer& L) {
     if ((unsigned long long)L.rows_all() * (L.d > L.F ? L.d : L.F) >= (1ull << 32))
       return fail(MOE_ERR_UNSUPPORTED, "T * k * max(d, d_ff) >= 2^32 with low-bit weights");
   }
+  if (L.mx_act) {
+    // whole 64-k MFMA steps; 32-bit offsets of the MXFP8 activation rows
+    if (L.d % 64 || L.F % 64)
+      return fail(MOE_ERR_UNSUPPORTED, "d = %d and d_ff = %d must be multiples of 64 with MXFP8 activations", L.d, L.F);
+    if ((unsigned long long)L.rows_all() * mx_row_bytes(L.d > L.F ? L.d : L.F) >= (1ull << 32))
+      return fail(MOE_ERR_UNSUPPORTED, "T * k * max(d, d_ff) >= 2^32 with MXFP8 activations");
+  }
   if (L.act != MOE_ACT_CLIPPED_SWIGLU && L.act != MOE_ACT_SILU) return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", L.act);
   if (L.act == MOE_ACT_CLIPPED_SWIGLU) {
     if (!(L.limit > 0.f) || !std::isfinite(L.limit)) return fail(MOE_ERR_INVALID_ARG, "limit = %g must be finite and > 0", (double)L.limit);
@@ -114,6 +121,12 @@ moe_status check_common(const Layer& L) {
       return fail(MOE_ERR_INVALID_ARG, "all affine biases are required");
   } else if (!L.wg || !L.wu || !L.wd) {
     return fail(MOE_ERR_INVALID_ARG, "w_gate, w_up and w_down are required");
+  }
+  if (L.mx_act) {
+    if (reinterpret_cast<uintptr_t>(L.x) % 16) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned with MXFP8 activations");
+    const uintptr_t sc = reinterpret_cast<uintptr_t>(L.wg_scales) | reinterpret_cast<uintptr_t>(L.wu_scales) |
+                         reinterpret_cast<uintptr_t>(L.wd_scales);
+    if (sc % 4) return fail(MOE_ERR_INVALID_ARG, "the scale tensors must be 4-byte aligned with MXFP8 activations");
   }
   const size_t xbytes = (size_t)L.T * L.d * L.elt();
   if (overlaps(L.out, xbytes, L.x, xbytes)) return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
@@ -152,8 +165,9 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   // Expert stages: weight streaming on MFMA for a few tokens (every expert
   // then holds at most kDecodeMaxTokens rows), grouped MFMA GEMMs for bf16 /
   // MXFP4 otherwise, vector-ALU tiles for fp32.
-  enum { kDecode, kMfma, kLowbit, kTiled } path;
+  enum { kDecode, kMfma, kLowbit, kMx, kTiled } path;
   if (L.dt == MOE_F32) path = kTiled;
+  else if (L.mx_act) path = kMx;
   else if (lowbit_format(L.wfmt)) path = kLowbit;
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
@@ -162,17 +176,27 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   const bool shared_dense = path == kLowbit && L.has_shared();
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
-    e = path == kDecode ? launch_gate_up_decode(L, W, s)
-        : path == kMfma ? launch_gate_up_mfma(L, W, s)
-        : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
+    if (path == kMx) {
+      e = launch_mx_quant(L.x, L.d, L.T, L.d, W.xq, W.xs, mx_row_bytes(L.d), s);
+      if (e == hipSuccess) e = launch_gate_up_mx(L, W, s);
+    } else {
+      e = path == kDecode ? launch_gate_up_decode(L, W, s)
+          : path == kMfma ? launch_gate_up_mfma(L, W, s)
+          : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
+    }
     if (e == hipSuccess && shared_dense) e = launch_gate_up_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
     StageTimer tm(s, MOE_STAGE_DOWN);
-    e = path == kDecode ? launch_down_decode(L, W, s)
-        : path == kMfma ? launch_down_mfma(L, W, s)
-        : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
+    if (path == kMx) {
+      e = launch_mx_quant(W.h, L.F_max(), L.rows_all(), L.F, W.hq, W.hs, mx_row_bytes(L.F), s);
+      if (e == hipSuccess) e = launch_down_mx(L, W, s);
+    } else {
+      e = path == kDecode ? launch_down_decode(L, W, s)
+          : path == kMfma ? launch_down_mfma(L, W, s)
+          : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
+    }
     if (e == hipSuccess && shared_dense) e = launch_down_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
@@ -213,6 +237,11 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   W->h = take(rows * (size_t)L.F_max() * L.elt());
   W->y = take(rows * (size_t)L.d * L.elt());
   W->xn = take(L.norm_w ? (size_t)L.T * L.d * L.elt() : 0);
+  const size_t xrow = L.mx_act ? (size_t)mx_row_bytes(L.d) : 0, hrow = L.mx_act ? (size_t)mx_row_bytes(L.F) : 0;
+  W->xq = static_cast<uint8_t*>(take((size_t)L.T * xrow));
+  W->xs = static_cast<uint8_t*>(take((size_t)L.T * xrow / 32));
+  W->hq = static_cast<uint8_t*>(take(rows * hrow));
+  W->hs = static_cast<uint8_t*>(take(rows * hrow / 32));
   return off;
 }
 
@@ -307,6 +336,55 @@ moe_status moe_block_forward_mxfp4(const moe_block* block, const void* x, const 
   if (routing) L.routing = *routing;
   apply_block(L, block);
   return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+size_t moe_ffn_workspace_bytes_mxfp8(int T, int d, int d_ff, int E, int k) {
+  if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E) return (size_t)-1;
+  if ((long long)T * k >= (1ll << 26)) return (size_t)-1;
+  if (T == 0) return 0;
+  Layer L;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k; L.dt = MOE_BF16;
+  L.wfmt = moe::WF_MXFP4; L.mx_act = 1;
+  moe::Work W;
+  return moe::carve_workspace(L, nullptr, &W);
+}
+
+moe_status moe_ffn_forward_mxfp4_mxfp8(const void* x, const void* router_w, const void* router_b,
+                                       const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                       const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                       const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                       int T, int d, int d_ff, int E, int k, float alpha, float limit, void* out,
+                                       void* workspace, size_t workspace_bytes, moe_routing_out* routing,
+                                       hipStream_t stream) {
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b;
+  L.wg_codes = w_gate_codes; L.wg_scales = w_gate_scales; L.bg = b_gate;
+  L.wu_codes = w_up_codes; L.wu_scales = w_up_scales; L.bu = b_up;
+  L.wd_codes = w_down_codes; L.wd_scales = w_down_scales; L.bd = b_down;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
+  L.dt = MOE_BF16; L.wfmt = moe::WF_MXFP4; L.mx_act = 1;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_mxfp8_quantize(const void* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  moe::g_detail[0] = '\0';
+  if (rows < 0) return moe::fail(MOE_ERR_INVALID_ARG, "rows = %d < 0", rows);
+  if (cols < 32 || cols % 32) return moe::fail(MOE_ERR_INVALID_ARG, "cols = %d must be a positive multiple of 32", cols);
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return moe::fail(MOE_ERR_INVALID_ARG, "x, codes and scales are required");
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 16)
+    return moe::fail(MOE_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  const size_t n = (size_t)rows * cols;
+  if (moe::overlaps(codes, n, x, 2 * n) || moe::overlaps(scales, n / 32, x, 2 * n) ||
+      moe::overlaps(codes, n, scales, n / 32))
+    return moe::fail(MOE_ERR_INVALID_ARG, "x, codes and scales must not overlap");
+  const hipError_t e = moe::launch_mx_quant(x, cols, rows, cols, codes, scales, cols, stream);
+  if (e != hipSuccess) return moe::fail(MOE_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return MOE_OK;
 }
 
 moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const void* router_b,

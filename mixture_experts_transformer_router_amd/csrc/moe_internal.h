@@ -32,6 +32,9 @@ constexpr int kRouteSplitK = 16;
 constexpr int kTileM = 64;
 // Rows per M-tile of the MFMA grouped GEMMs.
 constexpr int kTileMBig = 256;
+// Bytes of one MXFP8 activation row of K elements in the workspace: whole
+// 128-element stages of the scaled-MFMA GEMMs, zero codes past K.
+inline int mx_row_bytes(int K) { return (K + 127) / 128 * 128; }
 // Upper bound on the number of 256-row tiles of a call.
 inline int max_big_tiles(int rows_all, int E_all) { return (rows_all + kTileMBig - 1) / kTileMBig + E_all; }
 
@@ -76,6 +79,9 @@ struct Layer {
   const void* norm_w = nullptr;
   float eps = 0.f;
   const void* x_resid = nullptr;
+  // MXFP4 experts on the scaled MFMA: the expert GEMMs' activation operands
+  // (x rows, h) are converted to MXFP8 first
+  int mx_act = 0;
 
   bool has_shared() const { return sh_wg != nullptr; }
   int n_experts_all() const { return E + (has_shared() ? 1 : 0); }
@@ -101,6 +107,10 @@ struct Work {
   void* h = nullptr;               // [rows_all, F_max] hidden activation (dt)
   void* y = nullptr;               // [rows_all, d] expert outputs (dt)
   void* xn = nullptr;              // block with a norm: [T, d] normalised rows (dt)
+  uint8_t* xq = nullptr;           // MXFP8 activations: x as E4M3 codes [T, mx_row_bytes(d)]
+  uint8_t* xs = nullptr;           //   and e8m0 scales [T, mx_row_bytes(d) / 32]
+  uint8_t* hq = nullptr;           //   h as codes [rows, mx_row_bytes(d_ff)]
+  uint8_t* hs = nullptr;           //   and scales [rows, mx_row_bytes(d_ff) / 32]
 };
 
 // Byte size of the workspace and the layout of its buffers (ws == nullptr:
@@ -124,6 +134,13 @@ hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s);
 // the dense bf16 GEMMs restricted to the shared expert's tiles
 hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s);
+// MXFP8 activations times MXFP4 weights on the scaled MFMA
+hipError_t launch_gate_up_mx(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_down_mx(const Layer& L, const Work& W, hipStream_t s);
+// MXFP8 conversion of R bf16 rows of K elements (row stride lds elements)
+// into codes [R, ldq] and scales [R, ldq / 32]; blocks past K get zero codes
+// and scale byte 0.  K % 32 == 0, ldq % 32 == 0, ldq >= K.
+hipError_t launch_mx_quant(const void* src, int lds, int R, int K, uint8_t* q, uint8_t* sc, int ldq, hipStream_t s);
 hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_rmsnorm(const Layer& L, const Work& W, hipStream_t s);
 

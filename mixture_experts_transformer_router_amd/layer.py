@@ -30,7 +30,10 @@ def block_of(w: Workload, t: dict):
 def workspace_for(w: Workload, device="cuda") -> torch.Tensor:
     dt = moe_ffn.MOE_F32 if w.dtype == "f32" else moe_ffn.MOE_BF16
     blk = moe_ffn.MoeBlock(1, w.norm_eps, 1) if w.block else None  # sizes only
-    n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared, block=blk)
+    if w.act_quant == "mxfp8":
+        n = moe_ffn.workspace_bytes_mxfp8(w.T, w.d, w.d_ff, w.E, w.k)
+    else:
+        n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared, block=blk)
     return moe_ffn.alloc_workspace(n, device)
 
 
@@ -59,6 +62,14 @@ def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=No
             shared_w_gate=t.get("shared_w_gate"), shared_w_up=t.get("shared_w_up"),
             shared_w_down=t.get("shared_w_down"), out=out, workspace=workspace, routing=routing,
             stream=stream, block=block)
+    if w.act_quant == "mxfp8":
+        if w.weights != "mxfp4" or w.block:
+            raise ValueError("MXFP8 activations are implemented for the plain MXFP4 layer")
+        return moe_ffn.forward_mxfp4_mxfp8(
+            t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),
+            t["w_up_codes"], t["w_up_scales"], t.get("b_up"), t["w_down_codes"], t["w_down_scales"],
+            t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
+            routing=routing, stream=stream)
     if w.weights == "mxfp4":
         return moe_ffn.forward_mxfp4(
             t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),

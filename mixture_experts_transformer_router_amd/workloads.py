@@ -33,6 +33,9 @@ class Workload:
     k: int
     dtype: str                 # "f32" | "bf16" (activations, dense weights, biases, out)
     weights: str = "dense"     # "dense" | "mxfp4" | "affine4" (groups of 32) | "affine8" (groups of 64)
+    # "mxfp8": the expert GEMMs' activation operands are converted to MXFP8
+    # (MXFP4 weights on the gfx950 scaled MFMA)
+    act_quant: Optional[str] = None
     routing: str = "gptoss"    # "gptoss" (top-k over logits, softmax over selected) | "grouped"
     act: str = "clipped_swiglu"  # "clipped_swiglu" | "silu"
     alpha: float = 1.702
@@ -117,4 +120,9 @@ GLM4_DENSE_BLOCK = Workload(
     routed_scaling_factor=1.0, score="softmax", router_bias="none", expert_bias=False, block=True)
 BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK, GLM4_DENSE_BLOCK)
 
-BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED}
+# The MXFP4 layer with MXFP8 activations (OCP MX E4M3, groups of 32, the
+# MXFP8 mode of glm4_moe_lite.go quantizationParams) on the scaled MFMA.
+GPTOSS_MXFP4_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp4_mxfp8act_T4096_d2880_E32_k4", act_quant="mxfp8")
+MX_ACT = (GPTOSS_MXFP4_MX8,)
+
+BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED + MX_ACT}

@@ -11,7 +11,8 @@ Rules (same on every workload):
   * permutation: expert offsets and sorted pairs re-derived by the oracle
     from the GPU's own indices, bit-exact;
   * outputs: max |gpu - ref| <= tol * max |ref| over the checked tokens, with
-    tol = 1e-4 for fp32 layers and 2e-2 for bf16 / MXFP4 layers; every output
+    tol = 1e-4 for fp32 layers and 2e-2 for bf16 / MXFP4 / MXFP8-activation
+    layers (the oracle rounds the activations to MXFP8 the same way); every output
     element must have been written (the output is pre-filled with NaN).
 """
 from __future__ import annotations
@@ -28,7 +29,7 @@ def cfg_of(w, e_score_bias=None) -> dict:
     c = dict(dtype=w.dtype, weights=w.weights, routing=w.routing, act=w.act, alpha=w.alpha,
              limit=w.limit, k=w.k, E=w.E, n_group=w.n_group, topk_group=w.topk_group,
              norm_topk_prob=w.norm_topk_prob, routed_scaling_factor=w.routed_scaling_factor,
-             score=w.score, block=w.block, norm_eps=w.norm_eps)
+             score=w.score, block=w.block, norm_eps=w.norm_eps, act_quant=w.act_quant)
     if e_score_bias is not None:
         c["e_score_bias"] = np.asarray(e_score_bias, dtype=np.float64)
     return c

@@ -190,3 +190,37 @@ def test_affine_argument_checks(lib):
     assert call(drop="down_biases") == M.MOE_ERR_INVALID_ARG
     assert b"biases" in lib.moe_last_error_detail()
     assert call(drop="up_q") == M.MOE_ERR_INVALID_ARG
+
+
+def test_mxfp8_activation_workspace_and_argument_checks(lib):
+    nw = lib.moe_ffn_workspace_bytes_mxfp8
+    plain = lib.moe_ffn_workspace_bytes(4096, 2880, 2880, 32, 4, M.MOE_BF16, 0)
+    need = nw(4096, 2880, 2880, 32, 4)
+    # x and h as codes (rows padded to 128 bytes) plus a scale byte per 32
+    assert need >= plain + (4096 + 4096 * 4) * 2944 * 33 // 32
+    assert nw(0, 64, 64, 8, 2) == 0
+    assert nw(8, 64, 64, 300, 2) == ctypes.c_size_t(-1).value
+
+    def call(d=128, F=128, T=16, x=FAKE, scales=FAKE, wsb=None):
+        n = nw(T, d, F, 8, 2)
+        return lib.moe_ffn_forward_mxfp4_mxfp8(x, FAKE, None, FAKE, scales, None, FAKE, FAKE, None, FAKE, FAKE,
+                                               None, T, d, F, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36),
+                                               n if wsb is None else wsb, None, None)
+    assert call(d=96) == M.MOE_ERR_UNSUPPORTED                 # whole 64-k MFMA steps
+    assert b"64" in lib.moe_last_error_detail()
+    assert call(F=160) == M.MOE_ERR_UNSUPPORTED
+    assert call(scales=FAKE + 2) == M.MOE_ERR_INVALID_ARG      # 4-byte aligned scale tensors
+    assert call(x=FAKE + 8) == M.MOE_ERR_INVALID_ARG           # 16-byte aligned x
+    # the MXFP4 layer's workspace is too small for the MXFP8 copies
+    assert call(wsb=lib.moe_ffn_workspace_bytes(16, 128, 128, 8, 2, M.MOE_BF16, 0)) == M.MOE_ERR_WORKSPACE
+    assert call(T=0) == M.MOE_OK
+
+
+def test_mxfp8_quantize_argument_checks(lib):
+    q = lib.moe_mxfp8_quantize
+    assert q(FAKE, 4, 48, FAKE2, FAKE2 + (1 << 30), None) == M.MOE_ERR_INVALID_ARG      # cols % 32
+    assert q(FAKE, -1, 64, FAKE2, FAKE2 + (1 << 30), None) == M.MOE_ERR_INVALID_ARG
+    assert q(None, 4, 64, FAKE2, FAKE2 + (1 << 30), None) == M.MOE_ERR_INVALID_ARG
+    assert q(FAKE + 8, 4, 64, FAKE2, FAKE2 + (1 << 30), None) == M.MOE_ERR_INVALID_ARG  # alignment
+    assert q(FAKE, 4, 64, FAKE + 64, FAKE2, None) == M.MOE_ERR_INVALID_ARG              # codes overlap x
+    assert q(None, 0, 64, None, None, None) == M.MOE_OK

@@ -262,3 +262,79 @@ AFFINE_CASES = list(W.QUANTIZED) + AFFINE_SMALL
 def test_affine_experts(w):
     _run_and_check(w, n_out_tokens=256 if w.T > 256 else w.T)
 
+
+
+# --- MXFP4 weights x MXFP8 activations on the scaled MFMA -----------------------------
+
+MX_CASES = [
+    W.GPTOSS_MXFP4_MX8,
+    # K in 128-wide stages: d = 256 two stages, d_ff = 192 one and a half
+    W.GPTOSS_MXFP4_MX8.scaled(T=150, d=256, d_ff=192, E=8, k=2, name="mx8_small"),
+    # one token; gate|up one whole stage, down one half stage
+    W.GPTOSS_MXFP4_MX8.scaled(T=1, d=128, d_ff=64, E=32, k=4, name="mx8_T1"),
+    # several row tiles per expert, 4.5 / 3.5 stages (steady pairs, then the tail)
+    W.GPTOSS_MXFP4_MX8.scaled(T=600, d=576, d_ff=448, E=4, k=2, name="mx8_many_tiles"),
+    # k = E; gate|up a single half stage
+    W.GPTOSS_MXFP4_MX8.scaled(T=70, d=64, d_ff=320, E=6, k=6, name="mx8_k_equals_E"),
+    # few tokens, long K (8 stages), N ragged against the 256-column tiles
+    W.GPTOSS_MXFP4_MX8.scaled(T=9, d=1024, d_ff=320, E=8, k=3, name="mx8_T9_long_k"),
+]
+
+
+@pytest.mark.parametrize("w", MX_CASES, ids=[w.name for w in MX_CASES])
+def test_mxfp8_activation_layer(w):
+    _run_and_check(w, n_out_tokens=256 if w.T > 256 else w.T)
+
+
+def test_mxfp8_quantize_matches_oracle_bit_exactly():
+    # the activation step alone: every code and scale byte must equal the oracle's
+    rng = np.random.default_rng(11)
+    rows, cols = 96, 320
+    v = rng.standard_normal((rows, cols)) * np.ldexp(1.0, rng.integers(-40, 40, (rows, 1)))
+    v[0, :32] = 0.0
+    v[1, 32:64] = -0.0
+    v[2, :32] = np.ldexp(rng.integers(-7, 8, 32).astype(np.float64), -133)   # bf16 subnormals
+    v[3, :] = rng.standard_normal(cols) * 1e37                                 # near the top of bf16
+    # exact E4M3 ties after scaling (max 1.0 -> scale 2^-8): 17/256, 19/256, and subnormal ties
+    v[4, :32] = 0.0
+    v[4, 0], v[4, 1], v[4, 2], v[4, 3], v[4, 4] = 1.0, 17 / 256, -19 / 256, 3 * 2.0 ** -18, 2.0 ** -18
+    v[5, :32] = 1.8125                                                          # saturation at 448
+    bits = I.f32_to_bf16_bits(v.astype(np.float32))
+    bits[6, 5] = 0x7FC0       # NaN
+    bits[7, 40] = 0x7F80      # +inf
+    bits[8, 70] = 0xFF80      # -inf
+    _say(f"[case] mxfp8_quantize rows={rows} cols={cols} seed=11")
+    x = LY.to_device({"x": bits}, DEV)["x"]
+    codes, scales = moe_ffn.mxfp8_quantize(x)
+    torch.cuda.synchronize()
+    ref_c, ref_s = O.mxfp8_quantize(O.bf16_to_f64(bits))
+    np.testing.assert_array_equal(scales.cpu().numpy(), ref_s)
+    np.testing.assert_array_equal(codes.cpu().numpy(), ref_c)
+    assert ref_s[6, 0] == 255 and ref_s[7, 1] == 255 and ref_s[8, 2] == 255 and ref_s[0, 0] == 0
+
+
+def test_mxfp8_activation_nan_scale():
+    # a NaN weight scale: the gate block's NaN reaches h, whose MXFP8 block then
+    # takes the NaN scale, so every output of those tokens is NaN; a NaN down
+    # block makes one output column NaN.  Elsewhere the oracle's values.
+    w = W.GPTOSS_MXFP4_MX8.scaled(T=150, d=256, d_ff=192, E=8, k=2, name="mx8_nan_scale")
+    a = I.make_inputs(w)
+    a["w_gate_scales"] = a["w_gate_scales"].copy()
+    a["w_gate_scales"][3, 5, 1] = 255
+    a["w_down_scales"] = a["w_down_scales"].copy()
+    a["w_down_scales"][6, 10, 4] = 255
+    _say(f"[case] {w.name} T={w.T} d={w.d} F={w.d_ff} E={w.E} k={w.k} seed={w.seed}")
+    t = LY.to_device(a, DEV)
+    out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, r = LY.run(w, t, out=out, routing=True)
+    torch.cuda.synchronize()
+    cfg = cfg_of(w)
+    g_idx = r["topk_idx"].cpu().numpy().astype(np.int64)
+    logits, _, _ = O.route(a, cfg)
+    ref = O.experts_forward(a, cfg, g_idx, O.forced_weights(logits, g_idx, cfg))
+    got = out.float().cpu().numpy().astype(np.float64)
+    nan_ref = np.isnan(ref)
+    assert nan_ref.all(axis=1).any() and nan_ref[~nan_ref.all(axis=1), 10].any()
+    np.testing.assert_array_equal(np.isnan(got), nan_ref)
+    fin = ~nan_ref
+    assert np.abs(got[fin] - ref[fin]).max() <= 2e-2 * np.abs(ref[fin]).max()
