@@ -160,6 +160,9 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   {
     StageTimer tm(s, MOE_STAGE_PERMUTE);
     e = launch_permute(L, W, s);
+    // MXFP8 activations: x's conversion is independent of the routing; it is
+    // timed with this stage so that the gate|up stage is the GEMM alone
+    if (e == hipSuccess && L.mx_act) e = launch_mx_quant(L.x, L.d, L.T, L.d, W.xq, W.xs, mx_row_bytes(L.d), s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
   // Expert stages: weight streaming on MFMA for a few tokens (every expert
@@ -177,8 +180,7 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     if (path == kMx) {
-      e = launch_mx_quant(L.x, L.d, L.T, L.d, W.xq, W.xs, mx_row_bytes(L.d), s);
-      if (e == hipSuccess) e = launch_gate_up_mx(L, W, s);
+      e = launch_gate_up_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_gate_up_decode(L, W, s)
           : path == kMfma ? launch_gate_up_mfma(L, W, s)

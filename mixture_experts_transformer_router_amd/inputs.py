@@ -95,6 +95,21 @@ def _mxfp4(rng, E, rows, cols, lo, hi):
     return codes, scales
 
 
+def _mxfp8(rng, E, rows, cols, lo, hi):
+    """E4M3 codes (sign, exponent field 3..12, mantissa uniform; never the NaN
+    code) and e8m0 scale bytes 127 + [lo, hi] per 32 elements."""
+    assert cols % 32 == 0
+    codes = np.empty((E, rows, cols), dtype=np.uint8)
+    scales = np.empty((E, rows, cols // 32), dtype=np.uint8)
+    for e in range(E):
+        sign = rng.integers(0, 2, size=(rows, cols), dtype=np.uint8)
+        expo = rng.integers(3, 13, size=(rows, cols), dtype=np.uint8)
+        mant = rng.integers(0, 8, size=(rows, cols), dtype=np.uint8)
+        codes[e] = (sign << np.uint8(7)) | (expo << np.uint8(3)) | mant
+        scales[e] = rng.integers(127 + lo, 127 + hi + 1, size=(rows, cols // 32), dtype=np.uint8)
+    return codes, scales
+
+
 def make_inputs(w: Workload, seed: int | None = None) -> dict:
     """Draw every input array of workload `w` (see module docstring for layout)."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
@@ -134,6 +149,15 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         out["w_up_codes"], out["w_up_scales"] = _mxfp4(rng, E, F, d, lo, hi)
         out["b_up"] = bias(E, F)
         out["w_down_codes"], out["w_down_scales"] = _mxfp4(rng, E, d, F, lo, hi)
+        out["b_down"] = bias(E, d)
+    elif w.weights == "mxfp8":
+        assert dt == "bf16"
+        lo, hi = w.mx_scale_exp_lo, w.mx_scale_exp_hi
+        out["w_gate_codes"], out["w_gate_scales"] = _mxfp8(rng, E, F, d, lo, hi)
+        out["b_gate"] = bias(E, F)
+        out["w_up_codes"], out["w_up_scales"] = _mxfp8(rng, E, F, d, lo, hi)
+        out["b_up"] = bias(E, F)
+        out["w_down_codes"], out["w_down_scales"] = _mxfp8(rng, E, d, F, lo, hi)
         out["b_down"] = bias(E, d)
     elif w.weights in ("affine4", "affine8"):
         assert dt == "bf16"

@@ -95,6 +95,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ["expert_decode.hip"],
     "mfma_gemm_kernel": ["expert_gemm_mfma.hip", "gemm_common.h"],
     "lowbit_gemm_kernel": ["expert_gemm_lowbit.hip", "gemm_common.h"],
+    "mx_gemm_kernel": ["expert_gemm_mx.hip", "gemm_common.h"],
 }
 COMMON_SOURCES = ["device_common.h", "moe_internal.h"]
 

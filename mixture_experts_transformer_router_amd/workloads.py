@@ -32,7 +32,7 @@ class Workload:
     E: int
     k: int
     dtype: str                 # "f32" | "bf16" (activations, dense weights, biases, out)
-    weights: str = "dense"     # "dense" | "mxfp4" | "affine4" (groups of 32) | "affine8" (groups of 64)
+    weights: str = "dense"     # "dense" | "mxfp4" | "mxfp8" | "affine4" (groups of 32) | "affine8" (groups of 64)
     # "mxfp8": the expert GEMMs' activation operands are converted to MXFP8
     # (MXFP4 weights on the gfx950 scaled MFMA)
     act_quant: Optional[str] = None
@@ -123,6 +123,9 @@ BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK, GLM4_DENSE_BLOCK)
 # The MXFP4 layer with MXFP8 activations (OCP MX E4M3, groups of 32, the
 # MXFP8 mode of glm4_moe_lite.go quantizationParams) on the scaled MFMA.
 GPTOSS_MXFP4_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp4_mxfp8act_T4096_d2880_E32_k4", act_quant="mxfp8")
-MX_ACT = (GPTOSS_MXFP4_MX8,)
+# MXFP8 expert weights (E4M3 codes, e8m0 scale per 32) with MXFP8 activations.
+GPTOSS_MXFP8_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp8w_mxfp8act_T4096_d2880_E32_k4", weights="mxfp8",
+                                       act_quant="mxfp8", mx_scale_exp_lo=-13, mx_scale_exp_hi=-9)
+MX_ACT = (GPTOSS_MXFP4_MX8, GPTOSS_MXFP8_MX8)
 
 BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED + MX_ACT}

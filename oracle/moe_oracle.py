@@ -362,7 +362,8 @@ class ExpertWeights:
     """Access to one layer's stacked expert weights, decoded to float64 per expert.
 
     `arrays` holds the stored inputs: w_gate/w_up/w_down (bf16 bits or f32) or
-    their MXFP4 (codes, scales) pairs, and b_gate/b_up/b_down (or None)."""
+    their MXFP4 / MXFP8 (codes, scales) pairs or affine (codes, scales,
+    biases), and b_gate/b_up/b_down (or None)."""
 
     def __init__(self, arrays: dict, dtype: str, weights: str):
         self.a = arrays
@@ -372,6 +373,8 @@ class ExpertWeights:
     def _mat(self, name: str, e: int) -> np.ndarray:
         if self.weights == "mxfp4":
             return mxfp4_decode(self.a[name + "_codes"][e], self.a[name + "_scales"][e])
+        if self.weights == "mxfp8":
+            return mxfp8_dequantize(self.a[name + "_codes"][e], self.a[name + "_scales"][e])
         if self.weights in ("affine4", "affine8"):
             bits = 4 if self.weights == "affine4" else 8
             group = 32 if bits == 4 else 64

@@ -535,3 +535,24 @@ def test_mxfp8_layer_rounds_activations_in_both_products():
     y = h @ Wd.T + bd
     np.testing.assert_allclose(O.expert_mlp(x[:1], Wg, bg, Wu, bu, Wd, bd, "clipped_swiglu", 1.702, 7.0, "mxfp8"),
                                y, rtol=0, atol=0)
+
+
+def test_mxfp8_weight_layer_equals_the_dense_layer_of_its_weights():
+    # MXFP8 weights are E4M3 values times powers of two: exact in float32, so a float32
+    # dense layer holding the decoded weights is the same layer through the pinned dense path
+    w = W.GPTOSS_MXFP8_MX8.scaled(T=20, d=64, d_ff=96, E=4, k=2, act_quant=None, name="pin_mxfp8w")
+    a = I.make_inputs(w)
+    ew = O.ExpertWeights(a, "bf16", "mxfp8")
+    dense = {k: v for k, v in a.items() if not k.startswith(("w_gate", "w_up", "w_down"))}
+    for name, pos in (("w_gate", 0), ("w_up", 2), ("w_down", 4)):
+        m = np.stack([ew.expert(e)[pos] for e in range(w.E)])
+        assert np.isfinite(m).all() and np.array_equal(m.astype(np.float32).astype(np.float64), m)
+        dense[name] = m.astype(np.float32)
+    for key in ("x", "router_w", "router_b", "b_gate", "b_up", "b_down"):
+        dense[key] = O.to_f64(a[key], "bf16").astype(np.float32)
+    c = _cfg(w)
+    cd = dict(c, dtype="f32", weights="dense")
+    np.testing.assert_array_equal(O.moe_layer(a, c)["out"], O.moe_layer(dense, cd)["out"])
+    # each decoded value is an E4M3 value times the block's power of two
+    codes, scales = a["w_up_codes"][1], a["w_up_scales"][1]
+    np.testing.assert_array_equal(ew.expert(1)[2], O.e4m3_value(codes) * np.repeat(np.ldexp(1.0, scales.astype(int) - 127), 32, axis=1))
