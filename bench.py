@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block|
-                                glm_int4|glm_int8|mxfp4_mx8]
+                                glm_int4|glm_int8|mxfp4_mx8|mxfp8_mx8]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
@@ -11,7 +11,7 @@ default workload is the GPT-OSS-20B-shaped decode layer (T=8, d=d_ff=2880,
 E=32, k=4, bf16).  Expert weights rotate over several device copies so that
 successive steps cannot hit the 256 MB last-level cache.  The block_*
 workloads run the same layers as MoE blocks (RMSNorm in front, residual
-after).  mxfp4_mx8 is the MXFP4 layer with MXFP8 activations on the
+after).  mxfp4_mx8 (mxfp8_mx8) is the MXFP4 (MXFP8) layer with MXFP8 activations on the
 scaled MFMA; its roofline peak is the dense fp8 MFMA rate (the E4M3 operand
 sets the instruction's rate).
 
@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm",
-                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8"])
+                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8", "mxfp8_mx8"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,7 +61,7 @@ def workload(name):
             "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
             "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK,
             "glm_int4": W.GLM4_MOE_LITE_INT4, "glm_int8": W.GLM4_MOE_LITE_INT8,
-            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8}[name]
+            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8, "mxfp8_mx8": W.GPTOSS_MXFP8_MX8}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -74,6 +74,8 @@ def algorithmic_gate_up(w, counts):
     active = [e for e, c in enumerate(counts) if c > 0]
     if w.weights == "mxfp4":
         wbytes_per_expert = 2 * (w.d_ff * w.d // 2 + w.d_ff * w.d // 32)
+    elif w.weights == "mxfp8":
+        wbytes_per_expert = 2 * (w.d_ff * w.d + w.d_ff * w.d // 32)
     elif w.weights in ("affine4", "affine8"):
         bits, group = (4, 32) if w.weights == "affine4" else (8, 64)
         wbytes_per_expert = 2 * (w.d_ff * w.d * bits // 8 + 2 * 2 * w.d_ff * w.d // group)
@@ -148,7 +150,7 @@ def main():
     w = workload(args.workload)
     steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
                            "block_decode": 500, "block_glm": 100, "dense_block": 100, "glm_int4": 100,
-                           "glm_int8": 100, "mxfp4_mx8": 50}[args.workload]
+                           "glm_int8": 100, "mxfp4_mx8": 50, "mxfp8_mx8": 50}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -219,7 +221,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp8 x mxfp4" if w.act_quant == "mxfp8" else w.dtype, "data": "synthetic",
+        "dtype": f"mxfp8 x {w.weights}" if w.act_quant == "mxfp8" else w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "active_experts": n_active, "weight_copies": len(copies), "parallelism": "none"},
         "roofline": roof, "cpu_baseline": cpu,

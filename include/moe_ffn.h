@@ -164,7 +164,23 @@ moe_status moe_ffn_forward_mxfp4_mxfp8(const void* x, const void* router_w, cons
                                        void* workspace, size_t workspace_bytes, moe_routing_out* routing,
                                        hipStream_t stream);
 
-/* Workspace bytes of moe_ffn_forward_mxfp4_mxfp8 ((size_t)-1 for invalid
+/* The same layer with MXFP8 expert weights (the MXFP8 mode of glm4_moe_lite.go
+ * quantizationParams: groups of 32, 8 bits; OCP Microscaling Formats v1.0):
+ *   *_codes  uint8 [E, rows, cols]: E4M3 codes (bit 7 sign, bits 6..3 exponent
+ *            with bias 7, bits 2..0 mantissa; S.1111.111 is NaN);
+ *   *_scales uint8 [E, rows, cols/32]: e8m0 scales as for MXFP4.
+ * Everything else as moe_ffn_forward_mxfp4_mxfp8 (MXFP8 activations, the
+ * scaled MFMA with E4M3 operands on both sides, the same workspace size and
+ * requirements; one expert's codes below 2^32 bytes). */
+moe_status moe_ffn_forward_mxfp8_mxfp8(const void* x, const void* router_w, const void* router_b,
+                                       const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                       const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                       const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                       int T, int d, int d_ff, int E, int k, float alpha, float limit, void* out,
+                                       void* workspace, size_t workspace_bytes, moe_routing_out* routing,
+                                       hipStream_t stream);
+
+/* Workspace bytes of moe_ffn_forward_mxfp4_mxfp8 and moe_ffn_forward_mxfp8_mxfp8 ((size_t)-1 for invalid
  * sizes, 0 for T == 0).  It adds the MXFP8 copies of x and h to the MXFP4
  * layer's workspace. */
 size_t moe_ffn_workspace_bytes_mxfp8(int T, int d, int d_ff, int E, int k);

@@ -1,7 +1,8 @@
 // Grouped expert GEMMs on the gfx950 scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4):
 // MXFP8 activations (E4M3 codes and e8m0 scales from mx_quant_kernel) times
-// MXFP4 expert weights (e2m1 codes and e8m0 scales, OCP Microscaling Formats
-// v1.0), fp32 accumulation.  The block scales are applied by the matrix core.
+// MXFP4 (e2m1) or MXFP8 (E4M3) expert weights with e8m0 scales (OCP
+// Microscaling Formats v1.0), fp32 accumulation.  The block scales are
+// applied by the matrix core.
 //
 //   gate|up:  h[r][f] = act(xq[t] . Wg[e][f] + bg[e][f], xq[t] . Wu[e][f] + bu[e][f])  (t = row_token[r])
 //   down:     y[r][n] = hq[r] . Wd[e][n] + bd[e][n]
@@ -14,8 +15,9 @@
 // of 32 x 32), the tile order, bias and activation epilogue of the bf16 GEMM.
 // K goes in stages of 128 through two LDS buffers per operand, filled by
 // global -> LDS copies a stage ahead: A 256 rows x 128 code bytes (rows
-// swizzled as the bf16 kernel's 64-wide bf16 stages), B 256 rows x 64 code
-// bytes (as its 32-wide stages), and each row's 4 scale bytes of the stage.
+// swizzled as the bf16 kernel's 64-wide bf16 stages), B 256 rows x 64 (e2m1,
+// as its 32-wide stages) or 128 (E4M3) code bytes, and each row's 4 scale
+// bytes of the stage.
 // A stage is two MFMA steps of 64 k.  The activation rows are the quantizer's
 // output: lda (a multiple of 128) bytes a row, zero codes past K, so whole
 // stages are always in bounds; weight copies past a row's end are clamped.
@@ -36,29 +38,44 @@ constexpr int NJ = 4;                    // 32-column results per wavefront
 constexpr int BN = 64 * NJ;              // 256 block columns
 constexpr int BKX = 128;                 // K elements per stage
 constexpr int RA = BM * 8 / kThreads;    // 16-byte A copies per thread and stage (8)
-constexpr int RB = BN * 4 / kThreads;    // 16-byte B copies (4)
 constexpr int RSB = BN * 2 / kThreads;   // B scale dwords (2)
-constexpr int kCopies = RA + RB + 1 + RSB;  // copy instructions per thread and stage (15)
+// weight code bytes of a B row per stage (WB = weight bits: 4 e2m1, 8 E4M3),
+// 16-byte B copies per thread and stage, and copy instructions per stage
+template <int WB> constexpr int b_row_bytes() { return WB * BKX / 8; }
+template <int WB> constexpr int b_copies() { return BN * (b_row_bytes<WB>() / 16) / kThreads; }
+template <int WB> constexpr int n_copies() { return RA + b_copies<WB>() + 1 + RSB; }
+constexpr int kMaxRB = 8;  // array bound for the B copies (b_copies<8>())
 
 // D (32 x 32) += A (32 x 64) * B (64 x 32) with block scales.  Lane
 // l = 32 h + r supplies A row r: code bytes 0..15 hold k = 16 h .. +15 and
-// bytes 16..31 hold k = 32 + 16 h .. +15; B column r: 16 bytes holding
-// k = 32 h .. +31 (element 2i in the low nibble); byte SEL of sa / sb: the
-// scale of A row r / B column r for k = 32 h .. +31.  The other scale bytes
-// are ignored.  Result layout as mfma_32x32x16.
+// bytes 16..31 hold k = 32 + 16 h .. +15; B column r: for E4M3 the same
+// layout, for e2m1 16 bytes holding k = 32 h .. +31 (element 2i in the low
+// nibble); byte SEL of sa / sb: the scale of A row r / B column r for
+// k = 32 h .. +31.  The other scale bytes are ignored.  Result layout as
+// mfma_32x32x16.
 template <int SEL>
 __device__ __forceinline__ f32x16_t mfma_mx(i32x8_t a, i32x4_t b, f32x16_t c, uint32_t sa, uint32_t sb) {
   const i32x8_t b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);  // e2m1 reads 4 registers
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b8, c, 0 /* A: E4M3 */, 4 /* B: E2M1 */, SEL, (int)sa,
                                                          SEL, (int)sb);
 }
+template <int SEL>
+__device__ __forceinline__ f32x16_t mfma_mx(i32x8_t a, i32x8_t b, f32x16_t c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0 /* A: E4M3 */, 0 /* B: E4M3 */, SEL, (int)sa,
+                                                         SEL, (int)sb);
+}
 
-template <bool GATED>
+template <bool GATED, int WB>
 __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
+  constexpr int BRB = b_row_bytes<WB>();      // B code bytes of a row per stage
+  constexpr int RB = b_copies<WB>();          // 16-byte B copies per thread and stage
+  constexpr int kCopies = n_copies<WB>();     // copy instructions per thread and stage
+  constexpr int BCPR = BRB / 16;              // 16-byte chunks of a B row
+  using bfrag_t = std::conditional_t<WB == 8, i32x8_t, i32x4_t>;
   // One LDS variable per stage (the compiler tells copies into one stage
   // from reads of another only by the variable they address).
   __shared__ uint16_t lds_a0[BM * 64], lds_a1[BM * 64];  // 128-byte rows
-  __shared__ uint16_t lds_b0[BN * 32], lds_b1[BN * 32];  // 64-byte rows
+  __shared__ uint16_t lds_b0[BN * BRB / 2], lds_b1[BN * BRB / 2];  // BRB-byte rows
   __shared__ uint32_t lds_sa0[BM], lds_sa1[BM];          // A row r: scale bytes of the stage's 4 blocks
   __shared__ uint32_t lds_sb0[2 * BN], lds_sb1[2 * BN];  // B row r: the two aligned dwords holding them
 
@@ -98,7 +115,8 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
   // ---- copy coordinates.  A round i: wavefront wv fills the 1 KB LDS
   // segment 4 i + wv, 8 rows of 128 bytes; lane l writes slot l % 8 of row
   // 8 (4 i + wv) + l / 8, which holds the logical chunk swz() maps there.
-  // B round i: 16 rows of 64 bytes, slot l % 4 of row 16 (4 i + wv) + l / 4.
+  // B round i: 1024 / BRB rows of BRB bytes, slot l % BCPR of row
+  // (1024 / BRB) (4 i + wv) + l / BCPR.
   uint32_t a_off[RA];  // byte offset of the copied chunk in stage 0
 #pragma unroll
   for (int i = 0; i < RA; ++i) {
@@ -107,19 +125,28 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
     a_off[i] = (uint32_t)a_token(row) * lda + 16u * (uint32_t)chunk;
   }
   const uint32_t sa_off = (uint32_t)a_token(tid) * (lda / 32);  // A scales: thread tid copies row tid
-  const int kb = K / 2;  // code bytes of a weight row
+  const int kb = K * WB / 8;  // code bytes of a weight row
   const size_t e_rows = (size_t)e * N;
   const uint8_t* const code_g = a.c0 + e_rows * kb;
   const uint8_t* const code_u = GATED ? a.c1 + e_rows * kb : code_g;
-  const uint8_t* b_src[RB];
-  uint32_t b_k[RB];  // byte offset of the copied chunk within the row's stage
+  // Copy round i reads the up tensor when its B tile rows r have
+  // r % 64 >= 32, which for these row numbers is i odd (E4M3: 8 rows a
+  // segment) or wv >= 2 (e2m1: 16 rows a segment), so the base is uniform
+  // (written out in copy_m: a lambda called from inside another lambda makes
+  // hipcc's host pass drop the kernel stubs).
+  // (sized by a namespace constant: a local array whose bound is a local
+  // constexpr of the template, captured by a lambda, also makes the host
+  // pass drop the kernel stubs)
+  static_assert(RB <= kMaxRB, "B copy rounds");
+  uint32_t b_off[kMaxRB];  // byte offset of the row from its tensor's expert base
+  uint32_t b_k[kMaxRB];    // byte offset of the copied chunk within the row's stage
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    const int row = 16 * (4 * i + wv) + (lane >> 2);
+    const int row = (1024 / BRB) * (4 * i + wv) + lane / BCPR;
     bool up;
     const int wrow = b_row(row, up);
-    b_src[i] = (up ? code_u : code_g) + (size_t)wrow * kb;
-    b_k[i] = 16u * (uint32_t)((swz<32>(row, lane & 3) - row * 32) >> 3);
+    b_off[i] = (uint32_t)wrow * (uint32_t)kb;
+    b_k[i] = 16u * (uint32_t)((swz<BRB / 2>(row, lane % BCPR) - row * (BRB / 2)) >> 3);
   }
   // B scales: dword q = 256 i + tid of a stage's table is dword q % 2 of the
   // aligned pair that holds B row q / 2's four scale bytes (its scale tensor
@@ -155,8 +182,9 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
       __builtin_amdgcn_global_load_lds(aq + (a_off[m] + (uint32_t)kt * BKX), As + (4 * m + wv) * 512, 16, 0, 0);
     } else if (m < RA + RB) {
       const int i = m - RA;
-      const uint32_t k = min((uint32_t)kt * 64u + b_k[i], (uint32_t)kb - 16u);
-      __builtin_amdgcn_global_load_lds(b_src[i] + k, Bs + (4 * i + wv) * 512, 16, 0, 0);
+      const uint32_t k = min((uint32_t)kt * BRB + b_k[i], (uint32_t)kb - 16u);
+      const bool up = GATED && (WB == 8 ? (i & 1) != 0 : wv >= 2);
+      __builtin_amdgcn_global_load_lds((up ? code_u : code_g) + (b_off[i] + k), Bs + (4 * i + wv) * 512, 16, 0, 0);
     } else if (m == RA + RB) {
       __builtin_amdgcn_global_load_lds(a.as + (sa_off + 4u * (uint32_t)kt), SAs + 64 * wv, 4, 0, 0);
     } else {
@@ -178,8 +206,11 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
   // A fragments are single-buffered: row block i of the next step is read
   // right after the current step's last MFMA on it (the other row blocks'
   // MFMAs cover the read).  B fragments alternate between two sets by step.
+  // E4M3 weights: B fragments single-buffered too (column block j refilled
+  // right after the step's last MFMA on it), for registers
+  constexpr int NBS = WB == 8 ? 1 : 2;
   i32x8_t fa[4];
-  i32x4_t fb[2][NJ];
+  bfrag_t fb[NBS][NJ];
   uint32_t sa[4], sb[NJ], sb_n[NJ];
   // A fragment of row block i for step t
   auto read_a = [&](const uint16_t* As, int t, int i) __attribute__((always_inline)) {
@@ -188,10 +219,16 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
     const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(As + swz<64>(row, 4 * t + 2 + fh));
     fa[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  // B fragment of column block j for step t into set t
+  // B fragment of column block j for step t into set t (E4M3: the one set)
   auto read_b = [&](const uint16_t* Bs, int t, int j) __attribute__((always_inline)) {
     const int row = wn * 128 + 32 * j + fr;
-    fb[t][j] = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(Bs + swz<32>(row, 2 * t + fh)));
+    if constexpr (WB == 8) {
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(Bs + swz<64>(row, 4 * t + fh));
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(Bs + swz<64>(row, 4 * t + 2 + fh));
+      fb[0][j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      fb[t][j] = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(Bs + swz<32>(row, 2 * t + fh)));
+    }
   };
   // scale dword of A row block i / B column block j of a stage
   auto read_sa = [&](const uint32_t* SAs, int i) __attribute__((always_inline)) {
@@ -203,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
   };
   auto mma = [&](int t, int i, int j) __attribute__((always_inline)) {
     if (t == 0) acc[i][j] = mfma_mx<0>(fa[i], fb[0][j], acc[i][j], sa[i], sb[j]);
-    else acc[i][j] = mfma_mx<2>(fa[i], fb[1][j], acc[i][j], sa[i], sb[j]);
+    else acc[i][j] = mfma_mx<2>(fa[i], fb[NBS - 1][j], acc[i][j], sa[i], sb[j]);
   };
 
   const int ktiles = (K + BKX - 1) / BKX;
@@ -259,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         mma(0, i, j);
-        if (i == 0) read_b(Bs, 1, j);
+        if (i == (NBS == 2 ? 0 : 3)) read_b(Bs, 1, j);
         if (j == NJ - 1) read_a(As, 1, i);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -284,10 +321,10 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
         mma(1, i, j);
         const int m = i * NJ + j;
         if (m < kCopies && more) copy_m(kt + 2, As, Bs, SAs, SBs, m);
-        if (i == 0) {
-          read_b(Bs1, 0, j);
-          sb_n[j] = read_sb(SBs1, j);
-        }
+        // more copies than MFMAs (E4M3 weights): the last ones double up
+        if (kCopies > 16 && m >= 32 - kCopies && more) copy_m(kt + 2, As, Bs, SAs, SBs, m + kCopies - 16);
+        if (i == 0) sb_n[j] = read_sb(SBs1, j);
+        if (i == (NBS == 2 ? 0 : 3)) read_b(Bs1, 0, j);
         if (j == NJ - 1) {
           read_a(As1, 0, i);
           sa[i] = read_sa(SAs1, i);
@@ -327,7 +364,8 @@ hipError_t launch_gate_up_mx(const Layer& L, const Work& W, hipStream_t s) {
   m.ldo = L.F_max();
   m.n_tiles = (L.F + BN / 2 - 1) / (BN / 2);
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
-  mx_gemm_kernel<true><<<grid, kThreads, 0, s>>>(m);
+  if (L.wfmt == WF_MXFP8) mx_gemm_kernel<true, 8><<<grid, kThreads, 0, s>>>(m);
+  else mx_gemm_kernel<true, 4><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
 
@@ -344,7 +382,8 @@ hipError_t launch_down_mx(const Layer& L, const Work& W, hipStream_t s) {
   m.ldo = L.d;
   m.n_tiles = (L.d + BN - 1) / BN;
   const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
-  mx_gemm_kernel<false><<<grid, kThreads, 0, s>>>(m);
+  if (L.wfmt == WF_MXFP8) mx_gemm_kernel<false, 8><<<grid, kThreads, 0, s>>>(m);
+  else mx_gemm_kernel<false, 4><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ moe_status check_common(const Layer& L) {
   if (lowbit_format(L.wfmt)) {
     // the low-bit kernels address one expert's codes and the activation
     // rows with 32-bit offsets
-    const unsigned long long code_bytes = (unsigned long long)L.d * L.F * (L.wfmt == WF_AFF8 ? 8 : 4) / 8;
+    const unsigned long long code_bytes = (unsigned long long)L.d * L.F * code_bits(L.wfmt) / 8;
     if (code_bytes >= (1ull << 32))
       return fail(MOE_ERR_UNSUPPORTED, "d * d_ff = %lld: an expert's codes reach 2^32 bytes", (long long)L.d * L.F);
     if ((unsigned long long)L.rows_all() * (L.d > L.F ? L.d : L.F) >= (1ull << 32))
@@ -117,7 +117,7 @@ moe_status check_common(const Layer& L) {
   if (lowbit_format(L.wfmt)) {
     if (!L.wg_codes || !L.wg_scales || !L.wu_codes || !L.wu_scales || !L.wd_codes || !L.wd_scales)
       return fail(MOE_ERR_INVALID_ARG, "all codes and scales are required");
-    if (L.wfmt != WF_MXFP4 && (!L.wg_qbias || !L.wu_qbias || !L.wd_qbias))
+    if ((L.wfmt == WF_AFF4 || L.wfmt == WF_AFF8) && (!L.wg_qbias || !L.wu_qbias || !L.wd_qbias))
       return fail(MOE_ERR_INVALID_ARG, "all affine biases are required");
   } else if (!L.wg || !L.wu || !L.wd) {
     return fail(MOE_ERR_INVALID_ARG, "w_gate, w_up and w_down are required");
@@ -366,6 +366,26 @@ moe_status moe_ffn_forward_mxfp4_mxfp8(const void* x, const void* router_w, cons
   L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
   L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
   L.dt = MOE_BF16; L.wfmt = moe::WF_MXFP4; L.mx_act = 1;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_mxfp8_mxfp8(const void* x, const void* router_w, const void* router_b,
+                                       const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, const void* b_gate,
+                                       const uint8_t* w_up_codes, const uint8_t* w_up_scales, const void* b_up,
+                                       const uint8_t* w_down_codes, const uint8_t* w_down_scales, const void* b_down,
+                                       int T, int d, int d_ff, int E, int k, float alpha, float limit, void* out,
+                                       void* workspace, size_t workspace_bytes, moe_routing_out* routing,
+                                       hipStream_t stream) {
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b;
+  L.wg_codes = w_gate_codes; L.wg_scales = w_gate_scales; L.bg = b_gate;
+  L.wu_codes = w_up_codes; L.wu_scales = w_up_scales; L.bu = b_up;
+  L.wd_codes = w_down_codes; L.wd_scales = w_down_scales; L.bd = b_down;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
+  L.dt = MOE_BF16; L.wfmt = moe::WF_MXFP8; L.mx_act = 1;
   L.out = out;
   if (routing) L.routing = *routing;
   return moe::run(L, workspace, workspace_bytes, stream);

@@ -11,9 +11,11 @@ namespace moe {
 
 // Storage format of the expert weights.
 // WF_AFF4 / WF_AFF8: affine group-quantized codes (4 bits, groups of 32 /
-// 8 bits, groups of 64) with bf16 scales and biases.
-enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2, WF_AFF4 = 3, WF_AFF8 = 4 };
+// 8 bits, groups of 64) with bf16 scales and biases.  WF_MXFP8: E4M3 codes
+// with an e8m0 scale per 32 (only with MXFP8 activations, on the scaled MFMA).
+enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2, WF_AFF4 = 3, WF_AFF8 = 4, WF_MXFP8 = 5 };
 inline bool lowbit_format(int wfmt) { return wfmt >= WF_MXFP4; }
+inline int code_bits(int wfmt) { return wfmt == WF_AFF8 || wfmt == WF_MXFP8 ? 8 : 4; }
 
 // Tokens handled by one block of the permute kernel.  Router blocks cover
 // route_block_tokens() tokens, a divisor of this.

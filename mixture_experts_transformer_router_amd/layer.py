@@ -63,13 +63,13 @@ def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=No
             shared_w_down=t.get("shared_w_down"), out=out, workspace=workspace, routing=routing,
             stream=stream, block=block)
     if w.act_quant == "mxfp8":
-        if w.weights != "mxfp4" or w.block:
-            raise ValueError("MXFP8 activations are implemented for the plain MXFP4 layer")
+        if w.weights not in ("mxfp4", "mxfp8") or w.block:
+            raise ValueError("MXFP8 activations are implemented for the plain MXFP4 / MXFP8 layer")
         return moe_ffn.forward_mxfp4_mxfp8(
             t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),
             t["w_up_codes"], t["w_up_scales"], t.get("b_up"), t["w_down_codes"], t["w_down_scales"],
             t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
-            routing=routing, stream=stream)
+            routing=routing, stream=stream, weights=w.weights)
     if w.weights == "mxfp4":
         return moe_ffn.forward_mxfp4(
             t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),

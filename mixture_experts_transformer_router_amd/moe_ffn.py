@@ -39,7 +39,7 @@ EXPORTED = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp4
             "moe_ffn_profile_enable", "moe_ffn_profile_read", "moe_block_workspace_bytes",
             "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped",
             "moe_block_forward_grouped_affine", "moe_ffn_forward_mxfp4_mxfp8",
-            "moe_ffn_workspace_bytes_mxfp8", "moe_mxfp8_quantize")
+            "moe_ffn_workspace_bytes_mxfp8", "moe_mxfp8_quantize", "moe_ffn_forward_mxfp8_mxfp8")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -110,6 +110,8 @@ def load() -> ctypes.CDLL:
                                         _I, _I, _I, _I, _I, _F, _F, _P, _P, _Z, _P, _P]
     L.moe_ffn_forward_mxfp4_mxfp8.restype = _I
     L.moe_ffn_forward_mxfp4_mxfp8.argtypes = L.moe_ffn_forward_mxfp4.argtypes
+    L.moe_ffn_forward_mxfp8_mxfp8.restype = _I
+    L.moe_ffn_forward_mxfp8_mxfp8.argtypes = L.moe_ffn_forward_mxfp4.argtypes
     L.moe_ffn_workspace_bytes_mxfp8.restype = _Z
     L.moe_ffn_workspace_bytes_mxfp8.argtypes = [_I, _I, _I, _I, _I]
     L.moe_mxfp8_quantize.restype = _I
@@ -251,16 +253,18 @@ def workspace_bytes_mxfp8(T, d, d_ff, E, k) -> int:
 
 def forward_mxfp4_mxfp8(x, router_w, router_b, w_gate_codes, w_gate_scales, b_gate, w_up_codes, w_up_scales,
                         b_up, w_down_codes, w_down_scales, b_down, k, alpha=1.702, limit=7.0, out=None,
-                        workspace=None, routing=False, stream=None):
+                        workspace=None, routing=False, stream=None, weights="mxfp4"):
     """moe_ffn_forward_mxfp4_mxfp8: the MXFP4 layer with MXFP8 activations on the
-    scaled MFMA.  Arguments as forward_mxfp4 (no block form)."""
+    scaled MFMA (weights="mxfp8": moe_ffn_forward_mxfp8_mxfp8, E4M3 weight codes
+    [E, rows, cols]).  Arguments as forward_mxfp4 (no block form)."""
     T, d = x.shape
     E, d_ff = w_gate_codes.shape[0], w_gate_codes.shape[1]
+    entry = {"mxfp4": "moe_ffn_forward_mxfp4_mxfp8", "mxfp8": "moe_ffn_forward_mxfp8_mxfp8"}[weights]
     out = torch.empty_like(x) if out is None else out
     ws = workspace if workspace is not None else alloc_workspace(
         workspace_bytes_mxfp8(T, d, d_ff, E, k), x.device)
     r, rs = _routing(T, k, E, x.device, routing)
-    st = load().moe_ffn_forward_mxfp4_mxfp8(
+    st = getattr(load(), entry)(
         _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w_gate_codes), _ptr(w_gate_scales), _ptr(b_gate),
         _ptr(w_up_codes), _ptr(w_up_scales), _ptr(b_up), _ptr(w_down_codes), _ptr(w_down_scales), _ptr(b_down),
         T, d, d_ff, E, k, alpha, limit, _ptr(out), _ptr(ws), ws.numel(),
@@ -395,8 +399,8 @@ def bound_layer_call(w, t: dict, out: torch.Tensor, workspace: torch.Tensor, str
                     MOE_ACT_SILU if w.act == "silu" else MOE_ACT_CLIPPED_SWIGLU, w.alpha, w.limit,
                     out, MOE_F32 if w.dtype == "f32" else MOE_BF16, workspace, workspace.numel(), rp, s,
                     block=blk)
-    if w.weights == "mxfp4" and getattr(w, "act_quant", None) == "mxfp8":
-        return bind("moe_ffn_forward_mxfp4_mxfp8", g("x"), g("router_w"), g("router_b"), g("w_gate_codes"),
+    if w.weights in ("mxfp4", "mxfp8") and getattr(w, "act_quant", None) == "mxfp8":
+        return bind(f"moe_ffn_forward_{w.weights}_mxfp8", g("x"), g("router_w"), g("router_b"), g("w_gate_codes"),
                     g("w_gate_scales"), g("b_gate"), g("w_up_codes"), g("w_up_scales"), g("b_up"),
                     g("w_down_codes"), g("w_down_scales"), g("b_down"), w.T, w.d, w.d_ff, w.E, w.k,
                     w.alpha, w.limit, out, workspace, workspace.numel(), rp, s)

@@ -12,8 +12,16 @@ Rules (same on every workload):
     from the GPU's own indices, bit-exact;
   * outputs: max |gpu - ref| <= tol * max |ref| over the checked tokens, with
     tol = 1e-4 for fp32 layers and 2e-2 for bf16 / MXFP4 / MXFP8-activation
-    layers (the oracle rounds the activations to MXFP8 the same way); every output
-    element must have been written (the output is pre-filled with NaN).
+    layers; every output element must have been written (the output is
+    pre-filled with NaN);
+  * MXFP8 activations: x converts exactly on both sides (it is bf16), but the
+    E4M3 code of an element of h is a decision taken on a value that the GPU
+    accumulates in fp32 and the oracle in fp64.  Where the oracle's g or u
+    moved by the GPU's accumulation error (H_REL of the sum of the products'
+    magnitudes) would change an element's code, either code is correct; each
+    output's bound grows by what those alternatives can change it (the
+    largest code change times |W_down| and the routing weight), as the
+    routing near-ties are compared on what is unique.
 """
 from __future__ import annotations
 
@@ -23,6 +31,10 @@ import torch
 from oracle import moe_oracle as O
 
 MARGIN = 1e-5
+# Relative accumulation error of g and u on the GPU (fp32 sums of MFMA
+# results that are themselves exact to ~1.2e-4 of the block's sum of product
+# magnitudes), as a fraction of the sum of |products|; used for the h codes.
+H_REL = 3e-4
 
 
 def cfg_of(w, e_score_bias=None) -> dict:
@@ -94,9 +106,43 @@ def check_layer(w, a: dict, gpu_out: torch.Tensor, r: dict, n_out_tokens: int = 
     idx_mix = np.where(use_gpu_choice[:, None], g_idx[toks], o_idx[toks])
     w_mix = np.where(use_gpu_choice[:, None], fw[toks], o_w[toks])
     ref = O.experts_forward(a, cfg, idx_mix, w_mix, tokens=toks)
-    err = np.abs(out[toks] - ref).max()
     scale = np.abs(ref).max()
     tol = tolerance(w)
-    assert err <= tol * scale, f"max|err| = {err:.3e} > {tol} * max|ref| = {tol * scale:.3e}"
+    extra = h_code_slack(a, cfg, idx_mix, w_mix, toks) if cfg.get("act_quant") == "mxfp8" else 0.0
+    excess = np.abs(out[toks] - ref) - extra
+    err = np.abs(out[toks] - ref).max()
+    assert excess.max() <= tol * scale, (f"max|err| - slack = {excess.max():.3e} > {tol} * max|ref| = {tol * scale:.3e} "
+                                         f"(max|err| {err:.3e})")
     return {"tokens_checked": int(toks.size), "near_ties": int(near.size), "set_ties": int(sets_only.sum()),
-            "max_err": float(err), "max_ref": float(scale), "rel": float(err / scale)}
+            "max_err": float(err), "max_ref": float(scale), "rel": float(err / scale),
+            "rel_beyond_slack": float(excess.max() / scale),
+            "max_slack_rel": float(np.max(extra) / scale) if np.ndim(extra) else 0.0}
+
+
+def h_code_slack(a: dict, cfg: dict, idx: np.ndarray, wts: np.ndarray, toks: np.ndarray) -> np.ndarray:
+    """Per output element, how far the output may move because E4M3 codes of h
+    that sit within the accumulation error of a rounding decision can go
+    either way (MXFP8-activation layers; see the module docstring)."""
+    dt = cfg["dtype"]
+    x = O.layer_input(a, cfg, toks)
+    W = O.ExpertWeights(a, dt, cfg.get("weights", "dense"))
+    alpha, limit = cfg.get("alpha", 1.702), cfg.get("limit", 7.0)
+    slack = np.zeros((toks.size, x.shape[1]))
+    for e in np.unique(idx):
+        t_sel, j_sel = np.nonzero(idx == e)
+        Wg, bg, Wu, bu, Wd, bd = W.expert(int(e))
+        X = O.mxfp8_round(x[t_sel])
+        g, u = X @ Wg.T, X @ Wu.T
+        dg, du = H_REL * (np.abs(X) @ np.abs(Wg.T)), H_REL * (np.abs(X) @ np.abs(Wu.T))
+        if bg is not None:
+            g = g + bg
+        if bu is not None:
+            u = u + bu
+        q0 = O.mxfp8_round(O.round_bf16(O.activation(g, u, "clipped_swiglu", alpha, limit)))
+        dev = np.zeros_like(q0)
+        for sg in (-1.0, 1.0):        # the activation is monotone in g and in u: corners bound it
+            for su in (-1.0, 1.0):
+                qc = O.mxfp8_round(O.round_bf16(O.activation(g + sg * dg, u + su * du, "clipped_swiglu", alpha, limit)))
+                dev = np.maximum(dev, np.abs(qc - q0))
+        slack[t_sel] += np.abs(wts[t_sel, j_sel])[:, None] * (dev @ np.abs(Wd.T))
+    return slack

@@ -214,6 +214,14 @@ def test_mxfp8_activation_workspace_and_argument_checks(lib):
     # the MXFP4 layer's workspace is too small for the MXFP8 copies
     assert call(wsb=lib.moe_ffn_workspace_bytes(16, 128, 128, 8, 2, M.MOE_BF16, 0)) == M.MOE_ERR_WORKSPACE
     assert call(T=0) == M.MOE_OK
+    # MXFP8 weights: the same checks
+    n = nw(16, 96, 128, 8, 2)
+    assert lib.moe_ffn_forward_mxfp8_mxfp8(FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None,
+                                           16, 96, 128, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36), n,
+                                           None, None) == M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ffn_forward_mxfp8_mxfp8(FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None,
+                                           16, 128, 128, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36),
+                                           nw(16, 128, 128, 8, 2), None, None) == M.MOE_ERR_INVALID_ARG
 
 
 def test_mxfp8_quantize_argument_checks(lib):

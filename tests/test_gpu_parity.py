@@ -278,6 +278,11 @@ MX_CASES = [
     W.GPTOSS_MXFP4_MX8.scaled(T=70, d=64, d_ff=320, E=6, k=6, name="mx8_k_equals_E"),
     # few tokens, long K (8 stages), N ragged against the 256-column tiles
     W.GPTOSS_MXFP4_MX8.scaled(T=9, d=1024, d_ff=320, E=8, k=3, name="mx8_T9_long_k"),
+    # MXFP8 (E4M3) weights: the full layer, 1.5 / 4.5 stages, a single half stage
+    W.GPTOSS_MXFP8_MX8,
+    W.GPTOSS_MXFP8_MX8.scaled(T=150, d=256, d_ff=192, E=8, k=2, name="mx8w_small"),
+    W.GPTOSS_MXFP8_MX8.scaled(T=600, d=576, d_ff=448, E=4, k=2, name="mx8w_many_tiles"),
+    W.GPTOSS_MXFP8_MX8.scaled(T=70, d=64, d_ff=320, E=6, k=6, name="mx8w_k_equals_E"),
 ]
 
 
