@@ -110,6 +110,21 @@ def _mxfp8(rng, E, rows, cols, lo, hi):
     return codes, scales
 
 
+def _nvfp4(rng, E, rows, cols, lo, hi):
+    """e2m1 codes uniform over the 16 codes, positive E4M3 block scales (one per
+    16 elements) with exponent field in [lo, hi] and any mantissa."""
+    assert cols % 16 == 0
+    codes = np.empty((E, rows, cols // 2), dtype=np.uint8)
+    scales = np.empty((E, rows, cols // 16), dtype=np.uint8)
+    for e in range(E):
+        c = rng.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+        codes[e] = c[:, 0::2] | (c[:, 1::2] << np.uint8(4))
+        expo = rng.integers(lo, hi + 1, size=(rows, cols // 16), dtype=np.uint8)
+        mant = rng.integers(0, 8, size=(rows, cols // 16), dtype=np.uint8)
+        scales[e] = (expo << np.uint8(3)) | mant
+    return codes, scales
+
+
 def make_inputs(w: Workload, seed: int | None = None) -> dict:
     """Draw every input array of workload `w` (see module docstring for layout)."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
@@ -159,6 +174,13 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         out["b_up"] = bias(E, F)
         out["w_down_codes"], out["w_down_scales"] = _mxfp8(rng, E, d, F, lo, hi)
         out["b_down"] = bias(E, d)
+    elif w.weights == "nvfp4":
+        # tensor scales 1.5 * 2^-k: every decoded weight is then a bf16 number
+        assert dt == "bf16"
+        for name, (r_, c_) in (("w_gate", (F, d)), ("w_up", (F, d)), ("w_down", (d, F))):
+            out[name + "_codes"], out[name + "_scales"] = _nvfp4(rng, E, r_, c_, 4, 8)
+            out[name + "_tensor_scale"] = np.float32(1.5 * 2.0 ** -(9 if name != "w_down" else 8))
+            out["b_" + name[2:]] = bias(E, r_)
     elif w.weights in ("affine4", "affine8"):
         assert dt == "bf16"
         bits = 4 if w.weights == "affine4" else 8

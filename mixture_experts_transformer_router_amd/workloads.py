@@ -32,7 +32,7 @@ class Workload:
     E: int
     k: int
     dtype: str                 # "f32" | "bf16" (activations, dense weights, biases, out)
-    weights: str = "dense"     # "dense" | "mxfp4" | "mxfp8" | "affine4" (groups of 32) | "affine8" (groups of 64)
+    weights: str = "dense"     # "dense" | "mxfp4" | "mxfp8" | "nvfp4" | "affine4" (groups of 32) | "affine8" (groups of 64)
     # "mxfp8": the expert GEMMs' activation operands are converted to MXFP8
     # (MXFP4 weights on the gfx950 scaled MFMA)
     act_quant: Optional[str] = None
@@ -127,5 +127,8 @@ GPTOSS_MXFP4_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp4_mxfp8act_T4096_d288
 GPTOSS_MXFP8_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp8w_mxfp8act_T4096_d2880_E32_k4", weights="mxfp8",
                                        act_quant="mxfp8", mx_scale_exp_lo=-13, mx_scale_exp_hi=-9)
 MX_ACT = (GPTOSS_MXFP4_MX8, GPTOSS_MXFP8_MX8)
+# NVFP4 expert weights (e2m1 codes, an E4M3 scale per 16, a tensor scale),
+# decoded to bf16 in registers (quantizationParams: NVFP4 = groups of 16, 4 bits).
+GPTOSS_NVFP4 = GPTOSS_MXFP4.scaled(name="gptoss20b_nvfp4_T4096_d2880_E32_k4", weights="nvfp4")
 
-BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED + MX_ACT}
+BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED + MX_ACT + (GPTOSS_NVFP4,)}

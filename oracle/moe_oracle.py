@@ -26,6 +26,10 @@ MoE layers of GPT-OSS and GLM4-MoE-Lite):
             element, the e8m0 scale and the conversion of a block of 32
             values (scale exponent = floor(log2 of the block's largest
             magnitude) - 8, elements rounded to nearest-even E4M3).
+  [NVFP4]   the same page's quantizationParams names NVFP4 (groups of 16, 4
+            bits, mode nvfp4) without its layout; read as the published
+            NVFP4 definition: e2m1 elements, an E4M3 scale per block of 16
+            and one fp32 scale per tensor.
   [GLM-Q]   the same glm4_moe_lite.go page on quantized experts:
             SwitchMLP (GatherQMM with weight, scales and biases, group size,
             bits, mode), supportsGatherQMM (affine, 4 or 8 bits),
@@ -178,6 +182,21 @@ def mxfp8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def mxfp8_round(v: np.ndarray) -> np.ndarray:
     """v as the MXFP8 values it converts to (quantize, then dequantize)."""
     return mxfp8_dequantize(*mxfp8_quantize(v))
+
+
+def nvfp4_decode(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) -> np.ndarray:
+    """Decode one NVFP4 matrix ([NVFP4]): codes uint8 [rows, cols/2] (element 2i
+    in the low nibble), scales uint8 [rows, cols/16] of E4M3 codes, one per 16
+    consecutive elements of a row, and a float tensor scale:
+        w[r, c] = e2m1(code[r, c]) * e4m3(scale[r, c // 16]) * tensor_scale."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    elem = np.empty((rows, 2 * half), dtype=np.float64)
+    elem[:, 0::2] = e2m1_value(codes & 0x0F)
+    elem[:, 1::2] = e2m1_value(codes >> 4)
+    sc = np.repeat(e4m3_value(scales), 16, axis=1)
+    assert sc.shape == elem.shape
+    return elem * sc * float(tensor_scale)
 
 
 def affine_decode(q: np.ndarray, scales: np.ndarray, biases: np.ndarray, bits: int, group: int) -> np.ndarray:
@@ -375,6 +394,9 @@ class ExpertWeights:
             return mxfp4_decode(self.a[name + "_codes"][e], self.a[name + "_scales"][e])
         if self.weights == "mxfp8":
             return mxfp8_dequantize(self.a[name + "_codes"][e], self.a[name + "_scales"][e])
+        if self.weights == "nvfp4":
+            return nvfp4_decode(self.a[name + "_codes"][e], self.a[name + "_scales"][e],
+                                float(self.a[name + "_tensor_scale"]))
         if self.weights in ("affine4", "affine8"):
             bits = 4 if self.weights == "affine4" else 8
             group = 32 if bits == 4 else 64

@@ -556,3 +556,45 @@ def test_mxfp8_weight_layer_equals_the_dense_layer_of_its_weights():
     # each decoded value is an E4M3 value times the block's power of two
     codes, scales = a["w_up_codes"][1], a["w_up_scales"][1]
     np.testing.assert_array_equal(ew.expert(1)[2], O.e4m3_value(codes) * np.repeat(np.ldexp(1.0, scales.astype(int) - 127), 32, axis=1))
+
+
+# ---- NVFP4 weights ------------------------------------------------------------
+
+def test_nvfp4_decode_golden_points():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "nvfp4_points.txt")):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        code, scale, ts, want = [part.strip() for part in line.split("|")]
+        c = int(code, 16)
+        # the code as element 0 (low nibble) and as element 1 (high nibble) of a 16-element block
+        for pos in (0, 1):
+            codes = np.zeros((1, 8), np.uint8)
+            codes[0, 0] = c if pos == 0 else c << 4
+            got = O.nvfp4_decode(codes, np.array([[int(scale, 16)]], np.uint8), float(ts))
+            assert got[0, pos] == float(want) and np.signbit(got[0, pos]) == np.signbit(float(want)), line
+        n += 1
+    assert n == 6
+
+
+def test_nvfp4_blocks_of_16_and_layer_equals_its_dense_layer():
+    # each scale covers 16 consecutive elements of a row
+    codes = np.full((2, 16), 0x22, np.uint8)             # every element 1.0
+    scales = np.array([[0x38, 0x40], [0x30, 0x48]], np.uint8)  # 1, 2 ; 0.5, 4
+    got = O.nvfp4_decode(codes, scales, 1.0)
+    np.testing.assert_array_equal(got, np.repeat([[1.0, 2.0], [0.5, 4.0]], 16, axis=1))
+    # the decoded weights are bf16 numbers (tensor scale 1.5 * 2^-k): the NVFP4 layer equals the
+    # float32 dense layer holding them, through the pinned dense path
+    w = W.GPTOSS_NVFP4.scaled(T=20, d=64, d_ff=96, E=4, k=2, name="pin_nvfp4")
+    a = I.make_inputs(w)
+    ew = O.ExpertWeights(a, "bf16", "nvfp4")
+    dense = {k: v for k, v in a.items() if not k.startswith(("w_gate", "w_up", "w_down"))}
+    for name, pos in (("w_gate", 0), ("w_up", 2), ("w_down", 4)):
+        m = np.stack([ew.expert(e)[pos] for e in range(w.E)])
+        assert np.array_equal(O.round_bf16(m[m != 0]), m[m != 0])
+        dense[name] = m.astype(np.float32)
+    for key in ("x", "router_w", "router_b", "b_gate", "b_up", "b_down"):
+        dense[key] = O.to_f64(a[key], "bf16").astype(np.float32)
+    c = _cfg(w)
+    np.testing.assert_array_equal(O.moe_layer(a, c)["out"], O.moe_layer(dense, dict(c, dtype="f32", weights="dense"))["out"])
