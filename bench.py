@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block|
-                                glm_int4|glm_int8|mxfp4_mx8|mxfp8_mx8]
+                                glm_int4|glm_int8|mxfp4_mx8|mxfp8_mx8|nvfp4]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm",
-                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8", "mxfp8_mx8"])
+                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8", "mxfp8_mx8", "nvfp4"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,7 +61,7 @@ def workload(name):
             "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
             "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK,
             "glm_int4": W.GLM4_MOE_LITE_INT4, "glm_int8": W.GLM4_MOE_LITE_INT8,
-            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8, "mxfp8_mx8": W.GPTOSS_MXFP8_MX8}[name]
+            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8, "mxfp8_mx8": W.GPTOSS_MXFP8_MX8, "nvfp4": W.GPTOSS_NVFP4}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -76,6 +76,8 @@ def algorithmic_gate_up(w, counts):
         wbytes_per_expert = 2 * (w.d_ff * w.d // 2 + w.d_ff * w.d // 32)
     elif w.weights == "mxfp8":
         wbytes_per_expert = 2 * (w.d_ff * w.d + w.d_ff * w.d // 32)
+    elif w.weights == "nvfp4":
+        wbytes_per_expert = 2 * (w.d_ff * w.d // 2 + w.d_ff * w.d // 16)
     elif w.weights in ("affine4", "affine8"):
         bits, group = (4, 32) if w.weights == "affine4" else (8, 64)
         wbytes_per_expert = 2 * (w.d_ff * w.d * bits // 8 + 2 * 2 * w.d_ff * w.d // group)
@@ -150,14 +152,14 @@ def main():
     w = workload(args.workload)
     steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
                            "block_decode": 500, "block_glm": 100, "dense_block": 100, "glm_int4": 100,
-                           "glm_int8": 100, "mxfp4_mx8": 50, "mxfp8_mx8": 50}[args.workload]
+                           "glm_int8": 100, "mxfp4_mx8": 50, "mxfp8_mx8": 50, "nvfp4": 50}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     a = I.make_inputs(w)
     t0 = LY.to_device(a, dev)
     copies = [t0]
-    weight_keys = [k for k in t0 if k not in ("x",) and t0[k] is not None]
+    weight_keys = [k for k in t0 if k not in ("x",) and isinstance(t0[k], torch.Tensor)]
     for _ in range(max(0, args.copies - 1)):
         copies.append({k: (v.clone() if k in weight_keys else v) for k, v in t0.items()})
     ws = LY.workspace_for(w, dev)

@@ -141,6 +141,27 @@ moe_status moe_ffn_forward_mxfp4(const void* x, const void* router_w, const void
                                  void* out, void* workspace, size_t workspace_bytes,
                                  moe_routing_out* routing, hipStream_t stream);
 
+/* GPT-OSS-style layer with NVFP4 expert weights (glm4_moe_lite.go
+ * quantizationParams: NVFP4 = groups of 16, 4 bits; the layout is the
+ * published NVFP4 one).  Same as moe_ffn_forward_mxfp4 except the scales:
+ *   *_codes  uint8 [E, rows, cols/2]: e2m1 codes as for MXFP4;
+ *   *_scales uint8 [E, rows, cols/16]: E4M3 codes (bit 7 sign, bits 6..3
+ *            exponent with bias 7, bits 2..0 mantissa; S.1111.111 is NaN),
+ *            one per 16 consecutive elements along cols;
+ *   *_tensor_scale: fp32 factor of the whole tensor (finite, else
+ *            MOE_ERR_INVALID_ARG).
+ * W = e2m1(code) * e4m3(scale) * tensor_scale; the weights are rounded to
+ * bf16 for the MFMA (exact when the product has at most 8 significant bits).
+ * A NaN scale yields NaN outputs where its block is used.  Workspace as
+ * moe_ffn_workspace_bytes(..., MOE_BF16, 0). */
+moe_status moe_ffn_forward_nvfp4(const void* x, const void* router_w, const void* router_b,
+                                 const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, float w_gate_tensor_scale,
+                                 const void* b_gate, const uint8_t* w_up_codes, const uint8_t* w_up_scales,
+                                 float w_up_tensor_scale, const void* b_up, const uint8_t* w_down_codes,
+                                 const uint8_t* w_down_scales, float w_down_tensor_scale, const void* b_down, int T,
+                                 int d, int d_ff, int E, int k, float alpha, float limit, void* out, void* workspace,
+                                 size_t workspace_bytes, moe_routing_out* routing, hipStream_t stream);
+
 /* GPT-OSS-style MXFP4 layer on the gfx950 scaled MFMA (MXFP8 activations).
  * Arguments, layouts and routing as moe_ffn_forward_mxfp4; the expert GEMMs
  * differ: the rows entering gate|up (x) and down (h, after bias and

@@ -3,12 +3,14 @@
 //   gate|up:  h[r][f] = act(x[t] . Wg[e][f] + bg[e][f], x[t] . Wu[e][f] + bu[e][f])
 //   down:     y[r][n] = h[r] . Wd[e][n] + bd[e][n]
 //   MXFP4:    W[e][n][k] = e2m1(code[e][n][k]) * 2^(scale[e][n][k / 32] - 127)
+//   NVFP4:    W[e][n][k] = e2m1(code[e][n][k]) * e4m3(scale[e][n][k / 16]) * tensor_scale
 //   affine:   W[e][n][k] = scale[e][n][k / G] * q[e][n][k] + bias[e][n][k / G]
 //             (4-bit codes with G = 32, 8-bit codes with G = 64)
 //
 // (MaxText GPT-OSS weight mapping "MOE EXPERTS"; the weight format of the
 // MXFP4 GPT-OSS checkpoints; OCP Microscaling Formats v1.0 for e2m1 / e8m0;
-// glm4_moe_lite.go SwitchMLP / quantizationParams for the affine experts.)
+// glm4_moe_lite.go SwitchMLP / quantizationParams for the affine experts and
+// the NVFP4 group of 16.)
 //
 // MXFP4 products e2m1 * 2^s are bf16 numbers, so those operands are exact;
 // affine weights are computed in fp32 (one fma) and rounded once to bf16.
@@ -18,7 +20,11 @@
 // into LDS (a quarter of the bf16 bytes), each wavefront reads its own code
 // fragments from there and converts them into the bf16 B operands of the
 // MFMAs, in the shadow of the previous step's MFMAs: gfx950's
-// v_cvt_scalef32_pk_bf16_fp4 for MXFP4; byte-to-float conversions, one fma
+// v_cvt_scalef32_pk_bf16_fp4 for MXFP4 (its scale is a power of two); for
+// NVFP4 v_cvt_scalef32_pk_f32_fp4 with scale 1, a multiply by the block's
+// fp32 scale (its E4M3 scale times the tensor scale; a lane's 32 codes of a
+// tile span two blocks of 16, steps 0-1 and 2-3) and a bf16 pack;
+// byte-to-float conversions, one fma
 // with the group's scale and bias, and a bf16 pack for affine codes.
 //
 // K permutation.  v_mfma_f32_32x32x16_bf16 takes 8 k values from each lane
@@ -55,7 +61,7 @@ constexpr int kGroupM = MOE_MX_GROUP_M;  // row tiles walked together within an 
 constexpr int BK = 64;                   // K elements per A stage and per decode tile
 constexpr int kCodeRowBytes = 128;       // bytes of a weight row's codes per copy group
 // weight formats
-constexpr int kFmtMx4 = 0, kFmtAff4 = 1, kFmtAff8 = 2;
+constexpr int kFmtMx4 = 0, kFmtAff4 = 1, kFmtAff8 = 2, kFmtNv4 = 3;
 // kinds of K-tile step (see tile_step)
 constexpr int kSteady = 0, kGeneral = 1, kLast = 2, kFinal = 3;
 template <int V> using int_c = std::integral_constant<int, V>;
@@ -87,18 +93,38 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+// Byte p of a word of e2m1 codes (low nibble first) as two exact fp32
+// values.  p must fold to a constant.  (The scaled conversions apply a
+// power-of-two scale, as MX blocks have; NVFP4 scales are multiplied after.)
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2v_t fp4_pair_f32(uint32_t codes, int p) {
+  if (p == 0) return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  if (p == 1) return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  if (p == 2) return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+}
+// Value of an E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent 0 is subnormal, S.1111.111 is NaN), exact in fp32.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t ex = (b >> 3) & 15u, m = b & 7u;
+  float v = ex == 0 ? (float)m * 0.001953125f : __uint_as_float(((ex + 120u) << 23) | (m << 20));
+  v = (b & 0x7fu) == 0x7fu ? __uint_as_float(0x7fc00000u) : v;
+  return (b & 0x80u) ? -v : v;
+}
 // byte b of w as a float (v_cvt_f32_ubyte<b>); b must fold to a constant
 __device__ __forceinline__ float ubyte(uint32_t w, int b) { return static_cast<float>((w >> (8 * b)) & 0xffu); }
 
 template <int FMT, bool GATED, int NJ, bool FAST>
 __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   constexpr bool MX = FMT == kFmtMx4;
+  constexpr bool NV = FMT == kFmtNv4;
+  constexpr bool FP4 = MX || NV;                   // e2m1 codes with byte scales
   constexpr int CB = FMT == kFmtAff8 ? 8 : 4;      // code bits
   constexpr int kTilesPerGroup = kCodeRowBytes / (BK * CB / 8);  // 4 (4-bit) or 2 (8-bit)
-  constexpr int QG = MX ? 32 : (CB == 4 ? 32 : 64);  // elements per scale
+  constexpr int QG = MX ? 32 : NV ? 16 : (CB == 4 ? 32 : 64);  // elements per scale
   constexpr bool SCALE_LDS = FAST;                 // scales (and biases) copied into LDS per group
-  constexpr int NT = MX ? 1 : 2;                   // scale tables: MXFP4 scales; affine scales and biases
-  constexpr int EB = MX ? 1 : 2;                   // bytes per table element (e8m0 byte / bf16)
+  constexpr int NT = FP4 ? 1 : 2;                  // scale tables: e8m0 / E4M3 scales; affine scales and biases
+  constexpr int EB = FP4 ? 1 : 2;                  // bytes per table element (scale byte / bf16)
   constexpr int SBY = EB * BK * kTilesPerGroup / QG;  // bytes of one row and code group in one table
   constexpr int kScaleDw = (SBY + 3) / 4 + 1;      // aligned dwords that hold them (2-byte aligned start)
   constexpr int BN = 64 * NJ;
@@ -161,13 +187,14 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   const int code_bytes = K * CB / 8;  // of one weight row
   const uint8_t* const code_gate = a.c0 + (size_t)e * N * code_bytes;
   const uint8_t* const code_up = GATED ? a.c1 + (size_t)e * N * code_bytes : code_gate;
-  const uint8_t* const scale_gate = MX ? a.s0 + (size_t)e * N * (K / 32) : nullptr;
-  const uint8_t* const scale_up = MX && GATED ? a.s1 + (size_t)e * N * (K / 32) : scale_gate;
+  // MXFP4 / NVFP4: scale bytes [E, N, K / QG]
+  const uint8_t* const scale_gate = FP4 ? a.s0 + (size_t)e * N * (K / QG) : nullptr;
+  const uint8_t* const scale_up = FP4 && GATED ? a.s1 + (size_t)e * N * (K / QG) : scale_gate;
   // affine: bf16 scales and biases [E, N, K / QG]
-  const uint16_t* const qs_gate = MX ? nullptr : reinterpret_cast<const uint16_t*>(a.s0) + (size_t)e * N * (K / QG);
-  const uint16_t* const qs_up = !MX && GATED ? reinterpret_cast<const uint16_t*>(a.s1) + (size_t)e * N * (K / QG) : qs_gate;
-  const uint16_t* const qb_gate = MX ? nullptr : a.qb0 + (size_t)e * N * (K / QG);
-  const uint16_t* const qb_up = !MX && GATED ? a.qb1 + (size_t)e * N * (K / QG) : qb_gate;
+  const uint16_t* const qs_gate = FP4 ? nullptr : reinterpret_cast<const uint16_t*>(a.s0) + (size_t)e * N * (K / QG);
+  const uint16_t* const qs_up = !FP4 && GATED ? reinterpret_cast<const uint16_t*>(a.s1) + (size_t)e * N * (K / QG) : qs_gate;
+  const uint16_t* const qb_gate = FP4 ? nullptr : a.qb0 + (size_t)e * N * (K / QG);
+  const uint16_t* const qb_up = !FP4 && GATED ? a.qb1 + (size_t)e * N * (K / QG) : qb_gate;
   // Code copy round i: lane l copies stored chunk l % 8 of B row
   // 32 i + code_r (code_r = 8 wv + l / 8 < 32), i.e. weight row
   // n0 + 32 (i / 2) + code_r of the gate (i even) or up (i odd) tensor in the
@@ -257,7 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   // scales of tile kt for this lane's half: FAST from the scale buffer,
   // else from the tensors into registers a tile ahead (a half past K loads
   // the row's last scale; take_scales replaces it).  Affine: the bf16 scale
-  // in the low and the bf16 bias in the high half of sraw.
+  // in the low and the bf16 bias in the high half of sraw; NVFP4: the scale
+  // bytes of the half's two blocks of 16 in bytes 0 and 1.
   uint32_t sraw[NJ];
   auto load_scales = [&](int kt) __attribute__((always_inline)) {
     if constexpr (SCALE_LDS) {
@@ -271,10 +299,19 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
         for (int t = 0; t < NT; ++t) {
           const uint8_t* Sb = reinterpret_cast<const uint8_t*>(lds_scale[(kt / kTilesPerGroup) & 1][t]);
           const int at = sc_at[t][j] + EB * el;
-          const uint32_t x = EB == 1 ? (uint32_t)Sb[at] : (uint32_t)*reinterpret_cast<const uint16_t*>(Sb + at);
+          uint32_t x;
+          if constexpr (NV) x = (uint32_t)Sb[at] | ((uint32_t)Sb[at + 1] << 8);
+          else x = EB == 1 ? (uint32_t)Sb[at] : (uint32_t)*reinterpret_cast<const uint16_t*>(Sb + at);
           v |= x << (16 * t);
         }
         sraw[j] = v;
+      }
+    } else if constexpr (NV) {
+      const int gi = min((BK * kt + 32 * fk) / 16, K / 16 - 2);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint8_t* p = ((GATED && (j & 1)) ? scale_up : scale_gate) + (uint32_t)clamp_row(frag_row(j)) * (uint32_t)(K / 16) + gi;
+        sraw[j] = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
       }
     } else if constexpr (!MX) {
       const int gi = min((BK * kt + 32 * fk) / QG, K / QG - 1);
@@ -291,14 +328,25 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
         sraw[j] = ((GATED && (j & 1)) ? scale_up : scale_gate)[(uint32_t)clamp_row(frag_row(j)) * (uint32_t)(K / 32) + cb];
     }
   };
-  float scf[NJ];      // scale factors of the current tile
-  float sbi[MX ? 1 : NJ];  // affine: biases of the current tile
-  uint32_t nan_j = 0; // MXFP4, bit j: scale byte 255 (NaN block) in the current tile
-  // scales of tile kt from sraw (a half past K: MXFP4 127, affine scale and
-  // bias 0, with zero codes either way)
+  float scf[NJ];      // scale factors of the current tile (NVFP4: of steps 0-1)
+  float scf2[NV ? NJ : 1];  // NVFP4: scale factors of steps 2-3
+  float sbi[FP4 ? 1 : NJ];  // affine: biases of the current tile
+  uint32_t nan_j = 0; // MXFP4 / NVFP4, bit j: a NaN scale in the current tile
+  // scales of tile kt from sraw (a half past K: scale 1 (MXFP4 byte 127),
+  // affine scale and bias 0, with zero codes either way)
   auto take_scales = [&](int kt) __attribute__((always_inline)) {
     const bool past = !FAST && BK * kt + 32 * fk >= K;
-    if constexpr (MX) {
+    if constexpr (NV) {
+      nan_j = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t sb = past ? 0x3838u : sraw[j];
+        const float ts = (GATED && (j & 1)) ? a.ts1 : a.ts0;
+        scf[j] = e4m3_value(sb & 0xffu) * ts;
+        scf2[j] = e4m3_value(sb >> 8) * ts;
+        nan_j |= ((sb & 0x7fu) == 0x7fu || (sb & 0x7f00u) == 0x7f00u ? 1u : 0u) << j;
+      }
+    } else if constexpr (MX) {
       nan_j = 0;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -372,9 +420,15 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   // the NaN weights would)
   auto cvt_part = [&](int s, int buf, int j, int p) __attribute__((always_inline)) {
     uint32_t v;
-    if constexpr (MX) {
+    if constexpr (FP4) {
       const uint32_t w = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
-      v = cvt_fp4_pair(w, scf[j], p);
+      if constexpr (NV) {
+        const float sc = s >= 2 ? scf2[j] : scf[j];
+        const f32x2v_t f = fp4_pair_f32(w, p);
+        v = pack2(f.x * sc, f.y * sc);
+      } else {
+        v = cvt_fp4_pair(w, scf[j], p);
+      }
       if (s == 0 && p == 0) v = (nan_j >> j) & 1 ? 0x7fc07fc0u : v;
     } else if constexpr (CB == 4) {
       // elements 2p, 2p + 1: the low and high nibble of byte p of word s,
@@ -565,8 +619,9 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
 // 4-byte aligned in base and size: their dwords are then copied whole.
 bool fast_shape(const Layer& L, int K, int N, const void* scales, const void* biases) {
   if (K % BK) return false;
-  const bool mx = L.wfmt == WF_MXFP4;
-  const size_t bytes = (size_t)L.E * N * (K / (L.wfmt == WF_AFF8 ? 64 : 32)) * (mx ? 1 : 2);
+  const bool mx = L.wfmt == WF_MXFP4 || L.wfmt == WF_NVFP4;  // byte scales, no biases
+  const int group = L.wfmt == WF_AFF8 ? 64 : L.wfmt == WF_NVFP4 ? 16 : 32;
+  const size_t bytes = (size_t)L.E * N * (K / group) * (mx ? 1 : 2);
   const auto aligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 4 == 0; };
   return bytes % 4 == 0 && aligned(scales) && (mx || aligned(biases));
 }
@@ -580,6 +635,7 @@ void launch_fmt(const MfmaArgs& m, dim3 grid, bool fast, hipStream_t s) {
 template <bool GATED, int NJ>
 void launch_any(const Layer& L, const MfmaArgs& m, dim3 grid, bool fast, hipStream_t s) {
   if (L.wfmt == WF_MXFP4) launch_fmt<kFmtMx4, GATED, NJ>(m, grid, fast, s);
+  else if (L.wfmt == WF_NVFP4) launch_fmt<kFmtNv4, GATED, NJ>(m, grid, fast, s);
   else if (L.wfmt == WF_AFF4) launch_fmt<kFmtAff4, GATED, NJ>(m, grid, fast, s);
   else launch_fmt<kFmtAff8, GATED, NJ>(m, grid, fast, s);
 }
@@ -593,6 +649,7 @@ hipError_t launch_gate_up_lowbit(const Layer& L, const Work& W, hipStream_t s) {
   m.row_token = W.row_token;
   m.c0 = L.wg_codes; m.s0 = L.wg_scales; m.c1 = L.wu_codes; m.s1 = L.wu_scales;
   m.qb0 = static_cast<const uint16_t*>(L.wg_qbias); m.qb1 = static_cast<const uint16_t*>(L.wu_qbias);
+  m.ts0 = L.ts_g; m.ts1 = L.ts_u;
   m.bias0 = static_cast<const uint16_t*>(L.bg);
   m.bias1 = static_cast<const uint16_t*>(L.bu);
   m.N = L.F; m.K = L.d; m.N_sh = L.F; m.K_sh = L.d;
@@ -612,6 +669,7 @@ hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s) {
   m.row_token = nullptr;
   m.c0 = L.wd_codes; m.s0 = L.wd_scales;
   m.qb0 = static_cast<const uint16_t*>(L.wd_qbias);
+  m.ts0 = L.ts_d;
   m.bias0 = static_cast<const uint16_t*>(L.bd);
   m.N = L.d; m.K = L.F; m.N_sh = L.d; m.K_sh = L.F;
   m.out = static_cast<uint16_t*>(W.y);

@@ -35,6 +35,7 @@ struct MfmaArgs {
   const uint8_t* as;          // MXFP8 activations: e8m0 scales [rows, lda / 32] of the codes at a
   const uint16_t* qb0;        // affine: bf16 biases [E, N, K / group] of c0 / c1
   const uint16_t* qb1;
+  float ts0, ts1;             // NVFP4: tensor scales of c0 / c1
   const uint16_t* bias0;      // [E, N] or nullptr
   const uint16_t* bias1;
   const uint16_t* sh_w0;      // shared expert [N_sh, K_sh] or nullptr

@@ -117,6 +117,8 @@ moe_status check_common(const Layer& L) {
   if (lowbit_format(L.wfmt)) {
     if (!L.wg_codes || !L.wg_scales || !L.wu_codes || !L.wu_scales || !L.wd_codes || !L.wd_scales)
       return fail(MOE_ERR_INVALID_ARG, "all codes and scales are required");
+    if (L.wfmt == WF_NVFP4 && !(std::isfinite(L.ts_g) && std::isfinite(L.ts_u) && std::isfinite(L.ts_d)))
+      return fail(MOE_ERR_INVALID_ARG, "NVFP4 tensor scales must be finite");
     if ((L.wfmt == WF_AFF4 || L.wfmt == WF_AFF8) && (!L.wg_qbias || !L.wu_qbias || !L.wd_qbias))
       return fail(MOE_ERR_INVALID_ARG, "all affine biases are required");
   } else if (!L.wg || !L.wu || !L.wd) {
@@ -386,6 +388,26 @@ moe_status moe_ffn_forward_mxfp8_mxfp8(const void* x, const void* router_w, cons
   L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
   L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
   L.dt = MOE_BF16; L.wfmt = moe::WF_MXFP8; L.mx_act = 1;
+  L.out = out;
+  if (routing) L.routing = *routing;
+  return moe::run(L, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_nvfp4(const void* x, const void* router_w, const void* router_b,
+                                 const uint8_t* w_gate_codes, const uint8_t* w_gate_scales, float w_gate_tensor_scale,
+                                 const void* b_gate, const uint8_t* w_up_codes, const uint8_t* w_up_scales,
+                                 float w_up_tensor_scale, const void* b_up, const uint8_t* w_down_codes,
+                                 const uint8_t* w_down_scales, float w_down_tensor_scale, const void* b_down, int T,
+                                 int d, int d_ff, int E, int k, float alpha, float limit, void* out, void* workspace,
+                                 size_t workspace_bytes, moe_routing_out* routing, hipStream_t stream) {
+  Layer L;
+  L.x = x; L.router_w = router_w; L.router_b = router_b;
+  L.wg_codes = w_gate_codes; L.wg_scales = w_gate_scales; L.bg = b_gate; L.ts_g = w_gate_tensor_scale;
+  L.wu_codes = w_up_codes; L.wu_scales = w_up_scales; L.bu = b_up; L.ts_u = w_up_tensor_scale;
+  L.wd_codes = w_down_codes; L.wd_scales = w_down_scales; L.bd = b_down; L.ts_d = w_down_tensor_scale;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k;
+  L.act = MOE_ACT_CLIPPED_SWIGLU; L.alpha = alpha; L.limit = limit;
+  L.dt = MOE_BF16; L.wfmt = moe::WF_NVFP4;
   L.out = out;
   if (routing) L.routing = *routing;
   return moe::run(L, workspace, workspace_bytes, stream);

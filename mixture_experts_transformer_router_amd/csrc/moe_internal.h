@@ -13,7 +13,8 @@ namespace moe {
 // WF_AFF4 / WF_AFF8: affine group-quantized codes (4 bits, groups of 32 /
 // 8 bits, groups of 64) with bf16 scales and biases.  WF_MXFP8: E4M3 codes
 // with an e8m0 scale per 32 (only with MXFP8 activations, on the scaled MFMA).
-enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2, WF_AFF4 = 3, WF_AFF8 = 4, WF_MXFP8 = 5 };
+// WF_NVFP4: e2m1 codes with an E4M3 scale per 16 and an fp32 tensor scale.
+enum WeightFmt : int { WF_F32 = 0, WF_BF16 = 1, WF_MXFP4 = 2, WF_AFF4 = 3, WF_AFF8 = 4, WF_MXFP8 = 5, WF_NVFP4 = 6 };
 inline bool lowbit_format(int wfmt) { return wfmt >= WF_MXFP4; }
 inline int code_bits(int wfmt) { return wfmt == WF_AFF8 || wfmt == WF_MXFP8 ? 8 : 4; }
 
@@ -61,6 +62,7 @@ struct Layer {
   const void* wg_qbias = nullptr;         // affine: bf16 biases of the codes
   const void* wu_qbias = nullptr;
   const void* wd_qbias = nullptr;
+  float ts_g = 1.f, ts_u = 1.f, ts_d = 1.f;  // NVFP4 tensor scales
   const void* sh_wg = nullptr;
   const void* sh_wu = nullptr;
   const void* sh_wd = nullptr;

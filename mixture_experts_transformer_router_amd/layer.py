@@ -15,6 +15,8 @@ def to_device(arrays: dict, device="cuda") -> dict:
     for key, a in arrays.items():
         if a is None:
             out[key] = None
+        elif np.ndim(a) == 0:
+            out[key] = float(a)        # a scalar (NVFP4 tensor scale) stays on the host
         elif a.dtype == np.uint16:
             out[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
         else:
@@ -70,6 +72,13 @@ def run(w: Workload, t: dict, out=None, workspace=None, routing=False, stream=No
             t["w_up_codes"], t["w_up_scales"], t.get("b_up"), t["w_down_codes"], t["w_down_scales"],
             t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out, workspace=workspace,
             routing=routing, stream=stream, weights=w.weights)
+    if w.weights == "nvfp4":
+        return moe_ffn.forward_nvfp4(
+            t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"],
+            float(t["w_gate_tensor_scale"]), t.get("b_gate"), t["w_up_codes"], t["w_up_scales"],
+            float(t["w_up_tensor_scale"]), t.get("b_up"), t["w_down_codes"], t["w_down_scales"],
+            float(t["w_down_tensor_scale"]), t.get("b_down"), w.k, alpha=w.alpha, limit=w.limit, out=out,
+            workspace=workspace, routing=routing, stream=stream)
     if w.weights == "mxfp4":
         return moe_ffn.forward_mxfp4(
             t["x"], t["router_w"], t.get("router_b"), t["w_gate_codes"], t["w_gate_scales"], t.get("b_gate"),

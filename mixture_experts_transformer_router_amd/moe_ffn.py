@@ -39,7 +39,8 @@ EXPORTED = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp4
             "moe_ffn_profile_enable", "moe_ffn_profile_read", "moe_block_workspace_bytes",
             "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped",
             "moe_block_forward_grouped_affine", "moe_ffn_forward_mxfp4_mxfp8",
-            "moe_ffn_workspace_bytes_mxfp8", "moe_mxfp8_quantize", "moe_ffn_forward_mxfp8_mxfp8")
+            "moe_ffn_workspace_bytes_mxfp8", "moe_mxfp8_quantize", "moe_ffn_forward_mxfp8_mxfp8",
+            "moe_ffn_forward_nvfp4")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -114,6 +115,9 @@ def load() -> ctypes.CDLL:
     L.moe_ffn_forward_mxfp8_mxfp8.argtypes = L.moe_ffn_forward_mxfp4.argtypes
     L.moe_ffn_workspace_bytes_mxfp8.restype = _Z
     L.moe_ffn_workspace_bytes_mxfp8.argtypes = [_I, _I, _I, _I, _I]
+    L.moe_ffn_forward_nvfp4.restype = _I
+    L.moe_ffn_forward_nvfp4.argtypes = [_P, _P, _P, _P, _P, _F, _P, _P, _P, _F, _P, _P, _P, _F, _P,
+                                        _I, _I, _I, _I, _I, _F, _F, _P, _P, _Z, _P, _P]
     L.moe_mxfp8_quantize.restype = _I
     L.moe_mxfp8_quantize.argtypes = [_P, _I, _I, _P, _P, _P]
     L.moe_ffn_forward_grouped.restype = _I
@@ -273,6 +277,26 @@ def forward_mxfp4_mxfp8(x, router_w, router_b, w_gate_codes, w_gate_scales, b_ga
     return (out, r) if routing else out
 
 
+def forward_nvfp4(x, router_w, router_b, w_gate_codes, w_gate_scales, w_gate_ts, b_gate, w_up_codes, w_up_scales,
+                  w_up_ts, b_up, w_down_codes, w_down_scales, w_down_ts, b_down, k, alpha=1.702, limit=7.0, out=None,
+                  workspace=None, routing=False, stream=None):
+    """moe_ffn_forward_nvfp4: codes uint8 [E,rows,cols/2], E4M3 scales uint8 [E,rows,cols/16],
+    float tensor scales."""
+    T, d = x.shape
+    E, d_ff = w_gate_codes.shape[0], w_gate_codes.shape[1]
+    out = torch.empty_like(x) if out is None else out
+    ws = workspace if workspace is not None else alloc_workspace(
+        workspace_bytes(T, d, d_ff, E, k, MOE_BF16), x.device)
+    r, rs = _routing(T, k, E, x.device, routing)
+    st = load().moe_ffn_forward_nvfp4(
+        _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w_gate_codes), _ptr(w_gate_scales), float(w_gate_ts),
+        _ptr(b_gate), _ptr(w_up_codes), _ptr(w_up_scales), float(w_up_ts), _ptr(b_up), _ptr(w_down_codes),
+        _ptr(w_down_scales), float(w_down_ts), _ptr(b_down), T, d, d_ff, E, k, alpha, limit, _ptr(out), _ptr(ws),
+        ws.numel(), ctypes.byref(rs) if rs is not None else None, _stream(stream))
+    _check(st)
+    return (out, r) if routing else out
+
+
 def mxfp8_quantize(x, codes=None, scales=None, stream=None):
     """moe_mxfp8_quantize: bf16 [rows, cols] -> (E4M3 codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
     rows, cols = x.shape
@@ -403,6 +427,12 @@ def bound_layer_call(w, t: dict, out: torch.Tensor, workspace: torch.Tensor, str
         return bind(f"moe_ffn_forward_{w.weights}_mxfp8", g("x"), g("router_w"), g("router_b"), g("w_gate_codes"),
                     g("w_gate_scales"), g("b_gate"), g("w_up_codes"), g("w_up_scales"), g("b_up"),
                     g("w_down_codes"), g("w_down_scales"), g("b_down"), w.T, w.d, w.d_ff, w.E, w.k,
+                    w.alpha, w.limit, out, workspace, workspace.numel(), rp, s)
+    if w.weights == "nvfp4":
+        return bind("moe_ffn_forward_nvfp4", g("x"), g("router_w"), g("router_b"), g("w_gate_codes"),
+                    g("w_gate_scales"), float(t["w_gate_tensor_scale"]), g("b_gate"), g("w_up_codes"),
+                    g("w_up_scales"), float(t["w_up_tensor_scale"]), g("b_up"), g("w_down_codes"),
+                    g("w_down_scales"), float(t["w_down_tensor_scale"]), g("b_down"), w.T, w.d, w.d_ff, w.E, w.k,
                     w.alpha, w.limit, out, workspace, workspace.numel(), rp, s)
     if w.weights == "mxfp4":
         return bind("moe_ffn_forward_mxfp4", g("x"), g("router_w"), g("router_b"), g("w_gate_codes"),

@@ -232,3 +232,16 @@ def test_mxfp8_quantize_argument_checks(lib):
     assert q(FAKE + 8, 4, 64, FAKE2, FAKE2 + (1 << 30), None) == M.MOE_ERR_INVALID_ARG  # alignment
     assert q(FAKE, 4, 64, FAKE + 64, FAKE2, None) == M.MOE_ERR_INVALID_ARG              # codes overlap x
     assert q(None, 0, 64, None, None, None) == M.MOE_OK
+
+
+
+def test_nvfp4_argument_checks(lib):
+    def call(d=128, F=128, ts=1.0, codes=FAKE):
+        n = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0)
+        return lib.moe_ffn_forward_nvfp4(FAKE, FAKE, None, codes, FAKE, ts, None, FAKE, FAKE, 1.0, None, FAKE, FAKE,
+                                         1.0, None, 16, d, F, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36), n, None, None)
+    assert call(ts=float("nan")) == M.MOE_ERR_INVALID_ARG
+    assert b"tensor scale" in lib.moe_last_error_detail()
+    assert call(ts=float("inf")) == M.MOE_ERR_INVALID_ARG
+    assert call(d=48) == M.MOE_ERR_UNSUPPORTED
+    assert call(codes=None) == M.MOE_ERR_INVALID_ARG

@@ -343,3 +343,45 @@ def test_mxfp8_activation_nan_scale():
     np.testing.assert_array_equal(np.isnan(got), nan_ref)
     fin = ~nan_ref
     assert np.abs(got[fin] - ref[fin]).max() <= 2e-2 * np.abs(ref[fin]).max()
+
+
+# --- NVFP4 weights (e2m1, E4M3 scale per 16, tensor scale), decoded in registers --------
+
+NV_CASES = [
+    W.GPTOSS_NVFP4,
+    W.GPTOSS_NVFP4.scaled(T=150, d=256, d_ff=192, E=8, k=2, name="nvfp4_small"),
+    # K ragged against the 64-wide tiles: the general kernel (scales in registers, a K tail)
+    W.GPTOSS_NVFP4.scaled(T=90, d=96, d_ff=160, E=6, k=3, name="nvfp4_ragged_k"),
+    W.GPTOSS_NVFP4.scaled(T=1, d=128, d_ff=64, E=32, k=4, name="nvfp4_T1"),
+]
+
+
+@pytest.mark.parametrize("w", NV_CASES, ids=[w.name for w in NV_CASES])
+def test_nvfp4_layer(w):
+    _run_and_check(w, n_out_tokens=256 if w.T > 256 else w.T)
+
+
+def test_nvfp4_nan_scale():
+    # an E4M3 NaN scale (0x7F) in a gate block makes every output of the tokens
+    # routed to that expert NaN; one in a down block only that output column
+    w = W.GPTOSS_NVFP4.scaled(T=150, d=256, d_ff=192, E=8, k=2, name="nvfp4_nan_scale")
+    a = I.make_inputs(w)
+    a["w_gate_scales"] = a["w_gate_scales"].copy()
+    a["w_gate_scales"][3, 5, 3] = 0x7F     # expert 3, gate row 5, elements 48..63
+    a["w_down_scales"] = a["w_down_scales"].copy()
+    a["w_down_scales"][6, 10, 9] = 0xFF    # expert 6, output column 10, elements 144..159
+    _say(f"[case] {w.name} T={w.T} d={w.d} F={w.d_ff} E={w.E} k={w.k} seed={w.seed}")
+    t = LY.to_device(a, DEV)
+    out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, r = LY.run(w, t, out=out, routing=True)
+    torch.cuda.synchronize()
+    cfg = cfg_of(w)
+    g_idx = r["topk_idx"].cpu().numpy().astype(np.int64)
+    logits, _, _ = O.route(a, cfg)
+    ref = O.experts_forward(a, cfg, g_idx, O.forced_weights(logits, g_idx, cfg))
+    got = out.float().cpu().numpy().astype(np.float64)
+    nan_ref = np.isnan(ref)
+    assert nan_ref.all(axis=1).any() and nan_ref[~nan_ref.all(axis=1), 10].any()
+    np.testing.assert_array_equal(np.isnan(got), nan_ref)
+    fin = ~nan_ref
+    assert np.abs(got[fin] - ref[fin]).max() <= 2e-2 * np.abs(ref[fin]).max()
