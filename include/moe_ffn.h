@@ -218,7 +218,8 @@ size_t moe_ffn_workspace_bytes_mxfp8(int T, int d, int d_ff, int E, int k);
  * is v's).  An all-zero block gets scale byte 0; a block holding a NaN or an
  * infinity gets scale byte 255 (NaN) and zero codes.  Enqueued on `stream`;
  * rows == 0 is a no-op.  The three buffers must not overlap.  Errors:
- * MOE_ERR_INVALID_ARG (nothing is launched). */
+ * MOE_ERR_INVALID_ARG, or MOE_ERR_UNSUPPORTED for rows * cols >= 2^40
+ * (nothing is launched). */
 moe_status moe_mxfp8_quantize(const void* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream);
 

@@ -419,6 +419,8 @@ moe_status moe_mxfp8_quantize(const void* x, int rows, int cols, uint8_t* codes,
   if (rows < 0) return moe::fail(MOE_ERR_INVALID_ARG, "rows = %d < 0", rows);
   if (cols < 32 || cols % 32) return moe::fail(MOE_ERR_INVALID_ARG, "cols = %d must be a positive multiple of 32", cols);
   if (rows == 0) return MOE_OK;
+  if ((long long)rows * cols >= (1ll << 40))
+    return moe::fail(MOE_ERR_UNSUPPORTED, "rows * cols = %lld >= 2^40", (long long)rows * cols);
   if (!x || !codes || !scales) return moe::fail(MOE_ERR_INVALID_ARG, "x, codes and scales are required");
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 16)
     return moe::fail(MOE_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");

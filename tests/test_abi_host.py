@@ -232,6 +232,7 @@ def test_mxfp8_quantize_argument_checks(lib):
     assert q(FAKE + 8, 4, 64, FAKE2, FAKE2 + (1 << 30), None) == M.MOE_ERR_INVALID_ARG  # alignment
     assert q(FAKE, 4, 64, FAKE + 64, FAKE2, None) == M.MOE_ERR_INVALID_ARG              # codes overlap x
     assert q(None, 0, 64, None, None, None) == M.MOE_OK
+    assert q(FAKE, 1 << 20, 1 << 20, FAKE2, FAKE2 + (1 << 44), None) == M.MOE_ERR_UNSUPPORTED
 
 
 
