@@ -63,6 +63,37 @@ struct StageTimer {
   }
 };
 
+// ---- side stream ------------------------------------------------------------
+// The bf16 shared expert of a low-bit layer runs as its own launches of the
+// dense GEMM; they go to a second stream of the device (default priority,
+// created on first use, kept until the process ends), forked after the
+// permutation and joined before the combine, so that its few tiles fill the
+// CUs the routed kernels leave idle instead of running after them.  The
+// fork/join records are made under a lock, so concurrent calls on one device
+// stay ordered; the side stream is shared and serialises their shared-expert
+// work.  Without a side stream the launches stay on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false, ok = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+SideStream* side_stream_locked() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  }
+  return ss.ok ? &ss : nullptr;
+}
+
 // ---- checks ----------------------------------------------------------------
 moe_status check_common(const Layer& L) {
   if (L.T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", L.T);
@@ -177,8 +208,21 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
   // low-bit routed experts with a (bf16) shared expert: the dense GEMM takes
-  // the shared expert's tiles
+  // the shared expert's tiles, on the side stream when there is one
   const bool shared_dense = path == kLowbit && L.has_shared();
+  SideStream* forked = nullptr;
+  if (shared_dense) {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* ss = side_stream_locked();
+    if (ss && hipEventRecord(ss->fork, s) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
+      e = launch_gate_up_mfma_shared(L, W, ss->s);
+      if (e == hipSuccess) e = launch_down_mfma_shared(L, W, ss->s);
+      if (e == hipSuccess) e = hipEventRecord(ss->join, ss->s);
+      if (e != hipSuccess) return fail(MOE_ERR_HIP, "shared expert launch: %s", hipGetErrorString(e));
+      forked = ss;
+    }
+  }
+  const bool shared_forked = forked != nullptr;
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     if (path == kMx) {
@@ -188,7 +232,7 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
           : path == kMfma ? launch_gate_up_mfma(L, W, s)
           : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
     }
-    if (e == hipSuccess && shared_dense) e = launch_gate_up_mfma_shared(L, W, s);
+    if (e == hipSuccess && shared_dense && !shared_forked) e = launch_gate_up_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
@@ -201,9 +245,16 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
           : path == kMfma ? launch_down_mfma(L, W, s)
           : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
     }
-    if (e == hipSuccess && shared_dense) e = launch_down_mfma_shared(L, W, s);
+    if (e == hipSuccess && shared_dense && !shared_forked) e = launch_down_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
+  if (shared_forked) {
+    // join: the combine reads the shared expert's rows.  (A later call's
+    // record of the event waits for at least as much: its side-stream work
+    // is queued after this call's.)
+    e = hipStreamWaitEvent(s, forked->join, 0);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "shared expert join: %s", hipGetErrorString(e));
+  }
   {
     StageTimer tm(s, MOE_STAGE_COMBINE);
     e = launch_combine(L, W, s);
