@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|prefill|mxfp4|glm|tiny|block_decode|block_glm|dense_block|
-                                glm_int4|glm_int8|mxfp4_mx8|mxfp8_mx8|nvfp4]
+                                glm_int4|glm_int8|mxfp4_mx8|mxfp8_mx8|nvfp4|mxfp4_decode]
 
 A step is one whole layer forward (route, permute, gate|up, down, combine)
 over one batch of seeded synthetic tokens already resident in HBM.  The
@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "mxfp4", "glm", "tiny", "block_decode", "block_glm",
-                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8", "mxfp8_mx8", "nvfp4"])
+                             "dense_block", "glm_int4", "glm_int8", "mxfp4_mx8", "mxfp8_mx8", "nvfp4",
+                             "mxfp4_decode"])
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,7 +62,8 @@ def workload(name):
             "glm": W.GLM4_MOE_LITE, "tiny": W.TINY_F32, "block_decode": W.GPTOSS_DECODE_BLOCK,
             "block_glm": W.GLM4_MOE_LITE_BLOCK, "dense_block": W.GLM4_DENSE_BLOCK,
             "glm_int4": W.GLM4_MOE_LITE_INT4, "glm_int8": W.GLM4_MOE_LITE_INT8,
-            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8, "mxfp8_mx8": W.GPTOSS_MXFP8_MX8, "nvfp4": W.GPTOSS_NVFP4}[name]
+            "mxfp4_mx8": W.GPTOSS_MXFP4_MX8, "mxfp8_mx8": W.GPTOSS_MXFP8_MX8, "nvfp4": W.GPTOSS_NVFP4,
+            "mxfp4_decode": W.GPTOSS_MXFP4_DECODE}[name]
 
 
 def algorithmic_gate_up(w, counts):
@@ -152,7 +154,8 @@ def main():
     w = workload(args.workload)
     steps = args.steps or {"decode": 500, "tiny": 500, "prefill": 50, "mxfp4": 50, "glm": 100,
                            "block_decode": 500, "block_glm": 100, "dense_block": 100, "glm_int4": 100,
-                           "glm_int8": 100, "mxfp4_mx8": 50, "mxfp8_mx8": 50, "nvfp4": 50}[args.workload]
+                           "glm_int8": 100, "mxfp4_mx8": 50, "mxfp8_mx8": 50, "nvfp4": 50,
+                           "mxfp4_decode": 500}[args.workload]
     warm = args.warmup if args.warmup is not None else max(5, steps // 10)
     dev = "cuda"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -198,7 +201,7 @@ def main():
 
     gu_ms, gu_n = prof["gate_up"]
     gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
-    if args.workload in ("decode", "block_decode"):
+    if args.workload in ("decode", "block_decode", "mxfp4_decode"):
         roof = {"bound": "hbm", "achieved": nbytes / gu_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
         peak = FP8_PEAK_TFLOPS if w.act_quant == "mxfp8" else BF16_PEAK_TFLOPS

@@ -17,6 +17,12 @@
 // owns kRowsPerWave * kWaves rows of one expert.  Blocks of experts without
 // rows exit at once.
 //
+// MXFP4 weights (e2m1 codes, an e8m0 scale per 32): a lane takes 32
+// consecutive elements of a row per 2048-element chunk, i.e. 16 bytes of
+// codes (a wavefront load is still one contiguous kilobyte) under exactly one
+// scale byte; v_cvt_scalef32_pk_bf16_fp4 turns each 8-element piece into bf16
+// (exact: e2m1 times a power of two) for the same dot products.
+//
 // After the reduction loop every lane holds partial sums of all
 // (row, token) outputs; a reduce-scatter over the 64 lanes (halving the value
 // set at each of the 6 exchange steps, DPP within 16 lanes, lane shuffles
@@ -56,6 +62,10 @@ struct DecodeArgs {
   const int32_t* row_token;   // gate|up: token of each sorted row; down: nullptr
   const uint16_t* w0;         // [E, N, K]: down, or gate
   const uint16_t* w1;         // up (gate|up only)
+  const uint8_t* c0;          // MXFP4: codes [E, N, K / 2] and e8m0 scales [E, N, K / 32] of w0 / w1
+  const uint8_t* s0;
+  const uint8_t* c1;
+  const uint8_t* s1;
   const uint16_t* bias0;      // [E, N] or nullptr
   const uint16_t* bias1;
   const uint16_t* sh_w0;      // shared expert [N_sh, K_sh] or nullptr
@@ -152,9 +162,24 @@ __device__ __forceinline__ bool lane_owns(int lane) {
   return own;
 }
 
+// e8m0 scale byte as the fp32 factor of the conversion (0: 2^-127, a
+// denormal; 255, NaN, is marked by the caller)
+__device__ __forceinline__ float e8m0_factor(uint32_t s) { return __uint_as_float(s == 0 ? 0x00400000u : (s << 23)); }
+
+// Word q of 16 bytes of e2m1 codes (8 codes, low nibble first) times the
+// scale as 8 bf16, in element order.
+__device__ __forceinline__ u32x4_t fp4_word_bf16(uint32_t w, float scale) {
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return r;
+}
+
 // One pass over the wavefront's weight rows for token slots t0 .. t0+TG-1
 // of the expert (slots >= m contribute zeros and are not stored).
-template <bool GATED, int TG>
+template <bool GATED, int TG, bool FP4>
 __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool shared, int N, int K, int nw, int m0,
                                             int m, int t0, int lane) {
   constexpr int G = GATED ? 2 : 1;
@@ -183,7 +208,60 @@ __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool sha
 #pragma unroll
   for (int i = 0; i < V; ++i) v[i] = 0.f;
 
-  const int chunks = (K + kChunk - 1) / kChunk;
+  if constexpr (FP4) {
+    // codes and scales of the wavefront's rows (rows past N read row N - 1)
+    const uint8_t* Cr[G][R];
+    const uint8_t* Sr[G][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const size_t row = (size_t)e * N + min(nw + r, N - 1);
+      Cr[0][r] = a.c0 + row * (K / 2);
+      Sr[0][r] = a.s0 + row * (K / 32);
+      if constexpr (GATED) {
+        Cr[1][r] = a.c1 + row * (K / 2);
+        Sr[1][r] = a.s1 + row * (K / 32);
+      }
+    }
+    constexpr int kChunk4 = 2048;  // elements of a row per wavefront load (64 lanes x 32)
+    const int chunks = (K + kChunk4 - 1) / kChunk4;
+    for (int c = 0; c < chunks; ++c) {
+      const int k = c * kChunk4 + 32 * lane;
+      if (k < K) {  // K % 32 == 0: a lane's 32 elements are all in range or all out
+        u32x4_t wc[G][R];
+        float sf[G][R];
+        bool nan[G][R];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            wc[g][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Cr[g][r] + k / 2));
+            const uint32_t sb = Sr[g][r][k / 32];
+            sf[g][r] = e8m0_factor(sb);
+            nan[g][r] = sb == 255u;
+          }
+        // the 8-element pieces one at a time (unrolled, the compiler would hold
+        // every token's 32 elements at once)
+#pragma unroll 1
+        for (int q = 0; q < 4; ++q) {
+          u32x4_t x[TG];
+#pragma unroll
+          for (int t = 0; t < TG; ++t) x[t] = (t0 + t < m) ? ld16(X[t] + k + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const uint32_t word = q == 0 ? wc[g][r].x : q == 1 ? wc[g][r].y : q == 2 ? wc[g][r].z : wc[g][r].w;
+              u32x4_t w8 = fp4_word_bf16(word, sf[g][r]);
+              // a NaN block: one NaN weight makes the row's sums NaN, as the oracle's would be
+              if (q == 0 && nan[g][r]) w8.x = 0x7fc07fc0u;
+#pragma unroll
+              for (int t = 0; t < TG; ++t) v[(g * R + r) * TG + t] = dot8(w8, x[t], v[(g * R + r) * TG + t]);
+            }
+        }
+      }
+    }
+  }
+  const int chunks = FP4 ? 0 : (K + kChunk - 1) / kChunk;
   for (int c = 0; c < chunks; ++c) {
     const int k = c * kChunk + 8 * lane;
     if (k < K) {  // K % 8 == 0: a lane's 8 elements are all in range or all out
@@ -229,7 +307,7 @@ __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool sha
   }
 }
 
-template <bool GATED>
+template <bool GATED, bool FP4>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int e = blockIdx.y;
   const bool shared = e >= a.E;
@@ -243,18 +321,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int nw = nb + (threadIdx.x >> 6) * kRowsPerWave;
   if (nw >= N) return;
-  // token group: the smallest power of two covering m, up to kMaxTg per pass
+  // token group: the smallest power of two covering m, up to MT per pass
+  // (MXFP4: up to 8, which keeps the kernel at two wavefronts per SIMD; an
+  // expert with more rows takes a second pass over its weights)
+  constexpr int MT = FP4 && kMaxTg > 8 ? 8 : kMaxTg;
   if (m <= 1) {
-    decode_pass<GATED, 1>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    decode_pass<GATED, 1, FP4>(a, e, shared, N, K, nw, m0, m, 0, lane);
   } else if (m <= 2) {
-    decode_pass<GATED, 2>(a, e, shared, N, K, nw, m0, m, 0, lane);
-  } else if (m <= 4 || kMaxTg < 8) {
-    for (int t0 = 0; t0 < m; t0 += 4 < kMaxTg ? 4 : kMaxTg)
-      decode_pass<GATED, (4 < kMaxTg ? 4 : kMaxTg)>(a, e, shared, N, K, nw, m0, m, t0, lane);
-  } else if (m <= 8 || kMaxTg < 16) {
-    for (int t0 = 0; t0 < m; t0 += 8) decode_pass<GATED, 8>(a, e, shared, N, K, nw, m0, m, t0, lane);
+    decode_pass<GATED, 2, FP4>(a, e, shared, N, K, nw, m0, m, 0, lane);
+  } else if (m <= 4 || MT < 8) {
+    for (int t0 = 0; t0 < m; t0 += 4 < MT ? 4 : MT)
+      decode_pass<GATED, (4 < MT ? 4 : MT), FP4>(a, e, shared, N, K, nw, m0, m, t0, lane);
+  } else if (m <= 8 || MT < 16) {
+    for (int t0 = 0; t0 < m; t0 += 8) decode_pass<GATED, 8, FP4>(a, e, shared, N, K, nw, m0, m, t0, lane);
   } else {
-    decode_pass<GATED, (kMaxTg < 16 ? 8 : 16)>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    decode_pass<GATED, (MT < 16 ? 8 : 16), FP4>(a, e, shared, N, K, nw, m0, m, 0, lane);
   }
 }
 
@@ -281,11 +362,13 @@ hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.bias1 = static_cast<const uint16_t*>(L.bu);
   d.sh_w0 = static_cast<const uint16_t*>(L.sh_wg);
   d.sh_w1 = static_cast<const uint16_t*>(L.sh_wu);
+  d.c0 = L.wg_codes; d.s0 = L.wg_scales; d.c1 = L.wu_codes; d.s1 = L.wu_scales;
   d.N = L.F; d.K = L.d; d.N_sh = L.F_sh; d.K_sh = L.d;
   d.out = static_cast<uint16_t*>(W.h);
   d.ldo = L.F_max();
   const dim3 grid((L.F_max() + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
-  decode_kernel<true><<<grid, 64 * kWaves, 0, s>>>(d);
+  if (L.wfmt == WF_MXFP4) decode_kernel<true, true><<<grid, 64 * kWaves, 0, s>>>(d);
+  else decode_kernel<true, false><<<grid, 64 * kWaves, 0, s>>>(d);
   return hipGetLastError();
 }
 
@@ -297,11 +380,13 @@ hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.w0 = static_cast<const uint16_t*>(L.wd);
   d.bias0 = static_cast<const uint16_t*>(L.bd);
   d.sh_w0 = static_cast<const uint16_t*>(L.sh_wd);
+  d.c0 = L.wd_codes; d.s0 = L.wd_scales;
   d.N = L.d; d.K = L.F; d.N_sh = L.d; d.K_sh = L.F_sh;
   d.out = static_cast<uint16_t*>(W.y);
   d.ldo = L.d;
   const dim3 grid((L.d + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
-  decode_kernel<false><<<grid, 64 * kWaves, 0, s>>>(d);
+  if (L.wfmt == WF_MXFP4) decode_kernel<false, true><<<grid, 64 * kWaves, 0, s>>>(d);
+  else decode_kernel<false, false><<<grid, 64 * kWaves, 0, s>>>(d);
   return hipGetLastError();
 }
 

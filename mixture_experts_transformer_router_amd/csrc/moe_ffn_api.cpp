@@ -204,6 +204,8 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   enum { kDecode, kMfma, kLowbit, kMx, kTiled } path;
   if (L.dt == MOE_F32) path = kTiled;
   else if (L.mx_act) path = kMx;
+  // MXFP4 weights (no shared expert) stream through the decode kernel for a few tokens
+  else if (L.wfmt == WF_MXFP4 && L.T <= kDecodeMaxTokens && !L.has_shared()) path = kDecode;
   else if (lowbit_format(L.wfmt)) path = kLowbit;
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;

@@ -127,8 +127,10 @@ GPTOSS_MXFP4_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp4_mxfp8act_T4096_d288
 GPTOSS_MXFP8_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp8w_mxfp8act_T4096_d2880_E32_k4", weights="mxfp8",
                                        act_quant="mxfp8", mx_scale_exp_lo=-13, mx_scale_exp_hi=-9)
 MX_ACT = (GPTOSS_MXFP4_MX8, GPTOSS_MXFP8_MX8)
+# The MXFP4 layer at decode (8 tokens): weight streaming of the 4.25-bit experts.
+GPTOSS_MXFP4_DECODE = GPTOSS_MXFP4.scaled(T=8, name="gptoss20b_mxfp4_decode_T8_d2880_E32_k4")
 # NVFP4 expert weights (e2m1 codes, an E4M3 scale per 16, a tensor scale),
 # decoded to bf16 in registers (quantizationParams: NVFP4 = groups of 16, 4 bits).
 GPTOSS_NVFP4 = GPTOSS_MXFP4.scaled(name="gptoss20b_nvfp4_T4096_d2880_E32_k4", weights="nvfp4")
 
-BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED + MX_ACT + (GPTOSS_NVFP4,)}
+BY_NAME = {w.name: w for w in ALL + BLOCKS + QUANTIZED + MX_ACT + (GPTOSS_NVFP4, GPTOSS_MXFP4_DECODE)}

@@ -385,3 +385,47 @@ def test_nvfp4_nan_scale():
     np.testing.assert_array_equal(np.isnan(got), nan_ref)
     fin = ~nan_ref
     assert np.abs(got[fin] - ref[fin]).max() <= 2e-2 * np.abs(ref[fin]).max()
+
+
+# --- MXFP4 weights at decode (T <= 16): the weight-streaming kernel ---------------------
+
+MXD_CASES = [
+    W.GPTOSS_MXFP4_DECODE,
+    # 16 rows per expert: two passes of 8 tokens over the weights
+    W.GPTOSS_MXFP4_DECODE.scaled(T=16, d=512, d_ff=256, E=4, k=4, name="mxfp4_decode_T16_two_passes"),
+    # K ragged against the 2048-element chunks of a wave load, 1..5 rows per expert
+    W.GPTOSS_MXFP4_DECODE.scaled(T=5, d=2112, d_ff=160, E=6, k=3, name="mxfp4_decode_T5_ragged_k"),
+    W.GPTOSS_MXFP4_DECODE.scaled(T=1, d=256, d_ff=96, E=32, k=4, name="mxfp4_decode_T1"),
+    # as a MoE block
+    W.GPTOSS_MXFP4_DECODE.scaled(T=8, d=256, d_ff=192, E=8, k=2, block=True, name="mxfp4_decode_block"),
+]
+
+
+@pytest.mark.parametrize("w", MXD_CASES, ids=[w.name for w in MXD_CASES])
+def test_mxfp4_decode(w):
+    _run_and_check(w)
+
+
+def test_mxfp4_decode_nan_scale():
+    # NaN e8m0 scales on the weight-streaming path: as on the GEMM path
+    w = W.GPTOSS_MXFP4_DECODE.scaled(T=12, d=256, d_ff=192, E=4, k=2, name="mxfp4_decode_nan_scale")
+    a = I.make_inputs(w)
+    a["w_gate_scales"] = a["w_gate_scales"].copy()
+    a["w_gate_scales"][1, 7, 2] = 255
+    a["w_down_scales"] = a["w_down_scales"].copy()
+    a["w_down_scales"][2, 20, 3] = 255
+    _say(f"[case] {w.name} T={w.T} d={w.d} F={w.d_ff} E={w.E} k={w.k} seed={w.seed}")
+    t = LY.to_device(a, DEV)
+    out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device=DEV)
+    out, r = LY.run(w, t, out=out, routing=True)
+    torch.cuda.synchronize()
+    cfg = cfg_of(w)
+    g_idx = r["topk_idx"].cpu().numpy().astype(np.int64)
+    logits, _, _ = O.route(a, cfg)
+    ref = O.experts_forward(a, cfg, g_idx, O.forced_weights(logits, g_idx, cfg))
+    got = out.float().cpu().numpy().astype(np.float64)
+    nan_ref = np.isnan(ref)
+    assert nan_ref.any()
+    np.testing.assert_array_equal(np.isnan(got), nan_ref)
+    fin = ~nan_ref
+    assert np.abs(got[fin] - ref[fin]).max() <= 2e-2 * np.abs(ref[fin]).max()
