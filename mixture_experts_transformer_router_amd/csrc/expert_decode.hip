@@ -179,11 +179,10 @@ __device__ __forceinline__ u32x4_t fp4_word_bf16(uint32_t w, float scale) {
 
 // One pass over the wavefront's weight rows for token slots t0 .. t0+TG-1
 // of the expert (slots >= m contribute zeros and are not stored).
-template <bool GATED, int TG, bool FP4>
+template <bool GATED, int TG, bool FP4, int R>
 __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool shared, int N, int K, int nw, int m0,
                                             int m, int t0, int lane) {
   constexpr int G = GATED ? 2 : 1;
-  constexpr int R = kRowsPerWave;
   constexpr int V = G * R * TG;  // value index ((g R + r) TG + t)
   static_assert((V & (V - 1)) == 0, "value count must be a power of two");
 
@@ -307,35 +306,46 @@ __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool sha
   }
 }
 
+// MXFP4 shapes.  A code row is K/2 bytes, so a wavefront takes more rows than
+// with bf16 to keep as many loads in flight; a pass takes at most 4 tokens,
+// since the widest token group sets the register budget of the whole kernel
+// and 4 keeps it at two wavefronts per SIMD (an expert with more rows makes
+// more passes over its weights).  gate|up reads two tensors per row, so it
+// takes half the rows of down.
+constexpr int kFp4RowsGated = 4, kFp4RowsDown = 8, kFp4MaxTg = 4;
+template <bool GATED, bool FP4> constexpr int rows_per_wave() {
+  return !FP4 ? kRowsPerWave : GATED ? kFp4RowsGated : kFp4RowsDown;
+}
+template <bool GATED, bool FP4> constexpr int max_token_group() { return FP4 ? kFp4MaxTg : kMaxTg; }
+
 template <bool GATED, bool FP4>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+  constexpr int RW = rows_per_wave<GATED, FP4>();
   const int e = blockIdx.y;
   const bool shared = e >= a.E;
   const int N = shared ? a.N_sh : a.N;
   const int K = shared ? a.K_sh : a.K;
-  const int nb = blockIdx.x * kRowsPerBlock;
+  const int nb = blockIdx.x * RW * kWaves;
   if (nb >= N) return;
   const int m0 = a.offsets[e];
   const int m = a.offsets[e + 1] - m0;  // <= kDecodeMaxTokens on this path
   if (m <= 0) return;
   const int lane = threadIdx.x & 63;
-  const int nw = nb + (threadIdx.x >> 6) * kRowsPerWave;
+  const int nw = nb + (threadIdx.x >> 6) * RW;
   if (nw >= N) return;
   // token group: the smallest power of two covering m, up to MT per pass
-  // (MXFP4: up to 8, which keeps the kernel at two wavefronts per SIMD; an
-  // expert with more rows takes a second pass over its weights)
-  constexpr int MT = FP4 && kMaxTg > 8 ? 8 : kMaxTg;
+  constexpr int MT = max_token_group<GATED, FP4>();
   if (m <= 1) {
-    decode_pass<GATED, 1, FP4>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    decode_pass<GATED, 1, FP4, RW>(a, e, shared, N, K, nw, m0, m, 0, lane);
   } else if (m <= 2) {
-    decode_pass<GATED, 2, FP4>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    decode_pass<GATED, 2, FP4, RW>(a, e, shared, N, K, nw, m0, m, 0, lane);
   } else if (m <= 4 || MT < 8) {
     for (int t0 = 0; t0 < m; t0 += 4 < MT ? 4 : MT)
-      decode_pass<GATED, (4 < MT ? 4 : MT), FP4>(a, e, shared, N, K, nw, m0, m, t0, lane);
+      decode_pass<GATED, (4 < MT ? 4 : MT), FP4, RW>(a, e, shared, N, K, nw, m0, m, t0, lane);
   } else if (m <= 8 || MT < 16) {
-    for (int t0 = 0; t0 < m; t0 += 8) decode_pass<GATED, 8, FP4>(a, e, shared, N, K, nw, m0, m, t0, lane);
+    for (int t0 = 0; t0 < m; t0 += 8) decode_pass<GATED, 8, FP4, RW>(a, e, shared, N, K, nw, m0, m, t0, lane);
   } else {
-    decode_pass<GATED, (MT < 16 ? 8 : 16), FP4>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    decode_pass<GATED, (MT < 16 ? 8 : 16), FP4, RW>(a, e, shared, N, K, nw, m0, m, 0, lane);
   }
 }
 
@@ -366,9 +376,13 @@ hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.N = L.F; d.K = L.d; d.N_sh = L.F_sh; d.K_sh = L.d;
   d.out = static_cast<uint16_t*>(W.h);
   d.ldo = L.F_max();
-  const dim3 grid((L.F_max() + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
-  if (L.wfmt == WF_MXFP4) decode_kernel<true, true><<<grid, 64 * kWaves, 0, s>>>(d);
-  else decode_kernel<true, false><<<grid, 64 * kWaves, 0, s>>>(d);
+  if (L.wfmt == WF_MXFP4) {
+    constexpr int rb = rows_per_wave<true, true>() * kWaves;
+    decode_kernel<true, true><<<dim3((L.F_max() + rb - 1) / rb, L.n_experts_all()), 64 * kWaves, 0, s>>>(d);
+  } else {
+    const dim3 grid((L.F_max() + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
+    decode_kernel<true, false><<<grid, 64 * kWaves, 0, s>>>(d);
+  }
   return hipGetLastError();
 }
 
@@ -384,9 +398,13 @@ hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.N = L.d; d.K = L.F; d.N_sh = L.d; d.K_sh = L.F_sh;
   d.out = static_cast<uint16_t*>(W.y);
   d.ldo = L.d;
-  const dim3 grid((L.d + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
-  if (L.wfmt == WF_MXFP4) decode_kernel<false, true><<<grid, 64 * kWaves, 0, s>>>(d);
-  else decode_kernel<false, false><<<grid, 64 * kWaves, 0, s>>>(d);
+  if (L.wfmt == WF_MXFP4) {
+    constexpr int rb = rows_per_wave<false, true>() * kWaves;
+    decode_kernel<false, true><<<dim3((L.d + rb - 1) / rb, L.n_experts_all()), 64 * kWaves, 0, s>>>(d);
+  } else {
+    const dim3 grid((L.d + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
+    decode_kernel<false, false><<<grid, 64 * kWaves, 0, s>>>(d);
+  }
   return hipGetLastError();
 }
 

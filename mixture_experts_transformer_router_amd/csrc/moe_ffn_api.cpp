@@ -198,9 +198,9 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
     if (e == hipSuccess && L.mx_act) e = launch_mx_quant(L.x, L.d, L.T, L.d, W.xq, W.xs, mx_row_bytes(L.d), s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
-  // Expert stages: weight streaming on MFMA for a few tokens (every expert
-  // then holds at most kDecodeMaxTokens rows), grouped MFMA GEMMs for bf16 /
-  // MXFP4 otherwise, vector-ALU tiles for fp32.
+  // Expert stages: weight streaming with vector dot products for a few tokens
+  // (every expert then holds at most kDecodeMaxTokens rows), grouped MFMA
+  // GEMMs otherwise, vector-ALU tiles for fp32.
   enum { kDecode, kMfma, kLowbit, kMx, kTiled } path;
   if (L.dt == MOE_F32) path = kTiled;
   else if (L.mx_act) path = kMx;

@@ -391,8 +391,8 @@ def test_nvfp4_nan_scale():
 
 MXD_CASES = [
     W.GPTOSS_MXFP4_DECODE,
-    # 16 rows per expert: two passes of 8 tokens over the weights
-    W.GPTOSS_MXFP4_DECODE.scaled(T=16, d=512, d_ff=256, E=4, k=4, name="mxfp4_decode_T16_two_passes"),
+    # 16 rows per expert: four passes of 4 tokens over the weights
+    W.GPTOSS_MXFP4_DECODE.scaled(T=16, d=512, d_ff=256, E=4, k=4, name="mxfp4_decode_T16_multi_pass"),
     # K ragged against the 2048-element chunks of a wave load, 1..5 rows per expert
     W.GPTOSS_MXFP4_DECODE.scaled(T=5, d=2112, d_ff=160, E=6, k=3, name="mxfp4_decode_T5_ragged_k"),
     W.GPTOSS_MXFP4_DECODE.scaled(T=1, d=256, d_ff=96, E=32, k=4, name="mxfp4_decode_T1"),
