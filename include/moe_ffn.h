@@ -63,6 +63,11 @@
  *   synchronisation.
  * Limits.  1 <= E <= 256, 1 <= k <= min(E, 16), d and d_ff multiples of 8
  *   (of 32 for MXFP4 weights), T * k < 2^26.
+ * Alignment.  x, router_w, the dense expert weights (routed and shared) and
+ *   the code tensors are read with 16-byte vector loads and must be 16-byte
+ *   aligned; out, the biases, the norm weight, the residual and the affine
+ *   scale and bias tables must be aligned to their element size.  Otherwise
+ *   MOE_ERR_INVALID_ARG.  (Whole allocations from hipMalloc or torch are.)
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H

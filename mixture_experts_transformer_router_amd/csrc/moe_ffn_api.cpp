@@ -155,8 +155,31 @@ moe_status check_common(const Layer& L) {
   } else if (!L.wg || !L.wu || !L.wd) {
     return fail(MOE_ERR_INVALID_ARG, "w_gate, w_up and w_down are required");
   }
+  // x, the router weight, the dense expert weights and the codes are read
+  // with 16-byte vector loads and global -> LDS copies; every other array at
+  // least element by element
+  const auto off16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; };
+  if (off16(L.x) || off16(L.router_w)) return fail(MOE_ERR_INVALID_ARG, "x and router_w must be 16-byte aligned");
+  if (lowbit_format(L.wfmt)) {
+    if (off16(L.wg_codes) || off16(L.wu_codes) || off16(L.wd_codes))
+      return fail(MOE_ERR_INVALID_ARG, "the code tensors must be 16-byte aligned");
+  } else if (off16(L.wg) || off16(L.wu) || off16(L.wd)) {
+    return fail(MOE_ERR_INVALID_ARG, "w_gate, w_up and w_down must be 16-byte aligned");
+  }
+  if (L.has_shared() && (off16(L.sh_wg) || off16(L.sh_wu) || off16(L.sh_wd)))
+    return fail(MOE_ERR_INVALID_ARG, "the shared expert's weights must be 16-byte aligned");
+  {
+    const size_t el = L.elt();
+    const auto off = [](const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
+    if (off(L.out, el) || off(L.router_b, el) || off(L.bg, el) || off(L.bu, el) || off(L.bd, el) ||
+        off(L.norm_w, el) || off(L.x_resid, el) || off(L.e_bias, 4))
+      return fail(MOE_ERR_INVALID_ARG, "out, the biases, the norm weight and the residual must be aligned to their element size");
+    if ((L.wfmt == WF_AFF4 || L.wfmt == WF_AFF8) &&
+        (off(L.wg_scales, 2) || off(L.wu_scales, 2) || off(L.wd_scales, 2) || off(L.wg_qbias, 2) ||
+         off(L.wu_qbias, 2) || off(L.wd_qbias, 2)))
+      return fail(MOE_ERR_INVALID_ARG, "the affine scales and biases (bf16) must be 2-byte aligned");
+  }
   if (L.mx_act) {
-    if (reinterpret_cast<uintptr_t>(L.x) % 16) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned with MXFP8 activations");
     const uintptr_t sc = reinterpret_cast<uintptr_t>(L.wg_scales) | reinterpret_cast<uintptr_t>(L.wu_scales) |
                          reinterpret_cast<uintptr_t>(L.wd_scales);
     if (sc % 4) return fail(MOE_ERR_INVALID_ARG, "the scale tensors must be 4-byte aligned with MXFP8 activations");

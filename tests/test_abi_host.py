@@ -92,6 +92,10 @@ def _fwd(lib, T=16, d=64, F=64, E=8, k=2, alpha=1.702, limit=7.0, dt=M.MOE_BF16,
     (dict(out=None), M.MOE_ERR_INVALID_ARG),
     (dict(dt=7), M.MOE_ERR_INVALID_ARG),
     (dict(out=FAKE), M.MOE_ERR_INVALID_ARG),                       # out aliases x
+    (dict(x=FAKE + 8), M.MOE_ERR_INVALID_ARG),                     # 16-byte vector loads
+    (dict(wr=FAKE + 4), M.MOE_ERR_INVALID_ARG),
+    (dict(wd=FAKE + 2), M.MOE_ERR_INVALID_ARG),
+    (dict(out=FAKE2 + 1), M.MOE_ERR_INVALID_ARG),                  # bf16 elements
     (dict(ws=0), M.MOE_ERR_WORKSPACE),
     (dict(wsb=1024), M.MOE_ERR_WORKSPACE),
     (dict(ws=FAKE + (1 << 36) + 64), M.MOE_ERR_WORKSPACE),          # misaligned
@@ -143,6 +147,8 @@ def test_mxfp4_argument_checks(lib):
     assert call(d=48) == M.MOE_ERR_UNSUPPORTED
     assert call(F=40) == M.MOE_ERR_UNSUPPORTED
     assert call(codes=None) == M.MOE_ERR_INVALID_ARG
+    assert call(codes=FAKE + 8) == M.MOE_ERR_INVALID_ARG
+    assert b"16-byte" in lib.moe_last_error_detail()
     # one expert's codes must stay under 2^32 bytes (32-bit offsets in the kernels)
     assert call(d=65536, F=131072) == M.MOE_ERR_UNSUPPORTED
     assert b"2^32" in lib.moe_last_error_detail()
