@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   if (!block_tile<kGroupM>(a, m_tile, n_tile)) return;
   const int4 desc = reinterpret_cast<const int4*>(a.tile_desc)[m_tile];
   const int e = desc.x;
-  if (e >= a.E) return;  // a shared expert's tiles are left to the dense kernel
+  if (e >= a.E) return;  // the launch covers routed experts only; kept as a guard
   const int N = a.N;
   const int K = a.K;
   const int n0 = n_tile * (GATED ? BN / 2 : BN);
@@ -656,7 +656,8 @@ hipError_t launch_gate_up_lowbit(const Layer& L, const Work& W, hipStream_t s) {
   m.out = static_cast<uint16_t*>(W.h);
   m.ldo = L.F_max();
   m.n_tiles = (L.F + 127) / 128;
-  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  m.e_end = L.E;  // routed experts only: a shared expert's tiles go to the dense kernel
+  const dim3 grid(grid_for(max_row_tiles(L, 0, L.E) * m.n_tiles));
   const bool fast = fast_shape(L, L.d, L.F, L.wg_scales, L.wg_qbias) && fast_shape(L, L.d, L.F, L.wu_scales, L.wu_qbias);
   launch_any<true, 4>(L, m, grid, fast, s);
   return hipGetLastError();
@@ -678,7 +679,8 @@ hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s) {
   const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
   const bool narrow = t192 * (256 + 48) < t256 * (256 + 64);
   m.n_tiles = narrow ? t192 : t256;
-  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  m.e_end = L.E;  // routed experts only: a shared expert's tiles go to the dense kernel
+  const dim3 grid(grid_for(max_row_tiles(L, 0, L.E) * m.n_tiles));
   const bool fast = fast_shape(L, L.F, L.d, L.wd_scales, L.wd_qbias);
   if (narrow) launch_any<false, 3>(L, m, grid, fast, s);
   else launch_any<false, 4>(L, m, grid, fast, s);

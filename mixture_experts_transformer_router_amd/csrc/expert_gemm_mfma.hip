@@ -391,9 +391,10 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
 }  // namespace
 
 namespace {
-hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first) {
+hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
   MfmaArgs m = base_args(L, W);
   m.e_first = e_first;
+  m.e_end = e_end;
   m.a = static_cast<const uint16_t*>(L.x);
   m.lda = L.d;
   m.row_token = W.row_token;
@@ -407,14 +408,15 @@ hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_firs
   m.out = static_cast<uint16_t*>(W.h);
   m.ldo = L.F_max();
   m.n_tiles = (L.F_max() + 127) / 128;
-  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
   mfma_gemm_kernel<true, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
 
-hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first) {
+hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
   MfmaArgs m = base_args(L, W);
   m.e_first = e_first;
+  m.e_end = e_end;
   m.a = static_cast<const uint16_t*>(W.h);
   m.lda = L.F_max();
   m.row_token = nullptr;
@@ -431,18 +433,24 @@ hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first) 
   const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
   const bool narrow = t192 * (256 + 192) < t256 * (256 + 256);
   m.n_tiles = narrow ? t192 : t256;
-  const dim3 grid(grid_for(max_row_tiles(L) * m.n_tiles));
+  const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
   if (narrow) mfma_gemm_kernel<false, 3, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   else mfma_gemm_kernel<false, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s) { return gate_up_mfma(L, W, s, 0); }
-hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s) { return down_mfma(L, W, s, 0); }
-hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t s) {
-  return gate_up_mfma(L, W, s, L.E);
+hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, bool routed_only) {
+  return gate_up_mfma(L, W, s, 0, routed_only ? L.E : L.n_experts_all());
 }
-hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s) { return down_mfma(L, W, s, L.E); }
+hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s, bool routed_only) {
+  return down_mfma(L, W, s, 0, routed_only ? L.E : L.n_experts_all());
+}
+hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t s) {
+  return gate_up_mfma(L, W, s, L.E, L.E + 1);
+}
+hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s) {
+  return down_mfma(L, W, s, L.E, L.E + 1);
+}
 
 }  // namespace moe

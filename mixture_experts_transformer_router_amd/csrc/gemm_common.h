@@ -42,7 +42,7 @@ struct MfmaArgs {
   const uint16_t* sh_w1;
   int N, K, N_sh, K_sh;
   int E, E_all;
-  int e_first;                // tiles of experts below e_first are skipped
+  int e_first, e_end;         // the launch covers the tiles of experts [e_first, e_end)
   const int32_t* offsets;     // [E_all + 1]
   const int32_t* tile_prefix; // [E_all + 1], 256-row tiles
   const int32_t* tile_desc;   // [tiles][4]: expert, first row, end row
@@ -116,14 +116,15 @@ __device__ __forceinline__ float expert_act_t(float g, float u, float alpha, flo
 }
 
 // Tile of this block.  The real number of row tiles is known only on the
-// device; every block reads it and the blocks of XCD x take the x-th
-// contiguous share of the tiles, walked kGroupM row tiles at a time, so the
-// blocks resident on one XCD reuse each other's A and B tiles through its L2.
-// Returns false for blocks without a tile, or whose tile belongs to an expert
-// below a.e_first.
+// device; every block reads the row tiles of its launch's experts
+// [e_first, e_end) (contiguous in the tile list) and the blocks of XCD x
+// take the x-th contiguous share of them, walked kGroupM row tiles at a time,
+// so the blocks resident on one XCD reuse each other's A and B tiles through
+// its L2.  Returns false for blocks without a tile.
 template <int kGroupM>
 __device__ __forceinline__ bool block_tile(const MfmaArgs& a, int& m_tile, int& n_tile) {
-  const int total_m = a.tile_prefix[a.E_all];
+  const int m_lo = a.tile_prefix[a.e_first];
+  const int total_m = a.tile_prefix[a.e_end] - m_lo;
   const int total = total_m * a.n_tiles;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   const int share = (total + kXcds - 1) / kXcds;
@@ -133,9 +134,9 @@ __device__ __forceinline__ bool block_tile(const MfmaArgs& a, int& m_tile, int& 
   const int first_m = group * kGroupM;
   const int gm = min(kGroupM, total_m - first_m);
   const int rr = L - group * kGroupM * a.n_tiles;
-  m_tile = first_m + rr % gm;
+  m_tile = m_lo + first_m + rr % gm;
   n_tile = rr / gm;
-  return a.e_first == 0 || reinterpret_cast<const int4*>(a.tile_desc)[m_tile].x >= a.e_first;
+  return true;
 }
 
 // Epilogue of a 256 x (64 NJ) tile held by 4 wavefronts (2 x 2, each 128 x
@@ -223,6 +224,8 @@ inline MfmaArgs base_args(const Layer& L, const Work& W) {
   MfmaArgs m{};
   m.E = L.E;
   m.E_all = L.n_experts_all();
+  m.e_first = 0;
+  m.e_end = m.E_all;
   m.offsets = W.offsets;
   m.tile_prefix = W.tile_prefix_big;
   m.tile_desc = W.tile_desc;
@@ -233,6 +236,15 @@ inline MfmaArgs base_args(const Layer& L, const Work& W) {
 }
 
 inline int max_row_tiles(const Layer& L) { return (L.rows_all() + BM - 1) / BM + L.n_experts_all(); }
+// Bound on the row tiles of experts [e_first, e_end): the routed experts hold
+// T k rows, the shared expert (index E) T rows, and each expert pads at most
+// one tile.
+inline int max_row_tiles(const Layer& L, int e_first, int e_end) {
+  long long rows = 0;
+  if (e_first < L.E) rows += (long long)L.T * L.k;
+  if (e_end > L.E) rows += L.T;
+  return (int)((rows + BM - 1) / BM) + (e_end - e_first);
+}
 inline int grid_for(int tiles) { return (tiles + kXcds - 1) / kXcds * kXcds; }
 
 }  // namespace gemm

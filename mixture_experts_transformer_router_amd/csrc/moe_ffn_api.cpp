@@ -232,9 +232,13 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   else if (lowbit_format(L.wfmt)) path = kLowbit;
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
-  // low-bit routed experts with a (bf16) shared expert: the dense GEMM takes
-  // the shared expert's tiles, on the side stream when there is one
-  const bool shared_dense = path == kLowbit && L.has_shared();
+  // A shared expert (bf16) next to many-token routed experts: its tiles go to
+  // their own launches of the dense GEMM, on the side stream when there is
+  // one, so that they fill the CUs the routed launches leave idle (the routed
+  // tiles alone often make whole waves over the CUs).  Low-bit routed experts
+  // always leave them to the dense GEMM; bf16 ones take them in their own
+  // launch when there is no side stream.
+  const bool shared_dense = (path == kLowbit || path == kMfma) && L.has_shared();
   SideStream* forked = nullptr;
   if (shared_dense) {
     std::lock_guard<std::mutex> lk(g_side_mu);
@@ -248,16 +252,17 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
     }
   }
   const bool shared_forked = forked != nullptr;
+  const bool shared_apart = path == kLowbit || shared_forked;  // shared tiles outside the routed launches
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     if (path == kMx) {
       e = launch_gate_up_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_gate_up_decode(L, W, s)
-          : path == kMfma ? launch_gate_up_mfma(L, W, s)
+          : path == kMfma ? launch_gate_up_mfma(L, W, s, shared_forked)
           : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
     }
-    if (e == hipSuccess && shared_dense && !shared_forked) e = launch_gate_up_mfma_shared(L, W, s);
+    if (e == hipSuccess && shared_dense && shared_apart && !shared_forked) e = launch_gate_up_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
@@ -267,10 +272,10 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
       if (e == hipSuccess) e = launch_down_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_down_decode(L, W, s)
-          : path == kMfma ? launch_down_mfma(L, W, s)
+          : path == kMfma ? launch_down_mfma(L, W, s, shared_forked)
           : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
     }
-    if (e == hipSuccess && shared_dense && !shared_forked) e = launch_down_mfma_shared(L, W, s);
+    if (e == hipSuccess && shared_dense && shared_apart && !shared_forked) e = launch_down_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
   if (shared_forked) {

@@ -130,8 +130,10 @@ hipError_t launch_gate_up(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s);
-hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s);
-hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s);
+// routed_only: the tiles of experts [0, E), leaving a shared expert's to the
+// _shared launchers; otherwise every expert's
+hipError_t launch_gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, bool routed_only);
+hipError_t launch_down_mfma(const Layer& L, const Work& W, hipStream_t s, bool routed_only);
 // low-bit expert weights (MXFP4, affine); the shared expert's tiles are skipped
 hipError_t launch_gate_up_lowbit(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s);
