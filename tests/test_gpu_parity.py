@@ -167,6 +167,29 @@ def test_deterministic_and_token_permutation_equivariant():
     assert torch.equal(o1[torch.from_numpy(perm).to(DEV)].view(torch.int16), o3.view(torch.int16))
 
 
+@pytest.mark.parametrize("base", [W.GLM4_MOE_LITE, W.GLM4_MOE_LITE_INT4], ids=["bf16", "int4"])
+def test_shared_expert_stream_back_to_back_calls(base):
+    # With many tokens the shared expert's GEMMs run on a second stream.  Two
+    # calls on one workspace, queued with no synchronisation between them, must
+    # each match the oracle (the second call's permutation must not overwrite
+    # the tile list while the first call's shared tiles still run), and a third
+    # call on the first inputs must repeat the first output bit for bit.
+    w1 = base.scaled(T=600, d=256, d_ff=192, E=64, k=6, d_ff_shared=192, name=f"shared_stream_{base.weights}")
+    w2 = w1.scaled(seed=w1.seed + 1)
+    _say(f"[case] {w1.name} T={w1.T} back-to-back")
+    a1, a2 = I.make_inputs(w1), I.make_inputs(w2)
+    t1, t2 = LY.to_device(a1, DEV), LY.to_device(a2, DEV)
+    ws = LY.workspace_for(w1, DEV)
+    outs = [torch.full((w1.T, w1.d), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    o1, r1 = LY.run(w1, t1, out=outs[0], workspace=ws, routing=True)
+    o2, r2 = LY.run(w2, t2, out=outs[1], workspace=ws, routing=True)
+    o3 = LY.run(w1, t1, out=outs[2], workspace=ws)
+    torch.cuda.synchronize()
+    check_layer(w1, a1, o1, r1, n_out_tokens=128)
+    check_layer(w2, a2, o2, r2, n_out_tokens=128)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
 def test_zero_tokens_is_noop_and_errors_leave_out_untouched():
     w = W.GPTOSS_DECODE.scaled(T=16, d=64, d_ff=64, E=4, k=2, name="errors")
     _say("[case] errors")
