@@ -52,9 +52,12 @@
  *   Non-NULL fields are filled (device pointers, caller-owned).
  * Workspace.  `workspace` is device memory of at least
  *   moe_ffn_workspace_bytes(...) bytes, 256-byte aligned; its contents on
- *   entry do not matter and are clobbered.
- * Stream.  All work is enqueued on `stream` (0 = the null stream).  The call
- *   returns without waiting for the GPU.
+ *   entry do not matter and are clobbered.  Every call's kernels read and
+ *   write it, so two calls may share a workspace only when one is ordered
+ *   after the other (the same stream, or an event between their streams).
+ * Stream.  All work is enqueued on `stream` (0 = the null stream), in launch
+ *   order; the library creates no stream or event of its own outside the
+ *   opt-in stage timer.  The call returns without waiting for the GPU.
  * Errors.  Every argument is checked on the host before anything is
  *   enqueued.  On an error nothing is launched, `out` and the workspace are
  *   untouched and a non-zero status is returned; moe_last_error_detail()
@@ -108,9 +111,12 @@ typedef struct {
 } moe_routing_out;
 
 /* Bytes of workspace a call with these sizes needs (pure host function).
- * d_ff_shared = 0 when there is no shared expert.  Returns 0 for T == 0 and
- * (size_t)-1 for sizes outside the limits. */
-size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int d_ff_shared);
+ * grouped: nonzero for the group-routed layer (moe_ffn_forward_grouped and
+ * its block and affine forms), zero for the GPT-OSS-style layers; only a
+ * group-routed layer has a shared expert.  d_ff_shared = 0 when there is no
+ * shared expert.  Returns 0 for T == 0 and (size_t)-1 for sizes outside the
+ * limits or a shared expert with grouped == 0. */
+size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int grouped, int d_ff_shared);
 
 /* GPT-OSS-style layer.
  * Routing: the k largest router logits per token (ties to the lower expert
@@ -211,6 +217,23 @@ moe_status moe_ffn_forward_mxfp8_mxfp8(const void* x, const void* router_w, cons
  * layer's workspace. */
 size_t moe_ffn_workspace_bytes_mxfp8(int T, int d, int d_ff, int E, int k);
 
+/* Where a call of moe_ffn_forward_mxfp4_mxfp8 or moe_ffn_forward_mxfp8_mxfp8
+ * with these sizes leaves the MXFP8 form of the hidden activation h in its
+ * workspace (pure host function).  After the call has run, and until the
+ * workspace is used again, the workspace holds
+ *   at byte *codes_offset:  uint8 [T * k, *row_bytes]: the E4M3 codes of h,
+ *                           one row per (token, slot) pair in expert-sorted
+ *                           order (row r belongs to pair sorted_pair[r] of
+ *                           moe_routing_out), elements d_ff.. zero codes;
+ *   at byte *scales_offset: uint8 [T * k, *row_bytes / 32]: their e8m0 scales.
+ * The down GEMM consumes exactly these codes.  They are what a checker needs
+ * to verify each rounding decision of h (E4M3 keeps 3 mantissa bits, so a
+ * value within fp32 accumulation error of a rounding boundary has two
+ * correct codes).  Output pointers may be NULL.  Errors: MOE_ERR_INVALID_ARG
+ * for sizes outside the limits or T == 0. */
+moe_status moe_ffn_mxfp8_h_layout(int T, int d, int d_ff, int E, int k, size_t* codes_offset,
+                                  size_t* scales_offset, int* row_bytes);
+
 /* MXFP8 conversion of bf16 rows, the activation step of
  * moe_ffn_forward_mxfp4_mxfp8 (OCP Microscaling Formats v1.0: E4M3 elements,
  * one e8m0 scale per 32 consecutive elements of a row).
@@ -282,7 +305,7 @@ typedef struct {
  * more when block->norm_w != NULL).  Same conventions as
  * moe_ffn_workspace_bytes, which it equals for a NULL block. */
 size_t moe_block_workspace_bytes(const moe_block* block, int T, int d, int d_ff, int E, int k,
-                                 moe_dtype dt, int d_ff_shared);
+                                 moe_dtype dt, int grouped, int d_ff_shared);
 
 /* The three layers as blocks: arguments as moe_ffn_forward,
  * moe_ffn_forward_mxfp4 and moe_ffn_forward_grouped, plus `block`.

@@ -63,37 +63,6 @@ struct StageTimer {
   }
 };
 
-// ---- side stream ------------------------------------------------------------
-// The bf16 shared expert of a low-bit layer runs as its own launches of the
-// dense GEMM; they go to a second stream of the device (default priority,
-// created on first use, kept until the process ends), forked after the
-// permutation and joined before the combine, so that its few tiles fill the
-// CUs the routed kernels leave idle instead of running after them.  The
-// fork/join records are made under a lock, so concurrent calls on one device
-// stay ordered; the side stream is shared and serialises their shared-expert
-// work.  Without a side stream the launches stay on the caller's stream.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false, ok = false;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-SideStream* side_stream_locked() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = g_side[dev];
-  if (!ss.tried) {
-    ss.tried = true;
-    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
-  }
-  return ss.ok ? &ss : nullptr;
-}
-
 // ---- checks ----------------------------------------------------------------
 moe_status check_common(const Layer& L) {
   if (L.T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", L.T);
@@ -232,37 +201,21 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   else if (lowbit_format(L.wfmt)) path = kLowbit;
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
-  // A shared expert (bf16) next to many-token routed experts: its tiles go to
-  // their own launches of the dense GEMM, on the side stream when there is
-  // one, so that they fill the CUs the routed launches leave idle (the routed
-  // tiles alone often make whole waves over the CUs).  Low-bit routed experts
-  // always leave them to the dense GEMM; bf16 ones take them in their own
-  // launch when there is no side stream.
-  const bool shared_dense = (path == kLowbit || path == kMfma) && L.has_shared();
-  SideStream* forked = nullptr;
-  if (shared_dense) {
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    SideStream* ss = side_stream_locked();
-    if (ss && hipEventRecord(ss->fork, s) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
-      e = launch_gate_up_mfma_shared(L, W, ss->s);
-      if (e == hipSuccess) e = launch_down_mfma_shared(L, W, ss->s);
-      if (e == hipSuccess) e = hipEventRecord(ss->join, ss->s);
-      if (e != hipSuccess) return fail(MOE_ERR_HIP, "shared expert launch: %s", hipGetErrorString(e));
-      forked = ss;
-    }
-  }
-  const bool shared_forked = forked != nullptr;
-  const bool shared_apart = path == kLowbit || shared_forked;  // shared tiles outside the routed launches
+  // A shared expert (bf16) next to many-token routed experts: bf16 routed
+  // experts take its tiles in their own launches; low-bit routed experts leave
+  // them to launches of the dense bf16 GEMM restricted to the shared expert,
+  // queued after the routed launch on the same stream.
+  const bool shared_apart = path == kLowbit && L.has_shared();
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     if (path == kMx) {
       e = launch_gate_up_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_gate_up_decode(L, W, s)
-          : path == kMfma ? launch_gate_up_mfma(L, W, s, shared_forked)
+          : path == kMfma ? launch_gate_up_mfma(L, W, s, false)
           : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
     }
-    if (e == hipSuccess && shared_dense && shared_apart && !shared_forked) e = launch_gate_up_mfma_shared(L, W, s);
+    if (e == hipSuccess && shared_apart) e = launch_gate_up_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "gate|up launch: %s", hipGetErrorString(e));
   {
@@ -272,19 +225,12 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
       if (e == hipSuccess) e = launch_down_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_down_decode(L, W, s)
-          : path == kMfma ? launch_down_mfma(L, W, s, shared_forked)
+          : path == kMfma ? launch_down_mfma(L, W, s, false)
           : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
     }
-    if (e == hipSuccess && shared_dense && shared_apart && !shared_forked) e = launch_down_mfma_shared(L, W, s);
+    if (e == hipSuccess && shared_apart) e = launch_down_mfma_shared(L, W, s);
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "down launch: %s", hipGetErrorString(e));
-  if (shared_forked) {
-    // join: the combine reads the shared expert's rows.  (A later call's
-    // record of the event waits for at least as much: its side-stream work
-    // is queued after this call's.)
-    e = hipStreamWaitEvent(s, forked->join, 0);
-    if (e != hipSuccess) return fail(MOE_ERR_HIP, "shared expert join: %s", hipGetErrorString(e));
-  }
   {
     StageTimer tm(s, MOE_STAGE_COMBINE);
     e = launch_combine(L, W, s);
@@ -294,6 +240,15 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
 }
 
 }  // namespace
+
+moe_status run_layer(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) { return run(L, ws, ws_bytes, s); }
+
+moe_status set_error(moe_status st, const char* what) {
+  snprintf(g_detail, sizeof(g_detail), "%s", what);
+  return st;
+}
+
+void clear_error() { g_detail[0] = '\0'; }
 
 size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   const size_t P = (size_t)L.T * L.k;
@@ -345,17 +300,19 @@ void apply_block(Layer& L, const moe_block* b) {
 
 extern "C" {
 
-size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int d_ff_shared) {
-  return moe_block_workspace_bytes(nullptr, T, d, d_ff, E, k, dt, d_ff_shared);
+size_t moe_ffn_workspace_bytes(int T, int d, int d_ff, int E, int k, moe_dtype dt, int grouped, int d_ff_shared) {
+  return moe_block_workspace_bytes(nullptr, T, d, d_ff, E, k, dt, grouped, d_ff_shared);
 }
 
 size_t moe_block_workspace_bytes(const moe_block* block, int T, int d, int d_ff, int E, int k, moe_dtype dt,
-                                 int d_ff_shared) {
+                                 int grouped, int d_ff_shared) {
   if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 256 || k < 1 || k > 16 || k > E || d_ff_shared < 0) return (size_t)-1;
   if ((long long)T * k >= (1ll << 26)) return (size_t)-1;
+  if (!grouped && d_ff_shared > 0) return (size_t)-1;  // only group-routed layers have a shared expert
   if (T == 0) return 0;
   Layer L;
   L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k; L.dt = dt;
+  L.grouped = grouped ? 1 : 0;
   L.F_sh = d_ff_shared;
   static const char dummy = 0;
   if (d_ff_shared > 0) L.sh_wg = &dummy;
@@ -432,6 +389,25 @@ size_t moe_ffn_workspace_bytes_mxfp8(int T, int d, int d_ff, int E, int k) {
   L.wfmt = moe::WF_MXFP4; L.mx_act = 1;
   moe::Work W;
   return moe::carve_workspace(L, nullptr, &W);
+}
+
+moe_status moe_ffn_mxfp8_h_layout(int T, int d, int d_ff, int E, int k, size_t* codes_offset,
+                                  size_t* scales_offset, int* row_bytes) {
+  moe::g_detail[0] = '\0';
+  if (moe_ffn_workspace_bytes_mxfp8(T, d, d_ff, E, k) == (size_t)-1)
+    return moe::fail(MOE_ERR_INVALID_ARG, "sizes outside the limits");
+  if (T == 0) return moe::fail(MOE_ERR_INVALID_ARG, "T = 0: the call has no workspace");
+  Layer L;
+  L.T = T; L.d = d; L.F = d_ff; L.E = E; L.k = k; L.dt = MOE_BF16;
+  L.wfmt = moe::WF_MXFP4; L.mx_act = 1;
+  moe::Work W;
+  // carve at a nonzero base: the offsets are the pointers minus the base
+  char* const base = reinterpret_cast<char*>(static_cast<uintptr_t>(1) << 20);
+  moe::carve_workspace(L, base, &W);
+  if (codes_offset) *codes_offset = static_cast<size_t>(reinterpret_cast<char*>(W.hq) - base);
+  if (scales_offset) *scales_offset = static_cast<size_t>(reinterpret_cast<char*>(W.hs) - base);
+  if (row_bytes) *row_bytes = moe::mx_row_bytes(d_ff);
+  return MOE_OK;
 }
 
 moe_status moe_ffn_forward_mxfp4_mxfp8(const void* x, const void* router_w, const void* router_b,

@@ -123,6 +123,13 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W);
 
 int route_block_tokens(const Layer& L);
 
+// Checks L, then enqueues the whole layer on `s` with workspace ws (the body
+// of every forward entry point).
+moe_status run_layer(Layer& L, void* ws, size_t ws_bytes, hipStream_t s);
+// Sets / clears the calling thread's error detail (moe_last_error_detail).
+moe_status set_error(moe_status st, const char* what);
+void clear_error();
+
 // Kernel launchers (each enqueues one kernel on `s`).
 hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s);

@@ -96,16 +96,16 @@ def _mxfp4(rng, E, rows, cols, lo, hi):
 
 
 def _mxfp8(rng, E, rows, cols, lo, hi):
-    """E4M3 codes (sign, exponent field 3..12, mantissa uniform; never the NaN
-    code) and e8m0 scale bytes 127 + [lo, hi] per 32 elements."""
+    """E4M3 codes uniform over the 254 finite codes (both zeros, the
+    subnormals and the largest magnitude 448 included; never a NaN code
+    S.1111.111) and e8m0 scale bytes 127 + [lo, hi] per 32 elements."""
     assert cols % 32 == 0
     codes = np.empty((E, rows, cols), dtype=np.uint8)
     scales = np.empty((E, rows, cols // 32), dtype=np.uint8)
     for e in range(E):
+        mag = rng.integers(0, 127, size=(rows, cols), dtype=np.uint8)     # 0x00 .. 0x7E
         sign = rng.integers(0, 2, size=(rows, cols), dtype=np.uint8)
-        expo = rng.integers(3, 13, size=(rows, cols), dtype=np.uint8)
-        mant = rng.integers(0, 8, size=(rows, cols), dtype=np.uint8)
-        codes[e] = (sign << np.uint8(7)) | (expo << np.uint8(3)) | mant
+        codes[e] = (sign << np.uint8(7)) | mag
         scales[e] = rng.integers(127 + lo, 127 + hi + 1, size=(rows, cols // 32), dtype=np.uint8)
     return codes, scales
 
@@ -175,11 +175,14 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         out["w_down_codes"], out["w_down_scales"] = _mxfp8(rng, E, d, F, lo, hi)
         out["b_down"] = bias(E, d)
     elif w.weights == "nvfp4":
-        # tensor scales 1.5 * 2^-k: every decoded weight is then a bf16 number
+        # fp32 tensor scales with a full 24-bit significand, drawn uniformly in
+        # [1, 2) times 2^-9 (2^-8 for down): decoded weights are generally not
+        # bf16 numbers
         assert dt == "bf16"
         for name, (r_, c_) in (("w_gate", (F, d)), ("w_up", (F, d)), ("w_down", (d, F))):
             out[name + "_codes"], out[name + "_scales"] = _nvfp4(rng, E, r_, c_, 4, 8)
-            out[name + "_tensor_scale"] = np.float32(1.5 * 2.0 ** -(9 if name != "w_down" else 8))
+            m = np.float32(rng.uniform(1.0, 2.0))
+            out[name + "_tensor_scale"] = np.float32(np.ldexp(m, -(9 if name != "w_down" else 8)))
             out["b_" + name[2:]] = bias(E, r_)
     elif w.weights in ("affine4", "affine8"):
         assert dt == "bf16"

@@ -35,7 +35,8 @@ def workspace_for(w: Workload, device="cuda") -> torch.Tensor:
     if w.act_quant == "mxfp8":
         n = moe_ffn.workspace_bytes_mxfp8(w.T, w.d, w.d_ff, w.E, w.k)
     else:
-        n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared, block=blk)
+        n = moe_ffn.workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, dt, w.d_ff_shared, block=blk,
+                                    grouped=w.routing == "grouped")
     return moe_ffn.alloc_workspace(n, device)
 
 

@@ -40,7 +40,7 @@ EXPORTED = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp4
             "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped",
             "moe_block_forward_grouped_affine", "moe_ffn_forward_mxfp4_mxfp8",
             "moe_ffn_workspace_bytes_mxfp8", "moe_mxfp8_quantize", "moe_ffn_forward_mxfp8_mxfp8",
-            "moe_ffn_forward_nvfp4")
+            "moe_ffn_forward_nvfp4", "moe_ffn_mxfp8_h_layout")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -102,7 +102,7 @@ def load() -> ctypes.CDLL:
                                 "`python -m mixture_experts_transformer_router_amd.build`")
     L = ctypes.CDLL(_LIB_PATH)
     L.moe_ffn_workspace_bytes.restype = _Z
-    L.moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+    L.moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I]
     L.moe_ffn_forward.restype = _I
     L.moe_ffn_forward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F,
                                   _P, _I, _P, _Z, _P, _P]
@@ -133,7 +133,9 @@ def load() -> ctypes.CDLL:
                                                    _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _F,
                                                    _P, _P, _Z, _P, _P]
     L.moe_block_workspace_bytes.restype = _Z
-    L.moe_block_workspace_bytes.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I]
+    L.moe_block_workspace_bytes.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _I]
+    L.moe_ffn_mxfp8_h_layout.restype = _I
+    L.moe_ffn_mxfp8_h_layout.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [_I]
     L.moe_last_error_detail.restype = ctypes.c_char_p
@@ -174,14 +176,26 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
-def workspace_bytes(T, d, d_ff, E, k, dtype=MOE_BF16, d_ff_shared=0, block: Optional[MoeBlock] = None) -> int:
+def workspace_bytes(T, d, d_ff, E, k, dtype=MOE_BF16, d_ff_shared=0, block: Optional[MoeBlock] = None,
+                    grouped: bool = False) -> int:
+    """moe_ffn_workspace_bytes (moe_block_workspace_bytes with `block`); grouped: the
+    group-routed layer (implied by a shared expert)."""
+    g = int(bool(grouped) or d_ff_shared > 0)
     if block is None:
-        n = load().moe_ffn_workspace_bytes(T, d, d_ff, E, k, dtype, d_ff_shared)
+        n = load().moe_ffn_workspace_bytes(T, d, d_ff, E, k, dtype, g, d_ff_shared)
     else:
-        n = load().moe_block_workspace_bytes(ctypes.byref(block), T, d, d_ff, E, k, dtype, d_ff_shared)
+        n = load().moe_block_workspace_bytes(ctypes.byref(block), T, d, d_ff, E, k, dtype, g, d_ff_shared)
     if n == ctypes.c_size_t(-1).value:
         raise MoeError(MOE_ERR_UNSUPPORTED, "sizes outside the library's limits")
     return n
+
+
+def mxfp8_h_layout(T, d, d_ff, E, k):
+    """moe_ffn_mxfp8_h_layout: (codes byte offset, scales byte offset, row bytes) of the
+    MXFP8 form of h in the workspace of an MXFP8-activation call."""
+    co, so, rb = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_int(0)
+    _check(load().moe_ffn_mxfp8_h_layout(T, d, d_ff, E, k, ctypes.byref(co), ctypes.byref(so), ctypes.byref(rb)))
+    return co.value, so.value, rb.value
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
@@ -319,7 +333,7 @@ def forward_grouped(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b
     Fs = shared_w_gate.shape[0] if shared_w_gate is not None else 0
     out = torch.empty_like(x) if out is None else out
     ws = workspace if workspace is not None else alloc_workspace(
-        workspace_bytes(T, d, d_ff, E, k, dt, Fs, block=block), x.device)
+        workspace_bytes(T, d, d_ff, E, k, dt, Fs, block=block, grouped=True), x.device)
     r, rs = _routing(T, k, E, x.device, routing)
     st = _entry("moe_ffn_forward_grouped", block)(
         _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(e_score_bias), _ptr(w_gate), _ptr(b_gate),
@@ -342,7 +356,7 @@ def forward_grouped_affine(experts: AffineExperts, x, router_w, router_b, k, n_g
     Fs = shared_w_gate.shape[0] if shared_w_gate is not None else 0
     out = torch.empty_like(x) if out is None else out
     ws = workspace if workspace is not None else alloc_workspace(
-        workspace_bytes(T, d, d_ff, E, k, MOE_BF16, Fs, block=block), x.device)
+        workspace_bytes(T, d, d_ff, E, k, MOE_BF16, Fs, block=block, grouped=True), x.device)
     r, rs = _routing(T, k, E, x.device, routing)
     st = load().moe_block_forward_grouped_affine(
         ctypes.byref(block) if block is not None else None, ctypes.byref(experts),

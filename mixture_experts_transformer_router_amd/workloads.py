@@ -124,8 +124,10 @@ BLOCKS = (GPTOSS_DECODE_BLOCK, GLM4_MOE_LITE_BLOCK, GLM4_DENSE_BLOCK)
 # MXFP8 mode of glm4_moe_lite.go quantizationParams) on the scaled MFMA.
 GPTOSS_MXFP4_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp4_mxfp8act_T4096_d2880_E32_k4", act_quant="mxfp8")
 # MXFP8 expert weights (E4M3 codes, e8m0 scale per 32) with MXFP8 activations.
+# Codes are uniform over the finite E4M3 codes (root mean square ~87), so the
+# scale exponents -16 .. -12 keep the gate and up pre-activations O(1).
 GPTOSS_MXFP8_MX8 = GPTOSS_MXFP4.scaled(name="gptoss20b_mxfp8w_mxfp8act_T4096_d2880_E32_k4", weights="mxfp8",
-                                       act_quant="mxfp8", mx_scale_exp_lo=-13, mx_scale_exp_hi=-9)
+                                       act_quant="mxfp8", mx_scale_exp_lo=-16, mx_scale_exp_hi=-12)
 MX_ACT = (GPTOSS_MXFP4_MX8, GPTOSS_MXFP8_MX8)
 # The MXFP4 layer at decode (8 tokens): weight streaming of the 4.25-bit experts.
 GPTOSS_MXFP4_DECODE = GPTOSS_MXFP4.scaled(T=8, name="gptoss20b_mxfp4_decode_T8_d2880_E32_k4")

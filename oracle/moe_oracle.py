@@ -541,6 +541,37 @@ def experts_forward(arrays: dict, cfg: dict, idx: np.ndarray, w: np.ndarray,
     return out
 
 
+def experts_forward_from_h(arrays: dict, cfg: dict, idx: np.ndarray, w: np.ndarray,
+                           h: np.ndarray) -> np.ndarray:
+    """The second half of the routed layer from given hidden rows:
+
+        out[t] = sum_{j = 0..k-1} w[t, j] * (h[t, j] Wd[idx[t, j]]^T + bd[idx[t, j]])
+
+    ([GLM] SwitchMLP.Forward: the down product of each expert's hidden rows;
+    [GLM] MoE.Forward: the weighted sum over the k slots).  h is float64
+    [n, k, d_ff], the values the down product consumes (for MXFP8 activations,
+    the dequantized E4M3 codes).  Layers with a shared expert or a MoE block
+    are not handled here."""
+    assert cfg.get("block") is None or not cfg.get("block")
+    W = ExpertWeights(arrays, cfg["dtype"], cfg.get("weights", "dense"))
+    assert W.shared() is None
+    n, k = idx.shape
+    Wd0 = W.expert(int(idx.flat[0]))[4] if idx.size else None
+    d = Wd0.shape[0] if Wd0 is not None else 0
+    y = np.zeros((n, k, d), dtype=np.float64)
+    for e in np.unique(idx):
+        t_sel, j_sel = np.nonzero(idx == e)
+        _, _, _, _, Wd, bd = W.expert(int(e))
+        ye = h[t_sel, j_sel] @ Wd.T
+        if bd is not None:
+            ye = ye + bd[None, :]
+        y[t_sel, j_sel] = ye
+    out = np.zeros((n, d), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * y[:, j]
+    return out
+
+
 def moe_layer(arrays: dict, cfg: dict, tokens: Optional[np.ndarray] = None) -> dict:
     """Whole MoE-FFN layer for the given tokens: routing, experts, combine.
     Returns dict(out, logits, idx, w), all float64 / int64."""
@@ -568,23 +599,33 @@ def forced_weights(logits: np.ndarray, idx: np.ndarray, cfg: dict) -> np.ndarray
 # Decision margins (how close a token's expert choice is to a tie).
 
 
+def selection_values(logits: np.ndarray, cfg: dict) -> np.ndarray:
+    """The values a token's expert choice ranks ([GLM] MoEGate.Forward: the
+    choice is made on the scores plus the correction bias when one is given).
+    GPT-OSS routing and grouped routing without a correction bias rank the
+    logits themselves: softmax and sigmoid are increasing in the logit, so the
+    order of the experts, and of the group maxima, is that of the logits.
+    With a correction bias the ranked values are s + e_score_bias."""
+    l = np.asarray(logits, dtype=np.float64)
+    if cfg.get("routing", "gptoss") == "grouped" and cfg.get("e_score_bias") is not None:
+        s = softmax(l) if cfg.get("score", "softmax") == "softmax" else sigmoid(l)
+        return s + np.asarray(cfg["e_score_bias"], dtype=np.float64)[None, :]
+    return l
+
+
 def route_margins(logits: np.ndarray, cfg: dict):
-    """Per-token margins of the routing decision in the space where it is made.
+    """Per-token margins of the routing decision in the space where it is made
+    (selection_values).
 
     Returns (boundary, inner): boundary = gap between the last selected and the
-    best unselected candidate (for grouped routing also the gap at the group
-    boundary, whichever is smaller); inner = smallest gap between consecutive
-    selected experts (decides their order only).  Gaps are measured in logit
-    space (softmax and sigmoid are monotone in the logit), or in score space
-    when a correction bias is in use."""
-    l = np.asarray(logits, dtype=np.float64)
+    best unselected candidate (for grouped routing also the gap between the
+    topk_group-th and the next group score, whichever is smaller); inner =
+    smallest gap between consecutive selected experts (decides their order
+    only)."""
+    l = selection_values(logits, cfg)
     T, E = l.shape
     k = cfg["k"]
     if cfg.get("routing", "gptoss") == "grouped":
-        eb = cfg.get("e_score_bias")
-        if eb is not None:
-            s = softmax(l) if cfg.get("score", "softmax") == "softmax" else sigmoid(l)
-            l = s + np.asarray(eb, dtype=np.float64)[None, :]
         ng, tg = cfg["n_group"], cfg["topk_group"]
         gs = E // ng
         G = l.reshape(T, ng, gs).max(axis=2)

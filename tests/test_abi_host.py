@@ -46,24 +46,43 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     n = lib.moe_ffn_workspace_bytes
-    assert n(0, 2880, 2880, 32, 4, M.MOE_BF16, 0) == 0
-    big = n(8192, 2880, 2880, 32, 4, M.MOE_BF16, 0)
+    assert n(0, 2880, 2880, 32, 4, M.MOE_BF16, 0, 0) == 0
+    big = n(8192, 2880, 2880, 32, 4, M.MOE_BF16, 0, 0)
     P = 8192 * 4
     assert big >= 2 * P * 2880 * 2          # hidden activations + expert outputs (bf16)
     assert big < 2 * P * 2880 * 2 + (8 << 20)
-    assert n(64, 64, 64, 8, 2, M.MOE_F32, 0) > n(64, 64, 64, 8, 2, M.MOE_BF16, 0)
+    assert n(64, 64, 64, 8, 2, M.MOE_F32, 0, 0) > n(64, 64, 64, 8, 2, M.MOE_BF16, 0, 0)
     # bf16 with T <= 16 also holds the router's 16 partial-logit slices [16][16][E] fp32
-    assert n(1, 64, 64, 8, 2, M.MOE_BF16, 0) >= 16 * 16 * 8 * 4 + 2 * (64 + 64) * 2
-    assert n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 1536) > n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 0)
+    assert n(1, 64, 64, 8, 2, M.MOE_BF16, 0, 0) >= 16 * 16 * 8 * 4 + 2 * (64 + 64) * 2
+    assert n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 1, 1536) > n(2048, 2048, 1536, 64, 6, M.MOE_BF16, 1, 0)
     bad = ctypes.c_size_t(-1).value
-    assert n(8, 64, 64, 300, 2, M.MOE_BF16, 0) == bad
-    assert n(8, 64, 64, 8, 9, M.MOE_BF16, 0) == bad
-    assert n(-1, 64, 64, 8, 2, M.MOE_BF16, 0) == bad
+    assert n(8, 64, 64, 300, 2, M.MOE_BF16, 0, 0) == bad
+    assert n(8, 64, 64, 8, 9, M.MOE_BF16, 0, 0) == bad
+    assert n(-1, 64, 64, 8, 2, M.MOE_BF16, 0, 0) == bad
+    # only a group-routed layer has a shared expert; without one the routing kind does not change the size
+    assert n(64, 64, 64, 8, 2, M.MOE_BF16, 0, 64) == bad
+    assert n(64, 64, 64, 8, 2, M.MOE_BF16, 1, 0) == n(64, 64, 64, 8, 2, M.MOE_BF16, 0, 0)
+    assert n(64, 64, 64, 8, 2, M.MOE_BF16, 1, 64) > n(64, 64, 64, 8, 2, M.MOE_BF16, 1, 0)
+
+
+def test_mxfp8_h_layout(lib):
+    # the MXFP8 codes and scales of h lie inside the workspace, after the bf16 h and y rows
+    T, d, F, E, k = 4096, 2880, 2880, 32, 4
+    co, so, rb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int()
+    assert lib.moe_ffn_mxfp8_h_layout(T, d, F, E, k, ctypes.byref(co), ctypes.byref(so), ctypes.byref(rb)) == M.MOE_OK
+    total = lib.moe_ffn_workspace_bytes_mxfp8(T, d, F, E, k)
+    assert rb.value == 2944                             # whole 128-element stages
+    assert co.value % 256 == 0 and so.value % 256 == 0
+    assert co.value >= 2 * T * k * F * 2                # past h and y (bf16)
+    assert co.value + T * k * rb.value <= so.value
+    assert so.value + T * k * rb.value // 32 <= total
+    assert lib.moe_ffn_mxfp8_h_layout(0, d, F, E, k, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_ffn_mxfp8_h_layout(T, d, F, 300, k, None, None, None) == M.MOE_ERR_INVALID_ARG
 
 
 def _fwd(lib, T=16, d=64, F=64, E=8, k=2, alpha=1.702, limit=7.0, dt=M.MOE_BF16, x=FAKE, wr=FAKE,
          wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE2, ws=None, wsb=None):
-    need = lib.moe_ffn_workspace_bytes(max(T, 0), d, F, E, min(k, 16) if k > 0 else 1, dt, 0)
+    need = lib.moe_ffn_workspace_bytes(max(T, 0), d, F, E, min(k, 16) if k > 0 else 1, dt, 0, 0)
     if ws is None:
         ws = FAKE + (1 << 36)
     if wsb is None:
@@ -113,7 +132,7 @@ def test_forward_argument_checks(lib, kw, status):
 
 
 def _grouped(lib, E=64, k=6, ng=8, tg=4, shared=(None, None, None), Fs=0, score=0, act=1, T=16, d=64, F=64):
-    need = lib.moe_ffn_workspace_bytes(T, d, F, E, min(k, 16), M.MOE_BF16, Fs)
+    need = lib.moe_ffn_workspace_bytes(T, d, F, E, min(k, 16), M.MOE_BF16, 1, Fs)
     return lib.moe_ffn_forward_grouped(FAKE, FAKE, None, None, FAKE, None, FAKE, None, FAKE, None,
                                        shared[0], shared[1], shared[2], Fs, T, d, F, E, k, ng, tg, 1, 1.8,
                                        score, act, 1.702, 7.0, FAKE2, M.MOE_BF16, FAKE + (1 << 36), need,
@@ -140,7 +159,7 @@ def test_grouped_argument_checks(lib, kw, status):
 
 def test_mxfp4_argument_checks(lib):
     def call(d=64, F=64, codes=FAKE):
-        need = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0)
+        need = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0, 0)
         return lib.moe_ffn_forward_mxfp4(FAKE, FAKE, None, codes, FAKE, None, FAKE, FAKE, None, FAKE, FAKE,
                                          None, 16, d, F, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36), need,
                                          None, None)
@@ -158,13 +177,13 @@ def test_block_workspace_and_argument_checks(lib):
     nb = lib.moe_block_workspace_bytes
     with_norm = M.MoeBlock(FAKE, 1e-5, 1)
     residual_only = M.MoeBlock(None, 0.0, 1)
-    assert nb(None, 64, 256, 128, 8, 2, M.MOE_BF16, 0) == n(64, 256, 128, 8, 2, M.MOE_BF16, 0)
-    assert nb(ctypes.byref(residual_only), 64, 256, 128, 8, 2, M.MOE_BF16, 0) == n(64, 256, 128, 8, 2, M.MOE_BF16, 0)
+    assert nb(None, 64, 256, 128, 8, 2, M.MOE_BF16, 0, 0) == n(64, 256, 128, 8, 2, M.MOE_BF16, 0, 0)
+    assert nb(ctypes.byref(residual_only), 64, 256, 128, 8, 2, M.MOE_BF16, 0, 0) == n(64, 256, 128, 8, 2, M.MOE_BF16, 0, 0)
     # the normalised rows: T * d elements more
-    assert nb(ctypes.byref(with_norm), 64, 256, 128, 8, 2, M.MOE_BF16, 0) >= n(64, 256, 128, 8, 2, M.MOE_BF16, 0) + 64 * 256 * 2
+    assert nb(ctypes.byref(with_norm), 64, 256, 128, 8, 2, M.MOE_BF16, 0, 0) >= n(64, 256, 128, 8, 2, M.MOE_BF16, 0, 0) + 64 * 256 * 2
 
     def call(block, wsb=None):
-        need = nb(ctypes.byref(block), 16, 64, 64, 8, 2, M.MOE_BF16, 0)
+        need = nb(ctypes.byref(block), 16, 64, 64, 8, 2, M.MOE_BF16, 0, 0)
         return lib.moe_block_forward(ctypes.byref(block), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
                                      16, 64, 64, 8, 2, 1.702, 7.0, FAKE2, M.MOE_BF16, FAKE + (1 << 36),
                                      need if wsb is None else wsb, None, None)
@@ -173,7 +192,7 @@ def test_block_workspace_and_argument_checks(lib):
     assert call(M.MoeBlock(FAKE, float("nan"), 0)) == M.MOE_ERR_INVALID_ARG
     assert call(M.MoeBlock(FAKE, float("inf"), 0)) == M.MOE_ERR_INVALID_ARG
     # a workspace sized for the plain layer is too small once the norm needs its rows
-    plain = n(16, 64, 64, 8, 2, M.MOE_BF16, 0)
+    plain = n(16, 64, 64, 8, 2, M.MOE_BF16, 0, 0)
     assert call(M.MoeBlock(FAKE, 1e-5, 1), wsb=plain) == M.MOE_ERR_WORKSPACE
     # T = 0 is a no-op for blocks too
     assert lib.moe_block_forward(ctypes.byref(with_norm), None, None, None, None, None, None, None, None, None,
@@ -185,7 +204,7 @@ def test_affine_argument_checks(lib):
         ex = M.AffineExperts(bits, *[FAKE] * 9)
         if drop:
             setattr(ex, drop, None)
-        need = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0)
+        need = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0, 0)
         return lib.moe_block_forward_grouped_affine(
             None, ctypes.byref(ex) if experts else None, FAKE, FAKE, None, None, None, None, None, None, None,
             None, 0, 16, d, F, 8, 2, 2, 1, 1, 1.0, 0, 1, 1.702, 7.0, FAKE2, FAKE + (1 << 36), need, None, None)
@@ -200,7 +219,7 @@ def test_affine_argument_checks(lib):
 
 def test_mxfp8_activation_workspace_and_argument_checks(lib):
     nw = lib.moe_ffn_workspace_bytes_mxfp8
-    plain = lib.moe_ffn_workspace_bytes(4096, 2880, 2880, 32, 4, M.MOE_BF16, 0)
+    plain = lib.moe_ffn_workspace_bytes(4096, 2880, 2880, 32, 4, M.MOE_BF16, 0, 0)
     need = nw(4096, 2880, 2880, 32, 4)
     # x and h as codes (rows padded to 128 bytes) plus a scale byte per 32
     assert need >= plain + (4096 + 4096 * 4) * 2944 * 33 // 32
@@ -218,7 +237,7 @@ def test_mxfp8_activation_workspace_and_argument_checks(lib):
     assert call(scales=FAKE + 2) == M.MOE_ERR_INVALID_ARG      # 4-byte aligned scale tensors
     assert call(x=FAKE + 8) == M.MOE_ERR_INVALID_ARG           # 16-byte aligned x
     # the MXFP4 layer's workspace is too small for the MXFP8 copies
-    assert call(wsb=lib.moe_ffn_workspace_bytes(16, 128, 128, 8, 2, M.MOE_BF16, 0)) == M.MOE_ERR_WORKSPACE
+    assert call(wsb=lib.moe_ffn_workspace_bytes(16, 128, 128, 8, 2, M.MOE_BF16, 0, 0)) == M.MOE_ERR_WORKSPACE
     assert call(T=0) == M.MOE_OK
     # MXFP8 weights: the same checks
     n = nw(16, 96, 128, 8, 2)
@@ -244,7 +263,7 @@ def test_mxfp8_quantize_argument_checks(lib):
 
 def test_nvfp4_argument_checks(lib):
     def call(d=128, F=128, ts=1.0, codes=FAKE):
-        n = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0)
+        n = lib.moe_ffn_workspace_bytes(16, d, F, 8, 2, M.MOE_BF16, 0, 0)
         return lib.moe_ffn_forward_nvfp4(FAKE, FAKE, None, codes, FAKE, ts, None, FAKE, FAKE, 1.0, None, FAKE, FAKE,
                                          1.0, None, 16, d, F, 8, 2, 1.702, 7.0, FAKE2, FAKE + (1 << 36), n, None, None)
     assert call(ts=float("nan")) == M.MOE_ERR_INVALID_ARG

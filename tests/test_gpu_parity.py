@@ -27,16 +27,24 @@ def _say(msg):
     sys.stdout.flush()
 
 
+def poisoned_workspace(w):
+    """The layer's workspace filled with 0xFF bytes (NaN in bf16 and fp32, -1
+    as int32): a kernel that reads a piece of it before writing it shows up
+    as a NaN output or a wrong index."""
+    return LY.workspace_for(w, DEV).fill_(0xFF)
+
+
 def _run_and_check(w, a=None, n_out_tokens=512, e_score_bias=None):
     _say(f"[case] {w.name} T={w.T} d={w.d} F={w.d_ff} E={w.E} k={w.k} dtype={w.dtype} "
-         f"weights={w.weights} routing={w.routing} seed={w.seed}")
+         f"weights={w.weights} routing={w.routing} score={w.score} seed={w.seed}")
     a = I.make_inputs(w) if a is None else a
     t = LY.to_device(a, DEV)
     out = torch.full((w.T, w.d), float("nan"), dtype=t["x"].dtype, device=DEV)
     eb = None if e_score_bias is None else torch.from_numpy(np.asarray(e_score_bias, np.float32)).to(DEV)
-    out, r = LY.run(w, t, out=out, routing=True, e_score_bias=eb)
+    ws = poisoned_workspace(w)
+    out, r = LY.run(w, t, out=out, workspace=ws, routing=True, e_score_bias=eb)
     torch.cuda.synchronize()
-    rep = check_layer(w, a, out, r, n_out_tokens=n_out_tokens, e_score_bias=e_score_bias)
+    rep = check_layer(w, a, out, r, n_out_tokens=n_out_tokens, e_score_bias=e_score_bias, workspace=ws)
     _say(f"[ok] {w.name}: {rep}")
     return rep
 
@@ -85,6 +93,35 @@ SMALL = [
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_small_shapes(w):
     _run_and_check(w)
+
+
+# The gate of the GLM page's MoEGate.Forward: sigmoid scores, a correction bias
+# for the selection, no group limit (n_group = topk_group = 1).
+PAGES_GATE = W.GLM4_MOE_LITE.scaled(n_group=1, topk_group=1, score="sigmoid",
+                                    name="glm4moelite_pages_gate_sigmoid_ebias_T2048")
+
+
+def _ebias(w, seed=7, std=0.05):
+    return np.random.default_rng(seed).normal(0, std, w.E)
+
+
+@pytest.mark.parametrize("w", [PAGES_GATE, PAGES_GATE.scaled(T=300, d=256, d_ff=192, d_ff_shared=128,
+                                                              name="pages_gate_small"),
+                               PAGES_GATE.scaled(T=12, d=576, d_ff=96, E=16, k=4, d_ff_shared=160,
+                                                 name="pages_gate_decode_T12")],
+                         ids=lambda w: w.name)
+def test_pages_gate_sigmoid_with_correction_bias(w):
+    _run_and_check(w, n_out_tokens=256 if w.T > 256 else w.T, e_score_bias=_ebias(w))
+
+
+def test_grouped_sigmoid_full_size():
+    w = W.GLM4_MOE_LITE.scaled(score="sigmoid", name="glm4moelite_sigmoid_T2048")
+    _run_and_check(w, n_out_tokens=256)
+
+
+def test_grouped_sigmoid_with_bias_and_groups_full_size():
+    w = W.GLM4_MOE_LITE.scaled(score="sigmoid", name="glm4moelite_sigmoid_ebias_groups_T2048")
+    _run_and_check(w, n_out_tokens=256, e_score_bias=_ebias(w, seed=8))
 
 
 def test_grouped_with_correction_bias():
@@ -167,27 +204,53 @@ def test_deterministic_and_token_permutation_equivariant():
     assert torch.equal(o1[torch.from_numpy(perm).to(DEV)].view(torch.int16), o3.view(torch.int16))
 
 
+DETERMINISM = [
+    W.GPTOSS_DECODE,                        # weight-streaming kernels (bf16)
+    W.GPTOSS_MXFP4_DECODE,                  # weight-streaming kernels on MXFP4 codes
+    W.GPTOSS_MXFP4.scaled(T=600, name="mxfp4_T600"),          # low-bit GEMM (MXFP4)
+    W.GPTOSS_MXFP4_MX8.scaled(T=600, name="mxfp4_mx8_T600"),  # scaled MFMA
+    W.GPTOSS_NVFP4.scaled(T=300, name="nvfp4_T300"),
+    W.GLM4_MOE_LITE_INT4.scaled(T=600, name="int4_T600"),     # affine GEMM + bf16 shared expert
+    W.GLM4_MOE_LITE.scaled(T=600, name="glm_T600"),
+]
+
+
+@pytest.mark.parametrize("w", DETERMINISM, ids=lambda w: w.name)
+def test_repeat_calls_are_bitwise_identical(w):
+    # every path sums in a fixed order: the same call twice gives the same bits
+    _say(f"[case] determinism {w.name} T={w.T}")
+    t = LY.to_device(I.make_inputs(w), DEV)
+    o1 = LY.run(w, t, workspace=poisoned_workspace(w))
+    o2 = LY.run(w, t, workspace=poisoned_workspace(w))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 @pytest.mark.parametrize("base", [W.GLM4_MOE_LITE, W.GLM4_MOE_LITE_INT4], ids=["bf16", "int4"])
-def test_shared_expert_stream_back_to_back_calls(base):
-    # With many tokens the shared expert's GEMMs run on a second stream.  Two
-    # calls on one workspace, queued with no synchronisation between them, must
-    # each match the oracle (the second call's permutation must not overwrite
-    # the tile list while the first call's shared tiles still run), and a third
-    # call on the first inputs must repeat the first output bit for bit.
-    w1 = base.scaled(T=600, d=256, d_ff=192, E=64, k=6, d_ff_shared=192, name=f"shared_stream_{base.weights}")
+def test_interleaved_calls_on_two_caller_streams(base):
+    # Calls on two caller streams, each with its own workspace, queued
+    # alternately with no synchronisation: every call must match the oracle
+    # (the library keeps no state between calls and enqueues only on the
+    # stream it is given), and a repeat of the first call on the other stream
+    # must give the same bits.
+    w1 = base.scaled(T=600, d=256, d_ff=192, E=64, k=6, d_ff_shared=192, name=f"two_streams_{base.weights}")
     w2 = w1.scaled(seed=w1.seed + 1)
-    _say(f"[case] {w1.name} T={w1.T} back-to-back")
+    _say(f"[case] {w1.name} T={w1.T} two streams")
     a1, a2 = I.make_inputs(w1), I.make_inputs(w2)
     t1, t2 = LY.to_device(a1, DEV), LY.to_device(a2, DEV)
-    ws = LY.workspace_for(w1, DEV)
-    outs = [torch.full((w1.T, w1.d), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
-    o1, r1 = LY.run(w1, t1, out=outs[0], workspace=ws, routing=True)
-    o2, r2 = LY.run(w2, t2, out=outs[1], workspace=ws, routing=True)
-    o3 = LY.run(w1, t1, out=outs[2], workspace=ws)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws1, ws2 = poisoned_workspace(w1), poisoned_workspace(w2)
+    outs = [torch.full((w1.T, w1.d), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    torch.cuda.synchronize()
+    o1, r1 = LY.run(w1, t1, out=outs[0], workspace=ws1, routing=True, stream=s1)
+    o2, r2 = LY.run(w2, t2, out=outs[1], workspace=ws2, routing=True, stream=s2)
+    o3 = LY.run(w1, t1, out=outs[2], workspace=ws1, stream=s1)
+    o4 = LY.run(w1, t1, out=outs[3], workspace=ws2, stream=s2)   # after o2 on s2: its workspace is free
     torch.cuda.synchronize()
     check_layer(w1, a1, o1, r1, n_out_tokens=128)
     check_layer(w2, a2, o2, r2, n_out_tokens=128)
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o4.view(torch.int16))
 
 
 def test_zero_tokens_is_noop_and_errors_leave_out_untouched():

@@ -222,6 +222,83 @@ def test_route_margins_hand_case():
     assert abs(b[0] - (2.0 - 1e-7 - 1.0)) < 1e-12 and abs(inner[0] - 1e-7) < 1e-12
 
 
+def test_route_margins_group_boundary_hand_case():
+    # E = 8 in 4 groups of 2; group maxima 5, 4, 4 - 1e-7, 1.  With 2 groups
+    # kept, the group decision is a near-tie (1e-7) while the experts of the
+    # kept groups {0, 1} are 1 apart (k = 1) or 0.1 apart (k = 2).
+    l = np.array([[5.0, 0.0, 4.0, 3.9, 4.0 - 1e-7, -1.0, 1.0, 0.5]])
+    cfg = {"routing": "grouped", "n_group": 4, "topk_group": 2, "k": 2}
+    b, inner = O.route_margins(l, cfg)
+    assert abs(b[0] - 1e-7) < 1e-12 and abs(inner[0] - 1.0) < 1e-12
+    # three groups kept: the group gap is 3 - 1e-7; the experts of groups
+    # {0, 1, 2} are 5, 4, 4 - 1e-7, 3.9, 0, -1
+    cfg3 = dict(cfg, topk_group=3)
+    b, inner = O.route_margins(l, cfg3)
+    assert abs(b[0] - 1e-7) < 1e-12 and abs(inner[0] - 1.0) < 1e-12
+    b, inner = O.route_margins(l, dict(cfg3, k=3))
+    assert abs(b[0] - (0.1 - 1e-7)) < 1e-12 and abs(inner[0] - 1e-7) < 1e-12
+    # all groups kept: plain top-k over the 8 logits
+    b, _ = O.route_margins(l, dict(cfg, topk_group=4, k=4))
+    assert abs(b[0] - (3.9 - 1.0)) < 1e-12
+
+
+def test_route_margins_with_correction_bias_are_in_score_space():
+    # sigmoid(0) = 1/2 for every expert: the logits tie exactly, the biased
+    # scores 0.5 + b do not
+    l = np.zeros((1, 4))
+    cfg = {"routing": "grouped", "n_group": 1, "topk_group": 1, "k": 2, "score": "sigmoid",
+           "e_score_bias": np.array([0.0, 0.1, 0.3, 0.1 - 1e-6])}
+    b, inner = O.route_margins(l, cfg)
+    assert abs(b[0] - 1e-6) < 1e-12 and abs(inner[0] - 0.2) < 1e-12
+    # two groups of 2, one kept: group scores 0.7 and 0.7 - 3e-6
+    cfg = {"routing": "grouped", "n_group": 2, "topk_group": 1, "k": 1, "score": "sigmoid",
+           "e_score_bias": np.array([0.2, 0.0, 0.2 - 3e-6, 0.1])}
+    b, inner = O.route_margins(l, cfg)
+    assert abs(b[0] - 3e-6) < 1e-12 and inner[0] == np.inf
+    # softmax scores: logits (ln 2, 0, 0, 0) give 2/5, 1/5, 1/5, 1/5
+    l2 = np.array([[math.log(2.0), 0.0, 0.0, 0.0]])
+    cfg = {"routing": "grouped", "n_group": 1, "topk_group": 1, "k": 2, "score": "softmax",
+           "e_score_bias": np.array([0.0, 0.1, 0.1 + 2e-6, 0.0])}
+    b, inner = O.route_margins(l2, cfg)
+    assert abs(b[0] - 2e-6) < 1e-12 and abs(inner[0] - (0.1 - 2e-6)) < 1e-12
+    np.testing.assert_allclose(O.selection_values(l2, cfg), [[0.4, 0.3, 0.3 + 2e-6, 0.2]], rtol=1e-15)
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("norm", [True, False])
+@pytest.mark.parametrize("with_bias", [False, True])
+@pytest.mark.parametrize("k", [1, 3])
+def test_forced_weights_are_the_routers_weights(score, norm, with_bias, k):
+    # forced_weights(l, idx) must equal the weights grouped_route gives its own
+    # choice, and, for any other choice, the library softmax / expit of the
+    # chosen logits, renormalised when k > 1 and norm_topk_prob, times rsf
+    rng = np.random.default_rng(21 + 2 * k + norm + 4 * with_bias)
+    T, E, rsf = 40, 16, 1.8
+    l = rng.normal(size=(T, E)) * 2
+    eb = rng.normal(size=E) * 0.05 if with_bias else None
+    cfg = {"routing": "grouped", "k": k, "n_group": 4, "topk_group": 2, "norm_topk_prob": norm,
+           "routed_scaling_factor": rsf, "score": score, "e_score_bias": eb}
+    idx, w = O.grouped_route(l, k, 4, 2, norm, rsf, score, eb)
+    np.testing.assert_allclose(O.forced_weights(l, idx, cfg), w, rtol=1e-14)
+    other = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    s = scipy.special.softmax(l, axis=1) if score == "softmax" else scipy.special.expit(l)
+    ws = np.take_along_axis(s, other, 1)
+    if k > 1 and norm:
+        ws = ws / ws.sum(1, keepdims=True)
+    np.testing.assert_allclose(O.forced_weights(l, other, cfg), ws * rsf, rtol=1e-14)
+
+
+def test_forced_weights_gptoss_are_the_softmax_of_the_chosen_logits():
+    rng = np.random.default_rng(25)
+    l = rng.normal(size=(30, 12)) * 3
+    cfg = {"routing": "gptoss", "k": 4}
+    idx, w = O.gptoss_route(l, 4)
+    np.testing.assert_allclose(O.forced_weights(l, idx, cfg), w, rtol=1e-14)
+    other = np.stack([rng.permutation(12)[:4] for _ in range(30)])
+    np.testing.assert_allclose(O.forced_weights(l, other, cfg),
+                               scipy.special.softmax(np.take_along_axis(l, other, 1), axis=1), rtol=1e-14)
+
+
 # --------------------------------------------------------------------------- permutation
 
 
@@ -584,10 +661,12 @@ def test_nvfp4_blocks_of_16_and_layer_equals_its_dense_layer():
     scales = np.array([[0x38, 0x40], [0x30, 0x48]], np.uint8)  # 1, 2 ; 0.5, 4
     got = O.nvfp4_decode(codes, scales, 1.0)
     np.testing.assert_array_equal(got, np.repeat([[1.0, 2.0], [0.5, 4.0]], 16, axis=1))
-    # the decoded weights are bf16 numbers (tensor scale 1.5 * 2^-k): the NVFP4 layer equals the
-    # float32 dense layer holding them, through the pinned dense path
+    # with tensor scales 1.5 * 2^-k the decoded weights are bf16 numbers: the NVFP4 layer equals
+    # the float32 dense layer holding them, through the pinned dense path
     w = W.GPTOSS_NVFP4.scaled(T=20, d=64, d_ff=96, E=4, k=2, name="pin_nvfp4")
     a = I.make_inputs(w)
+    for name in ("w_gate", "w_up", "w_down"):
+        a[name + "_tensor_scale"] = np.float32(1.5 * 2.0 ** -9)
     ew = O.ExpertWeights(a, "bf16", "nvfp4")
     dense = {k: v for k, v in a.items() if not k.startswith(("w_gate", "w_up", "w_down"))}
     for name, pos in (("w_gate", 0), ("w_up", 2), ("w_down", 4)):
@@ -598,3 +677,19 @@ def test_nvfp4_blocks_of_16_and_layer_equals_its_dense_layer():
         dense[key] = O.to_f64(a[key], "bf16").astype(np.float32)
     c = _cfg(w)
     np.testing.assert_array_equal(O.moe_layer(a, c)["out"], O.moe_layer(dense, dict(c, dtype="f32", weights="dense"))["out"])
+
+
+def test_nvfp4_decode_with_a_general_tensor_scale():
+    # the generator's tensor scales use the whole fp32 significand; the decode is
+    # the exact product e2m1 * e4m3 * tensor scale (float64), factor by factor
+    # against torch's float8_e4m3fn and the e2m1 table
+    w = W.GPTOSS_NVFP4.scaled(T=4, d=64, d_ff=32, E=2, k=1, name="pin_nvfp4_ts")
+    a = I.make_inputs(w)
+    ts = float(a["w_up_tensor_scale"])
+    assert ts != O.round_bf16(np.array([ts]))[0]            # not a bf16 number
+    codes, scales = a["w_up_codes"][1], a["w_up_scales"][1]
+    el = np.empty((codes.shape[0], 2 * codes.shape[1]), np.uint8)
+    el[:, 0::2], el[:, 1::2] = codes & 0x0F, codes >> 4
+    e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])[el]
+    sc = torch.from_numpy(scales).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(O.nvfp4_decode(codes, scales, ts), e2m1 * np.repeat(sc, 16, axis=1) * ts)
