@@ -382,6 +382,35 @@ moe_status moe_block_forward_grouped_affine(const moe_block* block, const moe_af
                                             void* out, void* workspace, size_t workspace_bytes,
                                             moe_routing_out* routing, hipStream_t stream);
 
+/* ---- No-allocation entry point --------------------------------------------
+ * For callers that cannot allocate device memory: work recorded under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.
+ * moe_ffn_forward_noalloc is moe_ffn_forward without the workspace
+ * arguments.  Its workspace is a fixed array in the library's device code of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes: the loader gives every GPU the library
+ * runs on a copy of its own, held until the process ends.  The call
+ * allocates nothing and calls no allocating routine; it runs the same
+ * kernels as moe_ffn_forward, on `stream`, on the stream's GPU (the current
+ * GPU for the null stream).
+ * Limit: a layer whose moe_ffn_workspace_bytes(T, d, d_ff, E, k, dt, 0, 0)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE and launches
+ * nothing (at d = d_ff = 2880, E = 32, k = 4, bf16: T up to about 1400).
+ * Every call on one GPU works in that GPU's single array: calls that can
+ * overlap in time on one GPU (on two streams, or from two threads without
+ * ordering between their streams) race on it and give wrong results; calls
+ * queued on one stream are ordered and safe.  No part of the array needs to
+ * start at zero (every kernel writes what a later kernel reads), and a call
+ * leaves the previous call's contents in it.  Errors as moe_ffn_forward,
+ * plus MOE_ERR_HIP when the array's address cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+moe_status moe_ffn_forward_noalloc(const void* x, const void* router_w, const void* router_b,
+                                   const void* w_gate, const void* b_gate,
+                                   const void* w_up, const void* b_up,
+                                   const void* w_down, const void* b_down,
+                                   int T, int d, int d_ff, int E, int k, float alpha, float limit,
+                                   void* out, moe_dtype dt, moe_routing_out* routing, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 

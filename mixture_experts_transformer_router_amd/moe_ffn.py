@@ -40,7 +40,8 @@ EXPORTED = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp4
             "moe_block_forward", "moe_block_forward_mxfp4", "moe_block_forward_grouped",
             "moe_block_forward_grouped_affine", "moe_ffn_forward_mxfp4_mxfp8",
             "moe_ffn_workspace_bytes_mxfp8", "moe_mxfp8_quantize", "moe_ffn_forward_mxfp8_mxfp8",
-            "moe_ffn_forward_nvfp4", "moe_ffn_mxfp8_h_layout")
+            "moe_ffn_forward_nvfp4", "moe_ffn_mxfp8_h_layout", "moe_ffn_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -106,6 +107,9 @@ def load() -> ctypes.CDLL:
     L.moe_ffn_forward.restype = _I
     L.moe_ffn_forward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F,
                                   _P, _I, _P, _Z, _P, _P]
+    L.moe_ffn_forward_noalloc.restype = _I
+    L.moe_ffn_forward_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F,
+                                          _P, _I, _P, _P]
     L.moe_ffn_forward_mxfp4.restype = _I
     L.moe_ffn_forward_mxfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _I, _I, _I, _I, _I, _F, _F, _P, _P, _Z, _P, _P]
@@ -238,6 +242,22 @@ def forward(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, k
         _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w_gate), _ptr(b_gate), _ptr(w_up), _ptr(b_up),
         _ptr(w_down), _ptr(b_down), T, d, d_ff, E, k, alpha, limit, _ptr(out), dt,
         _ptr(ws), ws.numel(), ctypes.byref(rs) if rs is not None else None, _stream(stream))
+    _check(st)
+    return (out, r) if routing else out
+
+
+def forward_noalloc(x, router_w, router_b, w_gate, b_gate, w_up, b_up, w_down, b_down, k,
+                    alpha=1.702, limit=7.0, out=None, routing=False, stream=None):
+    """moe_ffn_forward_noalloc: moe_ffn_forward with the library's own scratch array as
+    the workspace (no workspace argument)."""
+    T, d = x.shape
+    E, d_ff = w_gate.shape[0], w_gate.shape[1]
+    out = torch.empty_like(x) if out is None else out
+    r, rs = _routing(T, k, E, x.device, routing)
+    st = load().moe_ffn_forward_noalloc(
+        _ptr(x), _ptr(router_w), _ptr(router_b), _ptr(w_gate), _ptr(b_gate), _ptr(w_up), _ptr(b_up),
+        _ptr(w_down), _ptr(b_down), T, d, d_ff, E, k, alpha, limit, _ptr(out), _dt(x),
+        ctypes.byref(rs) if rs is not None else None, _stream(stream))
     _check(st)
     return (out, r) if routing else out
 
