@@ -37,7 +37,7 @@ using namespace gemm;
 
 // Tuning knobs (compile-time; -D overrides for sweeps).
 #ifndef MOE_GEMM_GROUP_M
-#define MOE_GEMM_GROUP_M 4
+#define MOE_GEMM_GROUP_M 8
 #endif
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
@@ -72,22 +72,31 @@ constexpr int kInterleaveLds = MOE_GEMM_INTERLEAVE_LDS;
 // At a tile boundary the first fragments of the next tile are read as one
 // burst right after the barrier (0) or one after each MFMA/copy pair (1).
 constexpr bool kBoundaryReadsInterleaved = MOE_GEMM_BOUNDARY_READS != 0;
+#ifndef MOE_GEMM_WAVES_N
+#define MOE_GEMM_WAVES_N 2
+#endif
+// Wavefronts along N: 2 (4 wavefronts of 128 x 128, one per SIMD) or 4 (8
+// wavefronts of 128 x 64, two per SIMD).
+constexpr int kWavesN = MOE_GEMM_WAVES_N;
 
 
 
 
-// NJ = 32-column result tiles per wavefront (block columns BN = 64 NJ);
-// BK = K elements per stage; NS / NSB = LDS stages of A / B.
-template <bool GATED, int NJ, int BK, int NS, int NSB>
-__global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
-  constexpr int BN = 64 * NJ;
+// NJ = 32-column result tiles per wavefront; WN = wavefronts along N (2 x WN
+// wavefronts, block columns BN = 32 NJ WN); BK = K elements per stage;
+// NS / NSB = LDS stages of A / B.
+template <bool GATED, int NJ, int BK, int NS, int NSB, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void mfma_gemm_kernel(MfmaArgs a) {
+  constexpr int NW = 2 * WN;              // wavefronts
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int BN = 32 * NJ * WN;
   constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
   constexpr int SEG_ROWS = 1024 / (2 * BK);  // rows per 1 KB copy segment
-  constexpr int RA = BM * CPR / kThreads; // copy instructions per wavefront and tile, A
-  constexpr int RB = BN * CPR / kThreads; // same, B
+  constexpr int RA = BM * CPR / NT;       // copy instructions per wavefront and tile, A
+  constexpr int RB = BN * CPR / NT;       // same, B
   static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
   static_assert(NS >= 2 && NSB >= NS && NSB <= NS + 1, "LDS stages");
-  static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "copy rounds");
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "copy rounds");
   static_assert(NS <= 5 && NSB <= 5, "stage variables");
   // One LDS variable per stage: the compiler tells copies into one stage from
   // reads of another only by the variable they address (see the pipeline).
@@ -134,11 +143,11 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   const int r_end = desc.z;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WN, wn = wv % WN;
 
   // ---- copy coordinates.  In round i, wavefront wv fills the 1 KB LDS
-  // segment 4 i + wv: lane l writes 16-byte slot l, i.e. row
-  // SEG_ROWS (4 i + wv) + l / CPR, stored chunk l % CPR, which holds the
+  // segment NW i + wv: lane l writes 16-byte slot l, i.e. row
+  // SEG_ROWS (NW i + wv) + l / CPR, stored chunk l % CPR, which holds the
   // logical chunk that swz() maps there.  Rows past the expert's last row (A)
   // or past N (B) copy a valid row instead: they only feed outputs that the
   // epilogue drops.
@@ -147,14 +156,14 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   int a_row[RA];
 #pragma unroll
   for (int i = 0; i < RA; ++i) {
-    const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int r = SEG_ROWS * (NW * i + wv) + ld_sub;
     const int gr = r0 + r < r_end ? r0 + r : r0;
     a_row[i] = a.row_token ? a.row_token[gr] : gr;
   }
   int b_row[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int r = SEG_ROWS * (NW * i + wv) + ld_sub;
     int wrow, up = 0;
     if constexpr (GATED) {
       const int q = r >> 6, sub = r & 63;
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   // it lands), so the counted waits below are exact.
   // logical chunk that lane slot ld_phys of round i holds (inverse of swz)
   auto ld_chunk_of = [&](int i) __attribute__((always_inline)) {
-    const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int row = SEG_ROWS * (NW * i + wv) + ld_sub;
     return (swz<BK>(row, ld_phys) - row * BK) >> 3;  // XOR is an involution
   };
   // round i of the copies of A / (dense) B tile kt into the stage at As / Bs.
@@ -183,12 +192,12 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   // stubs without a diagnostic.)
   auto copy_a = [&](int kt, uint16_t* As, int i) __attribute__((always_inline)) {
     const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
-    __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (4 * i + wv) * 512, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (NW * i + wv) * 512, 16, 0, 0);
   };
   auto copy_b = [&](int kt, uint16_t* Bs, int i) __attribute__((always_inline)) {
     const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
     const uint16_t* wsrc = (b_row[i] & 1) ? w_up : w_gate;
-    __builtin_amdgcn_global_load_lds(wsrc + (size_t)(b_row[i] >> 1) * K + k, Bs + (4 * i + wv) * 512, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wsrc + (size_t)(b_row[i] >> 1) * K + k, Bs + (NW * i + wv) * 512, 16, 0, 0);
   };
   auto issue_a = [&](int kt, int sa) __attribute__((always_inline)) {
     uint16_t* As = stage_a(sa);
@@ -207,11 +216,11 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
 #pragma unroll
     for (int i = 0; i < RA; ++i)
       if (kt * BK + 8 * ld_chunk_of(i) >= K)
-        *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(As + (NW * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < RB; ++i)
       if (kt * BK + 8 * ld_chunk_of(i) >= K)
-        *reinterpret_cast<u32x4_t*>(Bs + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(Bs + (NW * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
   };
 
   f32x16_t acc[4][NJ];
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(MfmaArgs a) {
   barrier_lds();  // every wavefront is done with the stages before they are reused
 
   // ---- epilogue: bias (+ activation) in registers, bf16 stores
-  store_tile<GATED, NJ>(a, acc, e, shared, N, n0, r0, r_end, wm, wn, lane);
+  store_tile<GATED, NJ, WN>(a, acc, e, shared, N, n0, r0, r_end, wm, wn, lane);
 }
 
 }  // namespace
@@ -409,7 +418,8 @@ hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_firs
   m.ldo = L.F_max();
   m.n_tiles = (L.F_max() + 127) / 128;
   const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
-  mfma_gemm_kernel<true, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
+  if (kWavesN == 4) mfma_gemm_kernel<true, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
+  else mfma_gemm_kernel<true, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   return hipGetLastError();
 }
 
@@ -434,8 +444,9 @@ hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, 
   const bool narrow = t192 * (256 + 192) < t256 * (256 + 256);
   m.n_tiles = narrow ? t192 : t256;
   const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
-  if (narrow) mfma_gemm_kernel<false, 3, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
-  else mfma_gemm_kernel<false, 4, kBK, kStages, kStagesB><<<grid, kThreads, 0, s>>>(m);
+  if (narrow) mfma_gemm_kernel<false, 3, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
+  else if (kWavesN == 4) mfma_gemm_kernel<false, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
+  else mfma_gemm_kernel<false, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   return hipGetLastError();
 }
 }  // namespace

@@ -116,35 +116,52 @@ __device__ __forceinline__ float expert_act_t(float g, float u, float alpha, flo
 }
 
 // Tile of this block.  The real number of row tiles is known only on the
-// device; every block reads the row tiles of its launch's experts
-// [e_first, e_end) (contiguous in the tile list) and the blocks of XCD x
-// take the x-th contiguous share of them, walked kGroupM row tiles at a time,
-// so the blocks resident on one XCD reuse each other's A and B tiles through
-// its L2.  Returns false for blocks without a tile.
+// device; every block reads the row-tile prefix of its launch's experts
+// [e_first, e_end) and the blocks of XCD x take the x-th contiguous share of
+// the launch's tiles.  The tile list runs expert by expert (an expert's
+// row tiles times the column tiles are contiguous in it); inside an expert it
+// is walked kGroupM row tiles at a time, the column tile outermost, so the
+// blocks resident on one XCD at a time cover a few row tiles of ONE expert
+// times several column tiles and reuse each other's A rows and weight panels
+// through that XCD's L2 (a group never mixes two experts' weights).  Returns
+// false for blocks without a tile.
 template <int kGroupM>
 __device__ __forceinline__ bool block_tile(const MfmaArgs& a, int& m_tile, int& n_tile) {
   const int m_lo = a.tile_prefix[a.e_first];
   const int total_m = a.tile_prefix[a.e_end] - m_lo;
-  const int total = total_m * a.n_tiles;
+  const int nt = a.n_tiles;
+  const int total = total_m * nt;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   const int share = (total + kXcds - 1) / kXcds;
   const int L = xcd * share + j;
   if (j >= share || L >= total) return false;
-  const int group = L / (kGroupM * a.n_tiles);
+  // the expert whose tiles hold L: the last e with tile_prefix[e] * nt <= m_lo * nt + L
+  int lo = a.e_first, hi = a.e_end;  // tile_prefix[lo] - m_lo <= L / nt < tile_prefix[hi] - m_lo
+  const int mL = L / nt;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_prefix[mid] - m_lo <= mL) lo = mid;
+    else hi = mid;
+  }
+  const int e_m0 = a.tile_prefix[lo] - m_lo;              // first row tile of the expert (launch-relative)
+  const int e_mt = a.tile_prefix[lo + 1] - m_lo - e_m0;   // its row tiles
+  const int l = L - e_m0 * nt;                            // index inside the expert's tiles
+  const int group = l / (kGroupM * nt);
   const int first_m = group * kGroupM;
-  const int gm = min(kGroupM, total_m - first_m);
-  const int rr = L - group * kGroupM * a.n_tiles;
-  m_tile = m_lo + first_m + rr % gm;
+  const int gm = min(kGroupM, e_mt - first_m);
+  const int rr = l - group * kGroupM * nt;
+  m_tile = m_lo + e_m0 + first_m + rr % gm;
   n_tile = rr / gm;
   return true;
 }
 
-// Epilogue of a 256 x (64 NJ) tile held by 4 wavefronts (2 x 2, each 128 x
-// 32 NJ as 4 x NJ results of 32 x 32): bias (+ activation) and bf16 stores.
-template <bool GATED, int NJ>
+// Epilogue of a 256 x (32 NJ WN) tile held by 2 x WN wavefronts (each
+// 128 x 32 NJ as 4 x NJ results of 32 x 32): bias (+ activation) and bf16
+// stores.
+template <bool GATED, int NJ, int WN = 2>
 __device__ __forceinline__ void store_tile(const MfmaArgs& a, f32x16_t (&acc)[4][NJ], int e, bool shared, int N,
                                            int n0, int r0, int r_end, int wm, int wn, int lane) {
-  constexpr int BN = 64 * NJ;
+  constexpr int BN = 32 * NJ * WN;
   const int fr = lane & 31, fk = lane >> 5;
   // A lane holds one column for 16 rows of each 32 x 32 result; a 4 x 4
   // transpose across each lane quad (two xor shuffles) gives it 4 consecutive
@@ -164,7 +181,7 @@ __device__ __forceinline__ void store_tile(const MfmaArgs& a, f32x16_t (&acc)[4]
   int colj[OJ];
 #pragma unroll
   for (int j = 0; j < OJ; ++j) {
-    colj[j] = GATED ? n0 + 32 * (2 * wn + j) : n0 + wn * 32 * NJ + 32 * j;
+    colj[j] = GATED ? n0 + 32 * (OJ * wn + j) : n0 + wn * 32 * NJ + 32 * j;
     const int c = colj[j] + fr;
     bv0[j] = (bias0 && c < N) ? bf16_to_f32(bias0[(size_t)e * N + c]) : 0.f;
     bv1[j] = (GATED && bias1 && c < N) ? bf16_to_f32(bias1[(size_t)e * N + c]) : 0.f;
