@@ -66,10 +66,11 @@
  *   synchronisation.
  * Limits.  1 <= E <= 256, 1 <= k <= min(E, 16), d and d_ff multiples of 8
  *   (of 32 for MXFP4 weights), T * k < 2^26.
- * Alignment.  x, router_w, the dense expert weights (routed and shared) and
- *   the code tensors are read with 16-byte vector loads and must be 16-byte
- *   aligned; out, the biases, the norm weight, the residual and the affine
- *   scale and bias tables must be aligned to their element size.  Otherwise
+ * Alignment.  x, router_w, the dense expert weights (routed and shared),
+ *   the code tensors and, for bf16 blocks, the RMSNorm weight are read with
+ *   16-byte vector loads and must be 16-byte aligned; out, the biases, the
+ *   residual, the fp32 norm weight and the affine scale and bias tables must
+ *   be aligned to their element size.  Otherwise
  *   MOE_ERR_INVALID_ARG.  (Whole allocations from hipMalloc or torch are.)
  */
 #ifndef MOE_FFN_H
@@ -293,8 +294,12 @@ moe_status moe_ffn_forward_grouped(const void* x, const void* router_w, const vo
  *         taken in fp32 with the combine, then rounded once)
  *
  * where layer() is the plain entry point's computation (routing included).
- * norm_w is a device array [d] of type dt (bf16 for the MXFP4 layer); eps
- * must be finite and >= 0.  A NULL block is the plain layer. */
+ * norm_w is a device array [d] of type dt (bf16 for the MXFP4 layer; bf16
+ * norm weights 16-byte aligned); eps must be finite and >= 0.  A NULL block
+ * is the plain layer.  With bf16 and more than 16 tokens the norm runs
+ * inside the router kernel, which streams the rows anyway and writes the
+ * normalised rows to the workspace for the expert stages; fp32 blocks and
+ * blocks of at most 16 tokens run a norm kernel first. */
 typedef struct {
   const void* norm_w; /* [d] RMSNorm scale; NULL = no norm */
   float eps;          /* RMSNorm epsilon (used when norm_w != NULL) */

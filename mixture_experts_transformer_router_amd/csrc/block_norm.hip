@@ -22,23 +22,6 @@ namespace {
 
 constexpr int kThreads = 512;
 
-// fp64 -> nearest bf16, ties to even, with one rounding.  The fp32 rounding
-// f of v is exact for the decision unless f lies exactly on a bf16 midpoint
-// (low 16 bits 0x8000) while v does not: no midpoint can lie strictly between
-// v and its nearest fp32.  In that case the sign of |v| - |f| decides.
-// Finite values in bf16's normal range (NaN is kept as a quiet NaN).
-__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
-  const float f = static_cast<float>(v);
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  if ((u & 0xffffu) == 0x8000u) {
-    const double rest = fabs(v) - fabs(static_cast<double>(f));
-    if (rest > 0.0) return static_cast<uint16_t>((u + 0x8000u) >> 16);  // magnitude up
-    if (rest < 0.0) return static_cast<uint16_t>(u >> 16);              // magnitude down
-  }
-  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
 template <typename TE> __device__ __forceinline__ void store_f64(TE* p, size_t i, double v);
 template <> __device__ __forceinline__ void store_f64<float>(float* p, size_t i, double v) {
   p[i] = static_cast<float>(v);  // v_cvt_f32_f64: round to nearest even

@@ -21,6 +21,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
+// fp64 -> nearest bf16, ties to even, with one rounding.  The fp32 rounding
+// f of v is exact for the decision unless f lies exactly on a bf16 midpoint
+// (low 16 bits 0x8000) while v does not: no midpoint can lie strictly between
+// v and its nearest fp32.  In that case the sign of |v| - |f| decides.
+// Finite values in bf16's normal range (NaN is kept as a quiet NaN).
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  const float f = static_cast<float>(v);
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  if ((u & 0xffffu) == 0x8000u) {
+    const double rest = fabs(v) - fabs(static_cast<double>(f));
+    if (rest > 0.0) return static_cast<uint16_t>((u + 0x8000u) >> 16);  // magnitude up
+    if (rest < 0.0) return static_cast<uint16_t>(u >> 16);              // magnitude down
+  }
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 template <typename T> __device__ __forceinline__ float load_f32(const T* p, size_t i);
 template <> __device__ __forceinline__ float load_f32<float>(const float* p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p, size_t i) {

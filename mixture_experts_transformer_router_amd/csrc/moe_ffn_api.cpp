@@ -137,6 +137,8 @@ moe_status check_common(const Layer& L) {
   }
   if (L.has_shared() && (off16(L.sh_wg) || off16(L.sh_wu) || off16(L.sh_wd)))
     return fail(MOE_ERR_INVALID_ARG, "the shared expert's weights must be 16-byte aligned");
+  // the bf16 router (many tokens) reads the RMSNorm weight with 16-byte loads
+  if (L.dt == MOE_BF16 && off16(L.norm_w)) return fail(MOE_ERR_INVALID_ARG, "the RMSNorm weight must be 16-byte aligned");
   {
     const size_t el = L.elt();
     const auto off = [](const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; };
@@ -174,12 +176,15 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   {
     StageTimer tm(s, MOE_STAGE_ROUTE);
     e = hipSuccess;
-    if (L.norm_w) {
-      // block prologue: the layer works on RMSNorm(x) from here on
+    // block prologue: the layer works on RMSNorm(x) from here on.  bf16 with
+    // more than 16 tokens: the router normalises the rows it streams and
+    // writes them to W.xn; otherwise a kernel of its own first.
+    if (L.norm_w && (L.dt == MOE_F32 || L.T <= kDecodeMaxTokens)) {
       e = launch_rmsnorm(L, W, s);
       L.x = W.xn;
     }
     if (e == hipSuccess) e = launch_route(L, W, s);
+    if (L.norm_w) L.x = W.xn;
   }
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "route launch: %s", hipGetErrorString(e));
   {

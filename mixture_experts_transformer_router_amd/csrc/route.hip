@@ -11,6 +11,13 @@
 //         stage adds the slices in order and chooses.
 //   fp32: 64 tokens per block on the vector ALUs, the input dimension
 //         streaming through LDS in chunks of 32.
+// MoE block (bf16, many tokens): the RMSNorm in front of the layer is fused
+// into route_mfma_kernel.  A block first sums the squares of its 16 rows in
+// fp64, then normalises each 8-element piece as it loads it for the logits
+// (x * r * w, rounded once to bf16) and stores the normalised rows for the
+// expert stages: x is not read by a norm kernel of its own, and xn is not
+// read back by the router.  (For T <= 16 the split router would need every
+// whole row in each of its blocks; the stand-alone norm kernel runs first.)
 //
 // Choice: see route_common.h.
 #include "route_common.h"
@@ -31,13 +38,14 @@ constexpr int kMfmaTokens = 16;
 // Their partial tiles are added either in wavefront order (sequential) or,
 // with TREE, pairwise in a fixed tree (wave w += wave w + n/2 for n = WAVES,
 // WAVES/2, ..., 2), both independent of timing.
-template <int EG, int WAVES, bool TREE>
+template <int EG, int WAVES, bool TREE, bool NORM>
 __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   constexpr int EP = 16 * EG;
   constexpr int kMfmaWaves = WAVES;
   __shared__ float lg[kMfmaTokens][EP + 1];
   __shared__ float part[TREE ? WAVES / 2 : 1][TREE ? EG * 4 * 64 : 1];
   __shared__ int cnt[EP];
+  __shared__ double ssq[NORM ? WAVES : 1][kMfmaTokens];
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -56,7 +64,8 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   // (always valid) addresses, and masked afterwards, so no load waits behind
   // a branch or another step's MFMA.
   const int steps = (d + 31) / 32;
-  constexpr int B = MOE_ROUTE_UNROLL;
+  // steps per load batch (the fused norm's fp64 products need registers)
+  constexpr int B = NORM ? (MOE_ROUTE_UNROLL > 2 ? 2 : MOE_ROUTE_UNROLL) : MOE_ROUTE_UNROLL;
   const uint16_t* wrow[EG];
   bool e_ok[EG];
 #pragma unroll
@@ -64,6 +73,33 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
     const int e = 16 * g + (lane & 15);
     e_ok[g] = e < E;
     wrow[g] = wr + (size_t)(e_ok[g] ? e : 0) * d;
+  }
+  // fused RMSNorm: the factor of each of the block's 16 rows, from an fp64
+  // sum of squares in a fixed order (a lane's elements, the 4 lanes of a row,
+  // then the wavefronts in order)
+  double rnorm = 0.0;
+  if constexpr (NORM) {
+    double ss = 0.0;
+    for (int s0 = wv; s0 < steps; s0 += B * kMfmaWaves) {
+      bf16x8_t xv[B];
+      bool okn[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int k = 32 * (s0 + u * kMfmaWaves) + 8 * kg;
+        okn[u] = k < d;
+        xv[u] = load_bf16x8(xr + (okn[u] ? k : 0));
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (okn[u]) ss = sumsq8(xv[u], ss);
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (lane < 16) ssq[wv][lane] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int w = 0; w < kMfmaWaves; ++w) tot += ssq[w][lane & 15];
+    rnorm = 1.0 / sqrt(tot / d + static_cast<double>(a.eps));
   }
   for (int s0 = wv; s0 < steps; s0 += B * kMfmaWaves) {
     bf16x8_t av[B], bv[B][EG];
@@ -76,6 +112,16 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
       av[u] = load_bf16x8(xr + kc);
 #pragma unroll
       for (int g = 0; g < EG; ++g) bv[u][g] = load_bf16x8(wrow[g] + kc);
+    }
+    if constexpr (NORM) {
+      // each (row, 8 elements) belongs to one lane of one wavefront: it
+      // normalises them, feeds them to the logits and stores them once
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int k = 32 * (s0 + u * kMfmaWaves) + 8 * kg;
+        av[u] = rms_scale8(av[u], rnorm, a.norm_w + (ok[u] ? k : 0));
+        if (tok_ok && ok[u]) *reinterpret_cast<bf16x8_t*>(a.xn + (size_t)tok * d + k) = av[u];
+      }
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
@@ -244,6 +290,24 @@ __global__ __launch_bounds__(kValuThreads) void route_valu_kernel(RouteArgs a) {
   for (int e = tid; e < E; e += kValuThreads) a.hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
+template <bool NORM>
+void launch_mfma_router(const RouteArgs& a, int E, int nblk, bool wide, hipStream_t s) {
+  // Fewer blocks than CUs (latency-bound): up to 64 experts take 16
+  // wavefronts and a tree sum.  Otherwise 8 wavefronts in wavefront order
+  // (more blocks resident per CU).
+  if (wide) {
+    if (E <= 16) route_mfma_kernel<1, 16, true, NORM><<<nblk, 64 * 16, 0, s>>>(a);
+    else if (E <= 32) route_mfma_kernel<2, 16, true, NORM><<<nblk, 64 * 16, 0, s>>>(a);
+    else route_mfma_kernel<4, 16, true, NORM><<<nblk, 64 * 16, 0, s>>>(a);
+  } else {
+    if (E <= 16) route_mfma_kernel<1, 8, false, NORM><<<nblk, 64 * 8, 0, s>>>(a);
+    else if (E <= 32) route_mfma_kernel<2, 8, false, NORM><<<nblk, 64 * 8, 0, s>>>(a);
+    else if (E <= 64) route_mfma_kernel<4, 8, false, NORM><<<nblk, 64 * 8, 0, s>>>(a);
+    else if (E <= 128) route_mfma_kernel<8, 8, false, NORM><<<nblk, 64 * 8, 0, s>>>(a);
+    else route_mfma_kernel<16, 8, false, NORM><<<nblk, 64 * 8, 0, s>>>(a);
+  }
+}
+
 }  // namespace
 
 int route_block_tokens(const Layer& L) { return L.dt == MOE_F32 ? kValuTokens : kMfmaTokens; }
@@ -264,22 +328,10 @@ hipError_t launch_route(const Layer& L, const Work& W, hipStream_t s) {
     else if (L.E <= 64) route_valu_kernel<16><<<nblk, kValuThreads, 0, s>>>(a);
     else route_valu_kernel<64><<<nblk, kValuThreads, 0, s>>>(a);
   } else {
-    // Fewer blocks than CUs (latency-bound): up to 64 experts take 16
-    // wavefronts and a tree sum.  Otherwise 8 wavefronts in wavefront order
-    // (more blocks resident per CU).
     constexpr bool kTree = MOE_ROUTE_TREE != 0;
     const bool wide = kTree && nblk < 256 && L.E <= 64;
-    if (wide) {
-      if (L.E <= 16) route_mfma_kernel<1, 16, true><<<nblk, 64 * 16, 0, s>>>(a);
-      else if (L.E <= 32) route_mfma_kernel<2, 16, true><<<nblk, 64 * 16, 0, s>>>(a);
-      else route_mfma_kernel<4, 16, true><<<nblk, 64 * 16, 0, s>>>(a);
-    } else {
-      if (L.E <= 16) route_mfma_kernel<1, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
-      else if (L.E <= 32) route_mfma_kernel<2, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
-      else if (L.E <= 64) route_mfma_kernel<4, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
-      else if (L.E <= 128) route_mfma_kernel<8, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
-      else route_mfma_kernel<16, 8, false><<<nblk, 64 * 8, 0, s>>>(a);
-    }
+    if (a.norm_w) launch_mfma_router<true>(a, L.E, nblk, wide, s);
+    else launch_mfma_router<false>(a, L.E, nblk, wide, s);
   }
   return hipGetLastError();
 }

@@ -32,7 +32,45 @@ struct RouteArgs {
   int32_t* hist;
   int32_t* user_idx;
   float* user_w;
+  // MoE block, bf16: RMSNorm of the rows fused into the router (nullptr: no
+  // norm).  The router computes each row's factor, feeds the normalised rows
+  // to its logits and writes them to xn for the expert stages.
+  const uint16_t* norm_w;
+  float eps;
+  uint16_t* xn;
 };
+
+// Fused RMSNorm (glm4_moe_lite.go, MoEBlock.Forward: PostAttentionLayerNorm):
+// 8 consecutive elements x[k .. k+7] of a row with factor r (the row's
+// 1 / sqrt(mean(x^2) + eps), fp64) become x * r * w rounded once from fp64 to
+// bf16 -- the same expression and rounding as the stand-alone norm kernel.
+__device__ __forceinline__ bf16x8_t rms_scale8(bf16x8_t xv, double r, const uint16_t* w8) {
+  const u32x4_t xw = __builtin_bit_cast(u32x4_t, xv);
+  const u32x4_t ww = *reinterpret_cast<const u32x4_t*>(w8);
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t xp = xw[i], wp = ww[i];
+    const uint16_t lo = f64_to_bf16(static_cast<double>(bf16_to_f32(xp & 0xffffu)) * r *
+                                    static_cast<double>(bf16_to_f32(wp & 0xffffu)));
+    const uint16_t hi = f64_to_bf16(static_cast<double>(bf16_to_f32(xp >> 16)) * r *
+                                    static_cast<double>(bf16_to_f32(wp >> 16)));
+    o[i] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+  }
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+// fp64 sum of squares of 8 bf16 elements added to ss in element order
+__device__ __forceinline__ double sumsq8(bf16x8_t xv, double ss) {
+  const u32x4_t xw = __builtin_bit_cast(u32x4_t, xv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double lo = bf16_to_f32(xw[i] & 0xffffu), hi = bf16_to_f32(xw[i] >> 16);
+    ss = fma(lo, lo, ss);
+    ss = fma(hi, hi, ss);
+  }
+  return ss;
+}
 
 // Choose the experts of token t from its logits row `lg` (LDS, E entries;
 // overwritten with selection scores on the grouped path) with one wavefront.
@@ -149,6 +187,10 @@ __device__ void choose_experts(const RouteArgs& a, float* lg, int t, int lane, i
   }
 }
 
+// The few-token path (bf16, T <= kDecodeMaxTokens): split-K router logits,
+// then one kernel that chooses the experts and permutes.
+inline bool few_token_route(const Layer& L) { return L.dt != MOE_F32 && L.T <= kDecodeMaxTokens; }
+
 inline RouteArgs route_args(const Layer& L, const Work& W) {
   RouteArgs a;
   a.x = L.x; a.wr = L.router_w; a.br = L.router_b; a.e_bias = L.e_bias;
@@ -157,12 +199,13 @@ inline RouteArgs route_args(const Layer& L, const Work& W) {
   a.norm = L.norm; a.score = L.score; a.rsf = L.rsf;
   a.idx = W.idx; a.w = W.w; a.hist = W.hist;
   a.user_idx = L.routing.topk_idx; a.user_w = L.routing.topk_w;
+  const bool fuse_norm = L.norm_w != nullptr && L.dt == MOE_BF16 && !few_token_route(L);
+  a.norm_w = fuse_norm ? static_cast<const uint16_t*>(L.norm_w) : nullptr;
+  a.eps = L.eps;
+  a.xn = fuse_norm ? static_cast<uint16_t*>(W.xn) : nullptr;
   return a;
 }
 
-// The few-token path (bf16, T <= kDecodeMaxTokens): split-K router logits,
-// then one kernel that chooses the experts and permutes.
-inline bool few_token_route(const Layer& L) { return L.dt != MOE_F32 && L.T <= kDecodeMaxTokens; }
 
 }  // namespace
 }  // namespace moe
