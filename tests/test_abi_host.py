@@ -191,6 +191,9 @@ def test_block_workspace_and_argument_checks(lib):
     assert b"eps" in lib.moe_last_error_detail()
     assert call(M.MoeBlock(FAKE, float("nan"), 0)) == M.MOE_ERR_INVALID_ARG
     assert call(M.MoeBlock(FAKE, float("inf"), 0)) == M.MOE_ERR_INVALID_ARG
+    # the bf16 router reads the norm weight with 16-byte loads
+    assert call(M.MoeBlock(FAKE + 2, 1e-5, 1)) == M.MOE_ERR_INVALID_ARG
+    assert b"16-byte" in lib.moe_last_error_detail()
     # a workspace sized for the plain layer is too small once the norm needs its rows
     plain = n(16, 64, 64, 8, 2, M.MOE_BF16, 0, 0)
     assert call(M.MoeBlock(FAKE, 1e-5, 1), wsb=plain) == M.MOE_ERR_WORKSPACE
