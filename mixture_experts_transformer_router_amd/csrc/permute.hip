@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxE = 257;  // 256 routed experts + shared
+constexpr int kScanPerLane = (kMaxE + 63) / 64;  // experts per lane in the offset scan
 
 struct PermuteArgs {
   const int32_t* idx;
@@ -30,7 +31,6 @@ struct PermuteArgs {
   int n_hist;           // router blocks
   int hist_per_block;   // router blocks per permute block (64 / router block tokens)
   int T, k, E, shared;
-  int tile_m, tile_m_big;
   int32_t* offsets;
   int32_t* tile_prefix;
   int32_t* tile_prefix_big;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
     for (int t = tid; t < parts * E; t += kThreads) {
       const int e = t % E, part = t / E;
       int tot = 0, bef = 0;
-#pragma unroll 4
+#pragma unroll 16
       for (int i = part; i < a.n_hist; i += parts) {
         const int c = a.hist[(size_t)i * E + e];
         tot += c;
@@ -87,36 +87,55 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
     __syncthreads();
   }
   for (int i = tid; i < 4 * kMaxE; i += kThreads) (&wcnt[0][0])[i] = 0;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) { off[e] = acc; acc += total[e]; }
-    off[E] = acc;
+  // Exclusive scans of the expert counts (off: routed experts, off[E] = all
+  // routed rows) and of their 64- and 256-row tile counts (tile prefixes:
+  // the shared expert, if any, is expert E with T rows).  Wavefront 0, lane l
+  // owning experts kScanPerLane l .. +kScanPerLane-1, a shuffle scan over the
+  // lanes.  Block 0 also writes them out.
+  const int Eall = E + (a.shared ? 1 : 0);
+  if (wv == 0) {
+    int rows[kScanPerLane], tiles[kScanPerLane];
+    int s_rows = 0, s_t64 = 0, s_t256 = 0;
+#pragma unroll
+    for (int v = 0; v < kScanPerLane; ++v) {
+      const int e = lane * kScanPerLane + v;
+      rows[v] = e < E ? total[e] : 0;
+      tiles[v] = e < E ? total[e] : e == E && a.shared ? a.T : 0;
+      s_rows += rows[v];
+      s_t64 += (tiles[v] + kTileM - 1) / kTileM;
+      s_t256 += (tiles[v] + kTileMBig - 1) / kTileMBig;
+    }
+    int i_rows = s_rows, i_t64 = s_t64, i_t256 = s_t256;  // inclusive scans over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int r = __shfl_up(i_rows, o, 64), q = __shfl_up(i_t64, o, 64), u = __shfl_up(i_t256, o, 64);
+      if (lane >= o) { i_rows += r; i_t64 += q; i_t256 += u; }
+    }
+    int o_rows = i_rows - s_rows, o_t64 = i_t64 - s_t64, o_t256 = i_t256 - s_t256;
+#pragma unroll
+    for (int v = 0; v < kScanPerLane; ++v) {
+      const int e = lane * kScanPerLane + v;
+      if (e <= E) off[e] = o_rows;
+      if (e <= Eall) tpb[e] = o_t256;
+      if (b == 0) {
+        if (e <= E) {
+          a.offsets[e] = o_rows;
+          if (a.user_offsets) a.user_offsets[e] = o_rows;
+        }
+        if (e == E && a.shared) a.offsets[E + 1] = o_rows + a.T;
+        if (e <= Eall) {
+          a.tile_prefix[e] = o_t64;
+          a.tile_prefix_big[e] = o_t256;
+        }
+      }
+      o_rows += rows[v];
+      o_t64 += (tiles[v] + kTileM - 1) / kTileM;
+      o_t256 += (tiles[v] + kTileMBig - 1) / kTileMBig;
+    }
   }
   __syncthreads();
 
   if (b == 0) {
-    const int Eall = E + (a.shared ? 1 : 0);
-    for (int e = tid; e <= E; e += kThreads) {
-      a.offsets[e] = off[e];
-      if (a.user_offsets) a.user_offsets[e] = off[e];
-    }
-    if (a.shared && tid == 0) a.offsets[E + 1] = off[E] + a.T;
-    if (tid == 0) {
-      int acc = 0, acc_big = 0;
-      for (int e = 0; e < Eall; ++e) {
-        a.tile_prefix[e] = acc;
-        a.tile_prefix_big[e] = acc_big;
-        tpb[e] = acc_big;
-        const int c = e < E ? total[e] : a.T;
-        acc += (c + a.tile_m - 1) / a.tile_m;
-        acc_big += (c + a.tile_m_big - 1) / a.tile_m_big;
-      }
-      a.tile_prefix[Eall] = acc;
-      a.tile_prefix_big[Eall] = acc_big;
-      tpb[Eall] = acc_big;
-    }
-    __syncthreads();
     // one descriptor per 256-row tile: {expert, first row, end row, 0}
     for (int e = tid; e < Eall; e += kThreads) {
       const int first = tpb[e];
@@ -126,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
       for (int j = 0; j < n; ++j) {
         int32_t* d = a.tile_desc + 4 * (size_t)(first + j);
         d[0] = e;
-        d[1] = r_begin + j * a.tile_m_big;
+        d[1] = r_begin + j * kTileMBig;
         d[2] = r_end;
         d[3] = 0;
       }
@@ -222,8 +241,8 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(RouteArgs ra
       const int e = lane * VPL + v;
       c[v] = e < E ? cnt[e] : 0;
       s_rows += c[v];
-      s_t64 += (c[v] + a.tile_m - 1) / a.tile_m;
-      s_t256 += (c[v] + a.tile_m_big - 1) / a.tile_m_big;
+      s_t64 += (c[v] + kTileM - 1) / kTileM;
+      s_t256 += (c[v] + kTileMBig - 1) / kTileMBig;
     }
     int i_rows = s_rows, i_t64 = s_t64, i_t256 = s_t256;  // inclusive scans over lanes
 #pragma unroll
@@ -244,8 +263,8 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(RouteArgs ra
         a.tile_prefix_big[e] = o_t256;
       }
       o_rows += c[v];
-      o_t64 += (c[v] + a.tile_m - 1) / a.tile_m;
-      o_t256 += (c[v] + a.tile_m_big - 1) / a.tile_m_big;
+      o_t64 += (c[v] + kTileM - 1) / kTileM;
+      o_t256 += (c[v] + kTileMBig - 1) / kTileMBig;
     }
     if (lane == 63) {  // totals: off[E] = P; the shared expert's T rows follow
       off[E] = o_rows;
@@ -257,8 +276,8 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(RouteArgs ra
         a.offsets[E + 1] = o_rows + T;
         a.tile_prefix[E] = t64;
         a.tile_prefix_big[E] = t256;
-        t64 += (T + a.tile_m - 1) / a.tile_m;
-        t256 += (T + a.tile_m_big - 1) / a.tile_m_big;
+        t64 += (T + kTileM - 1) / kTileM;
+        t256 += (T + kTileMBig - 1) / kTileMBig;
         tpb[E + 1] = t256;
       }
       const int Eall = E + (a.shared ? 1 : 0);
@@ -278,7 +297,7 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(RouteArgs ra
     for (int j = 0; j < n; ++j) {
       int32_t* dsc = a.tile_desc + 4 * (size_t)(first + j);
       dsc[0] = e;
-      dsc[1] = r_begin + j * a.tile_m_big;
+      dsc[1] = r_begin + j * kTileMBig;
       dsc[2] = r_end;
       dsc[3] = 0;
     }
@@ -311,8 +330,6 @@ hipError_t launch_permute(const Layer& L, const Work& W, hipStream_t s) {
   a.hist_per_block = kPermuteTokens / rb;
   const int nblk = (L.T + kPermuteTokens - 1) / kPermuteTokens;
   a.shared = L.has_shared() ? 1 : 0;
-  a.tile_m = kTileM;
-  a.tile_m_big = kTileMBig;
   a.offsets = W.offsets; a.tile_prefix = W.tile_prefix; a.tile_prefix_big = W.tile_prefix_big;
   a.tile_desc = W.tile_desc;
   a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
