@@ -29,6 +29,8 @@
 #include <type_traits>
 
 #include "gemm_common.h"
+#include "permute_common.h"
+#include "route_mfma.h"
 
 namespace moe {
 namespace {
@@ -85,8 +87,10 @@ constexpr int kWavesN = MOE_GEMM_WAVES_N;
 // NJ = 32-column result tiles per wavefront; WN = wavefronts along N (2 x WN
 // wavefronts, block columns BN = 32 NJ WN); BK = K elements per stage;
 // NS / NSB = LDS stages of A / B.
+// One block tile: rows [r0, r_end) of expert e (the shared expert is e = E),
+// column tile n_tile.
 template <bool GATED, int NJ, int BK, int NS, int NSB, int WN>
-__global__ __launch_bounds__(128 * WN, 1) void mfma_gemm_kernel(MfmaArgs a) {
+__device__ __forceinline__ void mfma_gemm_tile(const MfmaArgs& a, int e, int r0, int r_end, int n_tile) {
   constexpr int NW = 2 * WN;              // wavefronts
   constexpr int NT = 64 * NW;             // threads
   constexpr int BN = 32 * NJ * WN;
@@ -130,17 +134,11 @@ __global__ __launch_bounds__(128 * WN, 1) void mfma_gemm_kernel(MfmaArgs a) {
     return st == 0 ? lds_b0 : lds_b1;
   };
 
-  int m_tile, n_tile;
-  if (!block_tile<kGroupM>(a, m_tile, n_tile)) return;
-  const int4 desc = reinterpret_cast<const int4*>(a.tile_desc)[m_tile];
-  const int e = desc.x;
   const bool shared = e >= a.E;
   const int N = shared ? a.N_sh : a.N;
   const int K = shared ? a.K_sh : a.K;
   const int n0 = n_tile * (GATED ? BN / 2 : BN);
   if (n0 >= N) return;
-  const int r0 = desc.y;
-  const int r_end = desc.z;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WN, wn = wv % WN;
@@ -158,7 +156,7 @@ __global__ __launch_bounds__(128 * WN, 1) void mfma_gemm_kernel(MfmaArgs a) {
   for (int i = 0; i < RA; ++i) {
     const int r = SEG_ROWS * (NW * i + wv) + ld_sub;
     const int gr = r0 + r < r_end ? r0 + r : r0;
-    a_row[i] = a.row_token ? a.row_token[gr] : gr;
+    a_row[i] = a.row_token ? a.row_token[gr] : gr - a.a_row0;
   }
   int b_row[RB];
 #pragma unroll
@@ -397,10 +395,56 @@ __global__ __launch_bounds__(128 * WN, 1) void mfma_gemm_kernel(MfmaArgs a) {
   store_tile<GATED, NJ, WN>(a, acc, e, shared, N, n0, r0, r_end, wm, wn, lane);
 }
 
+// The tiles of experts [e_first, e_end) in the XCD-aware order, one per block.
+template <bool GATED, int NJ, int BK, int NS, int NSB, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void mfma_gemm_kernel(MfmaArgs a) {
+  int m_tile, n_tile;
+  if (!block_tile<kGroupM>(a, m_tile, n_tile)) return;
+  const int4 desc = reinterpret_cast<const int4*>(a.tile_desc)[m_tile];
+  mfma_gemm_tile<GATED, NJ, BK, NS, NSB, WN>(a, desc.x, desc.y, desc.z, n_tile);
+}
+
+// ---- the shared expert beside the router and the permutation ---------------
+// The shared expert's T rows (sorted rows [P, P + T), P = T k, one per token
+// in token order) need neither the routing nor the permutation.  Its gate|up
+// tiles therefore run in the router's launch and its down tiles in the
+// permutation's, on CUs those leave idle, and the routed launches are whole
+// waves of routed tiles.  The first blocks of such a launch are router (or
+// permutation) blocks; block n_other + i is shared tile i: row tile i % mt,
+// column tile i / mt (mt row tiles: with n_other a multiple of 8, the tiles
+// of one row tile stay on one XCD and share its A panel through that L2).
+template <bool GATED, int NJ>
+__device__ __forceinline__ void shared_tile(const MfmaArgs& a, int i, int P, int T) {
+  const int mt = (T + BM - 1) / BM;
+  const int m = i % mt, n = i / mt;
+  if (n >= a.n_tiles) return;
+  mfma_gemm_tile<GATED, NJ, kBK, 2, 2, 2>(a, a.E, P + BM * m, P + T, n);
+}
+
+// router blocks (4 wavefronts each, tree sum) and the shared expert's gate|up
+template <int EG>
+__global__ __launch_bounds__(256, 1) void route_shared_gate_up_kernel(RouteArgs ra, int n_route, MfmaArgs a, int P, int T) {
+  if ((int)blockIdx.x < n_route) {
+    route_mfma_block<EG, 4, true, false>(ra, blockIdx.x);
+    return;
+  }
+  shared_tile<true, 4>(a, blockIdx.x - n_route, P, T);
+}
+
+// permutation blocks and the shared expert's down product
+template <int NJ>
+__global__ __launch_bounds__(256, 1) void permute_shared_down_kernel(PermuteArgs pa, int n_perm, MfmaArgs a, int P, int T) {
+  if ((int)blockIdx.x < n_perm) {
+    permute_block(pa, blockIdx.x);
+    return;
+  }
+  shared_tile<false, NJ>(a, blockIdx.x - n_perm, P, T);
+}
+
 }  // namespace
 
 namespace {
-hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
+MfmaArgs gate_up_args(const Layer& L, const Work& W, int e_first, int e_end) {
   MfmaArgs m = base_args(L, W);
   m.e_first = e_first;
   m.e_end = e_end;
@@ -417,13 +461,19 @@ hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_firs
   m.out = static_cast<uint16_t*>(W.h);
   m.ldo = L.F_max();
   m.n_tiles = (L.F_max() + 127) / 128;
-  const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
-  if (kWavesN == 4) mfma_gemm_kernel<true, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
-  else mfma_gemm_kernel<true, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
-  return hipGetLastError();
+  return m;
 }
 
-hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
+// Column tile width 192 or 256, whichever copies fewer bytes into LDS:
+// per K step a row tile copies (256 + width) rows for each column tile.
+// (The copies bound this kernel, so padded columns cost less than narrow
+// tiles: d = 2880 takes 12 tiles of 256 rather than 15 of 192.)
+bool down_narrow(const Layer& L) {
+  const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
+  return t192 * (256 + 192) < t256 * (256 + 256);
+}
+
+MfmaArgs down_args(const Layer& L, const Work& W, int e_first, int e_end) {
   MfmaArgs m = base_args(L, W);
   m.e_first = e_first;
   m.e_end = e_end;
@@ -436,15 +486,22 @@ hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, 
   m.N = L.d; m.K = L.F; m.N_sh = L.d; m.K_sh = L.F_sh;
   m.out = static_cast<uint16_t*>(W.y);
   m.ldo = L.d;
-  // Column tile width 192 or 256, whichever copies fewer bytes into LDS:
-  // per K step a row tile copies (256 + width) rows for each column tile.
-  // (The copies bound this kernel, so padded columns cost less than narrow
-  // tiles: d = 2880 takes 12 tiles of 256 rather than 15 of 192.)
-  const int t192 = (L.d + 191) / 192, t256 = (L.d + 255) / 256;
-  const bool narrow = t192 * (256 + 192) < t256 * (256 + 256);
-  m.n_tiles = narrow ? t192 : t256;
+  m.n_tiles = down_narrow(L) ? (L.d + 191) / 192 : (L.d + 255) / 256;
+  return m;
+}
+
+hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
+  const MfmaArgs m = gate_up_args(L, W, e_first, e_end);
   const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
-  if (narrow) mfma_gemm_kernel<false, 3, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
+  if (kWavesN == 4) mfma_gemm_kernel<true, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
+  else mfma_gemm_kernel<true, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
+  return hipGetLastError();
+}
+
+hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
+  const MfmaArgs m = down_args(L, W, e_first, e_end);
+  const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
+  if (down_narrow(L)) mfma_gemm_kernel<false, 3, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   else if (kWavesN == 4) mfma_gemm_kernel<false, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
   else mfma_gemm_kernel<false, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   return hipGetLastError();
@@ -462,6 +519,32 @@ hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t
 }
 hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s) {
   return down_mfma(L, W, s, L.E, L.E + 1);
+}
+
+hipError_t launch_route_shared_gate_up(const Layer& L, const Work& W, hipStream_t s) {
+  const RouteArgs ra = route_args(L, W);
+  const int n_route = (L.T + kMfmaTokens - 1) / kMfmaTokens;
+  MfmaArgs m = gate_up_args(L, W, L.E, L.E + 1);
+  const int P = L.T * L.k;
+  m.row_token = nullptr;  // shared row P + t is token t
+  m.a_row0 = P;
+  const dim3 grid(n_route + (L.T + BM - 1) / BM * m.n_tiles);
+  if (L.E <= 16) route_shared_gate_up_kernel<1><<<grid, 256, 0, s>>>(ra, n_route, m, P, L.T);
+  else if (L.E <= 32) route_shared_gate_up_kernel<2><<<grid, 256, 0, s>>>(ra, n_route, m, P, L.T);
+  else if (L.E <= 64) route_shared_gate_up_kernel<4><<<grid, 256, 0, s>>>(ra, n_route, m, P, L.T);
+  else route_shared_gate_up_kernel<8><<<grid, 256, 0, s>>>(ra, n_route, m, P, L.T);  // E <= kSharedBesideMaxE
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_shared_down(const Layer& L, const Work& W, hipStream_t s) {
+  const PermuteArgs pa = permute_args(L, W);
+  const int n_perm = (L.T + kPermuteTokens - 1) / kPermuteTokens;
+  const MfmaArgs m = down_args(L, W, L.E, L.E + 1);
+  const int P = L.T * L.k;
+  const dim3 grid(n_perm + (L.T + BM - 1) / BM * m.n_tiles);
+  if (down_narrow(L)) permute_shared_down_kernel<3><<<grid, 256, 0, s>>>(pa, n_perm, m, P, L.T);
+  else permute_shared_down_kernel<4><<<grid, 256, 0, s>>>(pa, n_perm, m, P, L.T);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -26,6 +26,7 @@ struct MfmaArgs {
   const uint16_t* a;          // gate|up: x [T, lda]; down: h [rows, lda] (MXFP8: E4M3 codes, lda bytes a row)
   int lda;
   const int32_t* row_token;   // gate|up: token of each sorted row; down: nullptr
+  int a_row0;                 // without row_token: A row of sorted row r is r - a_row0
   const uint16_t* w0;         // dense [E, N, K] (down, or gate)
   const uint16_t* w1;         // dense up
   const uint8_t* c0;          // low-bit codes [E, N, K * bits / 8]; scales: MXFP4 e8m0 bytes

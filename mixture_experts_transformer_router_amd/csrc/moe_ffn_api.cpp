@@ -172,29 +172,6 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   if (overlaps(L.out, (size_t)L.T * L.d * L.elt(), ws, need)) return fail(MOE_ERR_INVALID_ARG, "out overlaps the workspace");
   carve_workspace(L, ws, &W);
 
-  hipError_t e;
-  {
-    StageTimer tm(s, MOE_STAGE_ROUTE);
-    e = hipSuccess;
-    // block prologue: the layer works on RMSNorm(x) from here on.  bf16 with
-    // more than 16 tokens: the router normalises the rows it streams and
-    // writes them to W.xn; otherwise a kernel of its own first.
-    if (L.norm_w && (L.dt == MOE_F32 || L.T <= kDecodeMaxTokens)) {
-      e = launch_rmsnorm(L, W, s);
-      L.x = W.xn;
-    }
-    if (e == hipSuccess) e = launch_route(L, W, s);
-    if (L.norm_w) L.x = W.xn;
-  }
-  if (e != hipSuccess) return fail(MOE_ERR_HIP, "route launch: %s", hipGetErrorString(e));
-  {
-    StageTimer tm(s, MOE_STAGE_PERMUTE);
-    e = launch_permute(L, W, s);
-    // MXFP8 activations: x's conversion is independent of the routing; it is
-    // timed with this stage so that the gate|up stage is the GEMM alone
-    if (e == hipSuccess && L.mx_act) e = launch_mx_quant(L.x, L.d, L.T, L.d, W.xq, W.xs, mx_row_bytes(L.d), s);
-  }
-  if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
   // Expert stages: weight streaming with vector dot products for a few tokens
   // (every expert then holds at most kDecodeMaxTokens rows), grouped MFMA
   // GEMMs otherwise, vector-ALU tiles for fp32.
@@ -206,18 +183,49 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
   else if (lowbit_format(L.wfmt)) path = kLowbit;
   else if (L.T <= kDecodeMaxTokens) path = kDecode;
   else path = kMfma;
-  // A shared expert (bf16) next to many-token routed experts: bf16 routed
-  // experts take its tiles in their own launches; low-bit routed experts leave
-  // them to launches of the dense bf16 GEMM restricted to the shared expert,
-  // queued after the routed launch on the same stream.
-  const bool shared_apart = path == kLowbit && L.has_shared();
+  // A shared expert (bf16) next to many-token routed experts: its gate|up
+  // tiles run in the router's launch and its down tiles in the
+  // permutation's (they need neither), so the routed launches are whole
+  // waves of routed tiles.  A MoE block's router writes the normalised rows
+  // the shared expert reads, so there the shared expert's tiles follow the
+  // routed ones: in the same launches (bf16 experts) or in launches of the
+  // dense bf16 GEMM restricted to the shared expert, queued after the routed
+  // launch on the same stream (low-bit experts).
+  const bool shared_beside = MOE_SHARED_BESIDE && (path == kMfma || path == kLowbit) && L.has_shared() && !L.norm_w &&
+                             L.dt == MOE_BF16 && L.T > kDecodeMaxTokens && L.E <= kSharedBesideMaxE;
+  const bool shared_apart = path == kLowbit && L.has_shared() && !shared_beside;
+  const bool routed_only = shared_beside;
+
+  hipError_t e;
+  {
+    StageTimer tm(s, MOE_STAGE_ROUTE);
+    e = hipSuccess;
+    // block prologue: the layer works on RMSNorm(x) from here on.  bf16 with
+    // more than 16 tokens: the router normalises the rows it streams and
+    // writes them to W.xn; otherwise a kernel of its own first.
+    if (L.norm_w && (L.dt == MOE_F32 || L.T <= kDecodeMaxTokens)) {
+      e = launch_rmsnorm(L, W, s);
+      L.x = W.xn;
+    }
+    if (e == hipSuccess) e = shared_beside ? launch_route_shared_gate_up(L, W, s) : launch_route(L, W, s);
+    if (L.norm_w) L.x = W.xn;
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "route launch: %s", hipGetErrorString(e));
+  {
+    StageTimer tm(s, MOE_STAGE_PERMUTE);
+    e = shared_beside ? launch_permute_shared_down(L, W, s) : launch_permute(L, W, s);
+    // MXFP8 activations: x's conversion is independent of the routing; it is
+    // timed with this stage so that the gate|up stage is the GEMM alone
+    if (e == hipSuccess && L.mx_act) e = launch_mx_quant(L.x, L.d, L.T, L.d, W.xq, W.xs, mx_row_bytes(L.d), s);
+  }
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
   {
     StageTimer tm(s, MOE_STAGE_GATE_UP);
     if (path == kMx) {
       e = launch_gate_up_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_gate_up_decode(L, W, s)
-          : path == kMfma ? launch_gate_up_mfma(L, W, s, false)
+          : path == kMfma ? launch_gate_up_mfma(L, W, s, routed_only)
           : path == kLowbit ? launch_gate_up_lowbit(L, W, s) : launch_gate_up(L, W, s);
     }
     if (e == hipSuccess && shared_apart) e = launch_gate_up_mfma_shared(L, W, s);
@@ -230,7 +238,7 @@ moe_status run(Layer& L, void* ws, size_t ws_bytes, hipStream_t s) {
       if (e == hipSuccess) e = launch_down_mx(L, W, s);
     } else {
       e = path == kDecode ? launch_down_decode(L, W, s)
-          : path == kMfma ? launch_down_mfma(L, W, s, false)
+          : path == kMfma ? launch_down_mfma(L, W, s, routed_only)
           : path == kLowbit ? launch_down_lowbit(L, W, s) : launch_down(L, W, s);
     }
     if (e == hipSuccess && shared_apart) e = launch_down_mfma_shared(L, W, s);

@@ -147,6 +147,17 @@ hipError_t launch_down_lowbit(const Layer& L, const Work& W, hipStream_t s);
 // the dense bf16 GEMMs restricted to the shared expert's tiles
 hipError_t launch_gate_up_mfma_shared(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s);
+// bf16 layers with a shared expert, more than kDecodeMaxTokens tokens, at most
+// kSharedBesideMaxE routed experts and no RMSNorm prologue: the router's
+// launch also runs the shared expert's gate|up tiles, the permutation's
+// launch its down tiles.  (The router block's LDS for more experts does not
+// fit beside the GEMM tile's.)
+constexpr int kSharedBesideMaxE = 128;
+#ifndef MOE_SHARED_BESIDE
+#define MOE_SHARED_BESIDE 1
+#endif
+hipError_t launch_route_shared_gate_up(const Layer& L, const Work& W, hipStream_t s);
+hipError_t launch_permute_shared_down(const Layer& L, const Work& W, hipStream_t s);
 // MXFP8 activations times MXFP4 weights on the scaled MFMA
 hipError_t launch_gate_up_mx(const Layer& L, const Work& W, hipStream_t s);
 hipError_t launch_down_mx(const Layer& L, const Work& W, hipStream_t s);
