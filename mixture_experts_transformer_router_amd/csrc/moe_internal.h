@@ -153,6 +153,8 @@ hipError_t launch_down_mfma_shared(const Layer& L, const Work& W, hipStream_t s)
 // launch its down tiles.  (The router block's LDS for more experts does not
 // fit beside the GEMM tile's.)
 constexpr int kSharedBesideMaxE = 128;
+// 0: the shared expert's tiles always follow the routed ones (kept for
+// timing the two schedules against each other).
 #ifndef MOE_SHARED_BESIDE
 #define MOE_SHARED_BESIDE 1
 #endif

@@ -79,6 +79,16 @@ SMALL = [
     W.GLM4_MOE_LITE.scaled(T=70, d=96, d_ff=64, E=16, k=3, n_group=4, topk_group=2,
                            dtype="f32", act="clipped_swiglu", expert_bias=True, router_bias="normal",
                            d_ff_shared=32, name="glm_f32_clipped_shared"),
+    # the shared expert beside the router and the permutation: one router
+    # block pair and one row tile (T = 17), a shared expert wider than the
+    # routed ones (its column tiles past the routed width), and more routed
+    # experts than that path takes (E = 160: the shared tiles follow the
+    # routed ones)
+    W.GLM4_MOE_LITE.scaled(T=17, d=128, d_ff=64, E=16, k=4, n_group=4, topk_group=2, d_ff_shared=64,
+                           name="glm_T17_shared"),
+    W.GLM4_MOE_LITE.scaled(T=40, d=192, d_ff=64, E=16, k=4, n_group=4, topk_group=2, d_ff_shared=320,
+                           name="glm_T40_wide_shared"),
+    W.GLM4_MOE_LITE.scaled(T=100, d=128, d_ff=64, E=160, k=6, d_ff_shared=64, name="glm_E160_shared"),
     # few-token (weight-streaming) path: K ragged against 512-element chunks,
     # weight rows ragged against the 16-row blocks, 1 .. 16 rows per expert
     W.GPTOSS_DECODE.scaled(T=5, d=520, d_ff=72, E=8, k=3, name="decode_T5_ragged"),
