@@ -101,21 +101,31 @@ def expert_weight_bytes(w):
             + ((2 * w.d_ff + w.d) * eb if w.expert_bias else 0))
 
 
+def shared_beside_router(w):
+    """Whether the library runs the shared expert's tiles in the router's and
+    the permutation's launches (bf16, more than 16 tokens, no RMSNorm
+    prologue, at most 128 routed experts); the timed gate|up stage then holds
+    the routed experts' tiles only."""
+    return bool(w.d_ff_shared) and w.dtype == "bf16" and w.act_quant is None and w.T > 16 \
+        and not w.block and w.E <= 128
+
+
 def algorithmic_gate_up(w, counts):
-    """Bytes and flops one gate|up launch must move / perform.
+    """Bytes and flops one gate|up stage must move / perform.
 
     bytes: gate and up weights and biases of every expert that has rows, the
     token rows (T x d) once, the hidden rows written (rows x d_ff).  flops: 2
-    per multiply-add of the gate and up products (the shared expert's too:
-    its tiles run in the same launch or, for low-bit routed experts, in a
-    launch of its own inside the timed gate|up stage)."""
+    per multiply-add of the gate and up products.  The shared expert counts
+    when its tiles run inside the timed gate|up stage (in the routed launch
+    or, beside low-bit routed experts, a launch of its own), not when they
+    run beside the router."""
     eb = 2 if w.dtype == "bf16" else 4
     active = [e for e, c in enumerate(counts) if c > 0]
     gu_bytes = 2 * matrix_bytes(w, w.d_ff, w.d) + (2 * w.d_ff * eb if w.expert_bias else 0)
     rows = w.P
     nbytes = len(active) * gu_bytes + w.T * w.d * eb + rows * w.d_ff * eb
     flops = 2.0 * rows * 2 * w.d_ff * w.d
-    if w.d_ff_shared:
+    if w.d_ff_shared and not shared_beside_router(w):
         nbytes += 2 * w.d_ff_shared * w.d * eb + w.T * w.d_ff_shared * eb
         flops += 2.0 * w.T * 2 * w.d_ff_shared * w.d
     return nbytes, flops, len(active)
