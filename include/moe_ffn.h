@@ -424,7 +424,11 @@ const char* moe_status_string(moe_status s);
 const char* moe_last_error_detail(void);
 
 /* ---- Opt-in stage timing -------------------------------------------------
- * Stages of one call, in launch order. */
+ * Stages of one call, in launch order.  A shared expert's products are timed
+ * with the gate|up and down stages, except in bf16 calls with more than 16
+ * tokens, at most 128 routed experts and no RMSNorm prologue: there its
+ * gate|up tiles run in the router's launch and its down tiles in the
+ * permutation's, and are timed with those stages. */
 typedef enum {
   MOE_STAGE_ROUTE = 0,    /* (block RMSNorm +) router logits + top-k + weights */
   MOE_STAGE_PERMUTE = 1,  /* per-expert counts, prefix sums, stable scatter */
