@@ -487,8 +487,10 @@ def test_nvfp4_nan_scale():
 
 MXD_CASES = [
     W.GPTOSS_MXFP4_DECODE,
-    # 16 rows per expert: four passes of 4 tokens over the weights
+    # 16 rows per expert: eight passes of 2 tokens over the weights
     W.GPTOSS_MXFP4_DECODE.scaled(T=16, d=512, d_ff=256, E=4, k=4, name="mxfp4_decode_T16_multi_pass"),
+    # 7 tokens over 2 experts: an odd row count ends on a half-filled pass of 2
+    W.GPTOSS_MXFP4_DECODE.scaled(T=7, d=320, d_ff=224, E=2, k=1, name="mxfp4_decode_T7_two_experts"),
     # K ragged against the 2048-element chunks of a wave load, 1..5 rows per expert
     W.GPTOSS_MXFP4_DECODE.scaled(T=5, d=2112, d_ff=160, E=6, k=3, name="mxfp4_decode_T5_ragged_k"),
     W.GPTOSS_MXFP4_DECODE.scaled(T=1, d=256, d_ff=96, E=32, k=4, name="mxfp4_decode_T1"),
