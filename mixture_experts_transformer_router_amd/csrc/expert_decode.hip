@@ -34,11 +34,14 @@
 #ifndef MOE_DECODE_WAVES
 #define MOE_DECODE_WAVES 4
 #endif
+// bf16: weight rows per wavefront and tokens per pass.  2 rows and passes of
+// at most 8 tokens (113 registers: four wavefronts per SIMD in the gated stage)
+// measured 0.7% faster per 8-token layer step than 4 rows and passes of 16.
 #ifndef MOE_DECODE_ROWS
-#define MOE_DECODE_ROWS 4
+#define MOE_DECODE_ROWS 2
 #endif
 #ifndef MOE_DECODE_MAX_TG
-#define MOE_DECODE_MAX_TG 16
+#define MOE_DECODE_MAX_TG 8
 #endif
 // MXFP4: tokens per pass, and how many of a chunk's four 8-element pieces
 // are unrolled (see the MXFP4 shapes below)
