@@ -25,7 +25,7 @@ struct CombineArgs {
   void* out;
 };
 
-// VEC elements per thread per step (8 for bf16 = 16 bytes, 4 for fp32).
+// VEC elements per thread (8 for bf16 = 16 bytes, 4 for fp32).
 template <typename TE, int VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
@@ -41,7 +41,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   if (threadIdx.x == 0) rows[16] = P + t;
   __syncthreads();
   const int nvec = a.d / VEC;
-  for (int v = threadIdx.x; v < nvec; v += kThreads) {
+  // block (t, c) covers vectors c kThreads .. c kThreads + kThreads - 1 of row t
+  {
+    const int v = blockIdx.y * kThreads + threadIdx.x;
+    if (v >= nvec) return;
     float acc[VEC];
 #pragma unroll
     for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
@@ -75,8 +78,12 @@ hipError_t launch_combine(const Layer& L, const Work& W, hipStream_t s) {
   a.T = L.T; a.d = L.d; a.k = L.k; a.shared = L.has_shared() ? 1 : 0;
   a.resid = L.x_resid;
   a.out = L.out;
-  if (L.dt == MOE_F32) combine_kernel<float, 4><<<L.T, kThreads, 0, s>>>(a);
-  else combine_kernel<uint16_t, 8><<<L.T, kThreads, 0, s>>>(a);
+  // one block per token and kThreads vectors of its row: a row of a few
+  // thousand elements takes a few blocks, each thread one vector
+  const int vec = L.dt == MOE_F32 ? 4 : 8;
+  const dim3 grid(L.T, (L.d / vec + kThreads - 1) / kThreads);
+  if (L.dt == MOE_F32) combine_kernel<float, 4><<<grid, kThreads, 0, s>>>(a);
+  else combine_kernel<uint16_t, 8><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
