@@ -97,6 +97,9 @@ SMALL = [
     W.GLM4_MOE_LITE.scaled(T=12, d=576, d_ff=96, E=16, k=4, n_group=4, topk_group=2,
                            d_ff_shared=160, name="glm_decode_T12_shared"),
     W.GLM4_MOE_LITE.scaled(T=3, d=1024, d_ff=256, E=64, k=6, d_ff_shared=40, name="glm_decode_T3"),
+    # rows of 257 16-byte vectors: the combine's second block per token holds one
+    W.GPTOSS_DECODE.scaled(T=3, d=2056, d_ff=64, E=4, k=2, name="decode_T3_d2056"),
+    W.GPTOSS_PREFILL.scaled(T=40, d=2056, d_ff=96, E=4, k=2, name="prefill_T40_d2056"),
 ]
 
 
