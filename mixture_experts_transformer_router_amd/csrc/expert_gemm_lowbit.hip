@@ -58,6 +58,15 @@ namespace {
 using namespace gemm;
 
 constexpr int kGroupM = MOE_MX_GROUP_M;  // row tiles walked together within an XCD
+// Wavefronts along N for MXFP4 weights: 4 (8 wavefronts of 128 x 64, two per
+// SIMD, so one wavefront's waits on LDS and conversions overlap the other's
+// MFMAs) or 2 (4 of 128 x 128).  The other formats keep 2: their decode needs
+// more registers, and at two wavefronts per SIMD they spill (INT4 gate|up 240
+// -> 347 us; MXFP4: 661 -> 656 us, down ~6% faster).
+#ifndef MOE_LOWBIT_MX4_WAVES_N
+#define MOE_LOWBIT_MX4_WAVES_N 4
+#endif
+constexpr int kMx4WavesN = MOE_LOWBIT_MX4_WAVES_N;
 constexpr int BK = 64;                   // K elements per A stage and per decode tile
 constexpr int kCodeRowBytes = 128;       // bytes of a weight row's codes per copy group
 // weight formats
@@ -65,6 +74,10 @@ constexpr int kFmtMx4 = 0, kFmtAff4 = 1, kFmtAff8 = 2, kFmtNv4 = 3;
 // kinds of K-tile step (see tile_step)
 constexpr int kSteady = 0, kGeneral = 1, kLast = 2, kFinal = 3;
 template <int V> using int_c = std::integral_constant<int, V>;
+// Bound of the A row-offset array (its first RA entries are used): an array
+// sized by a local constexpr that depends on a template parameter, captured
+// by a lambda, makes this hipcc's host pass drop the kernel stubs.
+constexpr int kMaxRA = 8;
 
 // Stored position of 16-byte chunk c of code row r in LDS: XOR-swizzled by
 // bits 1..3 of the row, so that the 16-byte reads of any 16 consecutive rows
@@ -114,8 +127,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 // byte b of w as a float (v_cvt_f32_ubyte<b>); b must fold to a constant
 __device__ __forceinline__ float ubyte(uint32_t w, int b) { return static_cast<float>((w >> (8 * b)) & 0xffu); }
 
-template <int FMT, bool GATED, int NJ, bool FAST>
-__global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
+// WN = wavefronts along N (2 x WN wavefronts, each 128 rows x 32 NJ columns).
+template <int FMT, bool GATED, int NJ, bool FAST, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void lowbit_gemm_kernel(MfmaArgs a) {
+  constexpr int NW = 2 * WN;        // wavefronts
+  constexpr int NTH = 64 * NW;      // threads
   constexpr bool MX = FMT == kFmtMx4;
   constexpr bool NV = FMT == kFmtNv4;
   constexpr bool FP4 = MX || NV;                   // e2m1 codes with byte scales
@@ -127,17 +143,17 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   constexpr int EB = FP4 ? 1 : 2;                  // bytes per table element (scale byte / bf16)
   constexpr int SBY = EB * BK * kTilesPerGroup / QG;  // bytes of one row and code group in one table
   constexpr int kScaleDw = (SBY + 3) / 4 + 1;      // aligned dwords that hold them (2-byte aligned start)
-  constexpr int BN = 64 * NJ;
+  constexpr int BN = 32 * NJ * WN;
   constexpr int CPR = BK / 8;               // 16-byte chunks per A row
   constexpr int SEG_ROWS = 1024 / (2 * BK); // A rows per 1 KB copy segment
-  constexpr int RA = BM * CPR / kThreads;   // A copy instructions per wavefront and tile
-  constexpr int RC = BN * kCodeRowBytes / 1024 / 4;  // code copy instructions per wavefront and group
+  constexpr int RA = BM * CPR / NTH;        // A copy instructions per wavefront and tile
+  constexpr int RC = BN * kCodeRowBytes / 1024 / NW;  // code copy instructions per wavefront and group
   static_assert(!GATED || NJ % 2 == 0, "gate|up pairs need an even number of column tiles");
   static_assert(BN * kCodeRowBytes % 4096 == 0, "code copy rounds");
   constexpr int KK = BK / 16;  // MFMA steps per tile
   static_assert(KK == 4, "a lane's 16-byte code piece covers the 4 steps of a tile");
   constexpr int NM = 4 * NJ;   // MFMAs per step
-  constexpr int RS = (BN * kScaleDw + kThreads - 1) / kThreads;  // copy rounds per wavefront, group and table
+  constexpr int RS = (BN * kScaleDw + NTH - 1) / NTH;  // copy rounds per wavefront, group and table
 
   // A stages are separate variables (the compiler tells copies into one from
   // reads of the other only by the variable they address); the steady loop
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   __shared__ uint16_t lds_a0[BM * BK], lds_a1[BM * BK];
   __shared__ uint16_t lds_code[2][BN * kCodeRowBytes / 2];
   // scale tables of two code groups; table t, row r: bytes 4 kScaleDw r .. + 4 kScaleDw - 1
-  __shared__ uint32_t lds_scale[2][NT][SCALE_LDS ? RS * kThreads : 1];
+  __shared__ uint32_t lds_scale[2][NT][SCALE_LDS ? RS * NTH : 1];
   auto stage_a = [&](int st) __attribute__((always_inline)) -> uint16_t* { return st == 0 ? lds_a0 : lds_a1; };
 
   int m_tile, n_tile;
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   const int r_end = desc.z;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WN, wn = wv % WN;
   const int fr = lane & 31, fk = lane >> 5;
 
   // B row r of the block is weight row n0 + 32 (r / 64) + r % 32 of the gate
@@ -170,15 +186,16 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   auto clamp_row = [&](int wrow) __attribute__((always_inline)) { return wrow < N ? wrow : n0; };
 
   // ---- copy coordinates (as the dense kernel: in round i wavefront wv fills
-  // the 1 KB LDS segment 4 i + wv, lane l its 16-byte slot l).
+  // the 1 KB LDS segment NW i + wv, lane l its 16-byte slot l).
   const int ld_sub = lane / CPR;
   const int ld_phys = lane % CPR;
   // element offset of each copied A row (the A operand is under 2^31
   // elements; the library checks)
-  uint32_t a_row[RA];
+  static_assert(RA <= kMaxRA, "A copy rounds");
+  uint32_t a_row[kMaxRA];
 #pragma unroll
   for (int i = 0; i < RA; ++i) {
-    const int r = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int r = SEG_ROWS * (NW * i + wv) + ld_sub;
     const int gr = r0 + r < r_end ? r0 + r : r0;
     a_row[i] = (uint32_t)(a.row_token ? a.row_token[gr] : gr) * (uint32_t)a.lda;
   }
@@ -196,17 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   const uint16_t* const qb_gate = FP4 ? nullptr : a.qb0 + (size_t)e * N * (K / QG);
   const uint16_t* const qb_up = !FP4 && GATED ? a.qb1 + (size_t)e * N * (K / QG) : qb_gate;
   // Code copy round i: lane l copies stored chunk l % 8 of B row
-  // 32 i + code_r (code_r = 8 wv + l / 8 < 32), i.e. weight row
-  // n0 + 32 (i / 2) + code_r of the gate (i even) or up (i odd) tensor in the
-  // gate|up stage, n0 + 32 i + code_r otherwise.  Bits 1..3 of the B row do
-  // not depend on i, nor does the logical chunk the slot holds.
+  // r = 8 NW i + code_r (code_r = 8 wv + l / 8 < 8 NW), i.e. weight row
+  // n0 + 32 (r / 64) + r % 32 of the gate (r % 64 < 32) or up tensor in the
+  // gate|up stage, n0 + r otherwise.  Bits 1..3 of the B row do not depend
+  // on i, nor does the logical chunk the slot holds.
   const int code_r = 8 * wv + (lane >> 3);
   const uint32_t code_lane = 16u * (uint32_t)code_chunk(code_r, lane & 7);
   // this lane's fragment rows: B row wn 32 NJ + 32 j + fr of the block, i.e.
-  // weight row n0 + 64 wn + 32 (j / 2) + fr of the gate (j even) or up tensor
-  // in the gate|up stage, n0 + 32 NJ wn + 32 j + fr otherwise
+  // weight row n0 + 16 NJ wn + 32 (j / 2) + fr of the gate (j even) or up
+  // tensor in the gate|up stage, n0 + 32 NJ wn + 32 j + fr otherwise
   auto frag_row = [&](int j) __attribute__((always_inline)) {
-    return GATED ? n0 + 64 * wn + 32 * (j / 2) + fr : n0 + 32 * NJ * wn + 32 * j + fr;
+    return GATED ? n0 + 16 * NJ * wn + 32 * (j / 2) + fr : n0 + 32 * NJ * wn + 32 * j + fr;
   };
   const int code_off0 = (wn * 32 * NJ + fr) * (kCodeRowBytes / 2);  // uint16 offset of fragment row j = 0
   const int code_x = (wn * 32 * NJ + fr) >> 1 & 7;  // row hash of the fragment rows (32 j keeps it)
@@ -215,10 +232,10 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
   const int tail_tile = (K % BK) != 0 ? ktiles - 1 : -1;
 
   auto copy_a = [&](int kt, uint16_t* As, int i) __attribute__((always_inline)) {
-    const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
+    const int row = SEG_ROWS * (NW * i + wv) + ld_sub;
     const int chunk = (swz<BK>(row, ld_phys) - row * BK) >> 3;  // logical chunk of this slot
     const int k = min(kt * BK + 8 * chunk, K - 8);
-    __builtin_amdgcn_global_load_lds(a.a + (a_row[i] + (uint32_t)k), As + (4 * i + wv) * 512, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.a + (a_row[i] + (uint32_t)k), As + (NW * i + wv) * 512, 16, 0, 0);
   };
   auto issue_a = [&](int kt, int sa) __attribute__((always_inline)) {
     uint16_t* As = stage_a(sa);
@@ -233,9 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
     const uint32_t piece = base + code_lane + 16 <= (uint32_t)code_bytes ? base + code_lane : 0u;
 #pragma unroll
     for (int i = 0; i < RC; ++i) {
-      const int wrow = clamp_row(GATED ? n0 + 32 * (i / 2) + code_r : n0 + 32 * i + code_r);
-      const uint8_t* src = (GATED && (i & 1)) ? code_up : code_gate;
-      __builtin_amdgcn_global_load_lds(src + ((uint32_t)wrow * (uint32_t)code_bytes + piece), Cs + (4 * i + wv) * 512, 16, 0, 0);
+      const int r = 8 * NW * i + code_r;
+      const int wrow = clamp_row(GATED ? n0 + 32 * (r >> 6) + (r & 31) : n0 + r);
+      const uint8_t* src = (GATED && (r & 63) >= 32) ? code_up : code_gate;
+      __builtin_amdgcn_global_load_lds(src + ((uint32_t)wrow * (uint32_t)code_bytes + piece), Cs + (NW * i + wv) * 512, 16, 0, 0);
     }
   };
   // Tensor t of the scale tables (MXFP4: e8m0 scales; affine: scales, then
@@ -259,13 +277,13 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
       const uintptr_t end_up = t_up - (size_t)e * N * (K / QG) * EB + tensor_bytes - 4;
 #pragma unroll
       for (int i = 0; i < RS; ++i) {
-        const int q = 64 * (4 * i + wv) + lane;
+        const int q = 64 * (NW * i + wv) + lane;
         const int r = min(q / kScaleDw, BN - 1);
         const bool up = GATED && (r & 63) >= 32;
         const int wrow = clamp_row(GATED ? n0 + 32 * (r >> 6) + (r & 31) : n0 + r);
         const uintptr_t row = (up ? t_up : t_gate) + (size_t)wrow * (K / QG) * EB + (size_t)SBY * g;
         const uintptr_t dw = min((row & ~(uintptr_t)3) + 4 * (q % kScaleDw), up ? end_up : end_gate);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dw), Ss + 64 * (4 * i + wv), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(dw), Ss + 64 * (NW * i + wv), 4, 0, 0);
       }
     }
   };
@@ -394,10 +412,10 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
     uint16_t* As = stage_a(sa);
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
-      const int row = SEG_ROWS * (4 * i + wv) + ld_sub;
+      const int row = SEG_ROWS * (NW * i + wv) + ld_sub;
       const int chunk = (swz<BK>(row, ld_phys) - row * BK) >> 3;
       if (kt * BK + 8 * chunk >= K)
-        *reinterpret_cast<u32x4_t*>(As + (4 * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(As + (NW * i + wv) * 512 + 8 * lane) = u32x4_t{0u, 0u, 0u, 0u};
     }
   };
 
@@ -611,7 +629,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowbit_gemm_kernel(MfmaArgs a) {
     for (; kt < ktiles; ++kt) tile_step(kt, int_c<kGeneral>{}, int_c<-1>{});
   }
 
-  store_tile<GATED, NJ>(a, acc, e, false, N, n0, r0, r_end, wm, wn, lane);
+  store_tile<GATED, NJ, WN>(a, acc, e, false, N, n0, r0, r_end, wm, wn, lane);
 }
 
 // The FAST kernel applies when K % 64 == 0 and the scale tensors (MXFP4:
@@ -626,18 +644,26 @@ bool fast_shape(const Layer& L, int K, int N, const void* scales, const void* bi
   return bytes % 4 == 0 && aligned(scales) && (mx || aligned(biases));
 }
 
-template <int FMT, bool GATED, int NJ>
+template <int FMT, bool GATED, int NJ, int WN>
 void launch_fmt(const MfmaArgs& m, dim3 grid, bool fast, hipStream_t s) {
-  if (fast) lowbit_gemm_kernel<FMT, GATED, NJ, true><<<grid, kThreads, 0, s>>>(m);
-  else lowbit_gemm_kernel<FMT, GATED, NJ, false><<<grid, kThreads, 0, s>>>(m);
+  if (fast) lowbit_gemm_kernel<FMT, GATED, NJ, true, WN><<<grid, 128 * WN, 0, s>>>(m);
+  else lowbit_gemm_kernel<FMT, GATED, NJ, false, WN><<<grid, 128 * WN, 0, s>>>(m);
 }
 
+// NJ = 32-column results per wavefront with WN = 2: 4 (256 columns a tile) or
+// 3 (192).  MXFP4 256-column tiles may run as 8 wavefronts of 128 x 64.
 template <bool GATED, int NJ>
 void launch_any(const Layer& L, const MfmaArgs& m, dim3 grid, bool fast, hipStream_t s) {
-  if (L.wfmt == WF_MXFP4) launch_fmt<kFmtMx4, GATED, NJ>(m, grid, fast, s);
-  else if (L.wfmt == WF_NVFP4) launch_fmt<kFmtNv4, GATED, NJ>(m, grid, fast, s);
-  else if (L.wfmt == WF_AFF4) launch_fmt<kFmtAff4, GATED, NJ>(m, grid, fast, s);
-  else launch_fmt<kFmtAff8, GATED, NJ>(m, grid, fast, s);
+  if (L.wfmt == WF_MXFP4) {
+    if constexpr (NJ == 4 && kMx4WavesN == 4) launch_fmt<kFmtMx4, GATED, 2, 4>(m, grid, fast, s);
+    else launch_fmt<kFmtMx4, GATED, NJ, 2>(m, grid, fast, s);
+  } else if (L.wfmt == WF_NVFP4) {
+    launch_fmt<kFmtNv4, GATED, NJ, 2>(m, grid, fast, s);
+  } else if (L.wfmt == WF_AFF4) {
+    launch_fmt<kFmtAff4, GATED, NJ, 2>(m, grid, fast, s);
+  } else {
+    launch_fmt<kFmtAff8, GATED, NJ, 2>(m, grid, fast, s);
+  }
 }
 
 }  // namespace
