@@ -17,17 +17,19 @@
 // owns kRowsPerWave * kWaves rows of one expert.  Blocks of experts without
 // rows exit at once.
 //
-// MXFP4 weights (e2m1 codes, an e8m0 scale per 32): a lane takes 32
-// consecutive elements of a row per 2048-element chunk, i.e. 16 bytes of
-// codes (a wavefront load is still one contiguous kilobyte) under exactly one
+// MXFP4 weights (e2m1 codes, an e8m0 scale per 32): a lane takes blocks of
+// 32 consecutive elements of a row, i.e. 16 bytes of codes under exactly one
 // scale byte; v_cvt_scalef32_pk_bf16_fp4 turns each 8-element piece into bf16
-// (exact: e2m1 times a power of two) for the same dot products.
+// (exact: e2m1 times a power of two) for the same dot products.  A row is
+// shared by 64, 32 or 16 lanes, whichever leaves the fewest idle lanes in a
+// row's last step (decode_pass_fp4); a wavefront load then covers 1024, 512
+// or 256 contiguous bytes of each of 1, 2 or 4 rows.
 //
 // After the reduction loop every lane holds partial sums of all
-// (row, token) outputs; a reduce-scatter over the 64 lanes (halving the value
-// set at each of the 6 exchange steps, DPP within 16 lanes, lane shuffles
-// across) leaves each output summed over the whole wavefront in one lane, in a
-// fixed order, so the result does not depend on timing.
+// (row, token) outputs; a reduce-scatter over the lanes of a row (halving the
+// value set at each exchange step, DPP within 16 lanes, lane shuffles across)
+// leaves each output summed over those lanes in one lane, in a fixed order,
+// so the result does not depend on timing.
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -128,10 +130,12 @@ __device__ __forceinline__ float exchange(float v) {
 // half of the values selected by the lane's decision bit and adds the
 // partner's copy of that half; once one value is left the remaining steps add
 // the partner's value.  Afterwards v[0 .. max(C/64, 1)) hold whole-wavefront
-// sums (see value_index).
-template <int J, int C>
+// sums (see lane_bits).  With JN < 6 only the first JN steps run: the sums are
+// then over the lanes that agree in the remaining bits (lane bit 5 for JN = 5,
+// bits 4 and 5 for JN = 4), i.e. over each 32- or 16-lane group.
+template <int J, int C, int JN = 6>
 __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
-  if constexpr (J < 6) {
+  if constexpr (J < JN) {
     const bool hi = (lane >> kDecisionBit[J]) & 1;
     if constexpr (C > 1) {
       constexpr int H = C / 2;
@@ -141,35 +145,35 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
         const float send = hi ? v[i] : v[H + i];
         v[i] = keep + exchange<J>(send);
       }
-      reduce_scatter<J + 1, H>(v, lane);
+      reduce_scatter<J + 1, H, JN>(v, lane);
     } else {
       v[0] += exchange<J>(v[0]);
-      reduce_scatter<J + 1, 1>(v, lane);
+      reduce_scatter<J + 1, 1, JN>(v, lane);
     }
   }
 }
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-// After reduce_scatter of V values, lane `lane` holds in v[i] the value with
-// index lane_bits * max(V/64, 1) + i, where lane_bits collects the decision
-// bits of the first min(log2 V, 6) steps, most significant first.  Lanes that
-// differ only in the other bits hold the same sums; the one with those bits
-// zero is the owner.
-template <int V>
+// After reduce_scatter of V values (JN steps), lane `lane` holds in v[i] the
+// value with index lane_bits * max(V/2^JN, 1) + i, where lane_bits collects the
+// decision bits of the first min(log2 V, JN) steps, most significant first.
+// Lanes that differ only in the other decision bits of those JN steps hold the
+// same sums; the one with those bits zero is the owner.
+template <int V, int JN = 6>
 __device__ __forceinline__ int lane_bits(int lane) {
-  constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
+  constexpr int S = ilog2(V) < JN ? ilog2(V) : JN;
   int b = 0;
 #pragma unroll
   for (int j = 0; j < S; ++j) b = (b << 1) | ((lane >> kDecisionBit[j]) & 1);
   return b;
 }
-template <int V>
+template <int V, int JN = 6>
 __device__ __forceinline__ bool lane_owns(int lane) {
-  constexpr int S = ilog2(V) < 6 ? ilog2(V) : 6;
+  constexpr int S = ilog2(V) < JN ? ilog2(V) : JN;
   bool own = true;
 #pragma unroll
-  for (int j = S; j < 6; ++j) own = own && !((lane >> kDecisionBit[j]) & 1);
+  for (int j = S; j < JN; ++j) own = own && !((lane >> kDecisionBit[j]) & 1);
   return own;
 }
 
@@ -188,9 +192,59 @@ __device__ __forceinline__ u32x4_t fp4_word_bf16(uint32_t w, float scale) {
   return r;
 }
 
-// One pass over the wavefront's weight rows for token slots t0 .. t0+TG-1
-// of the expert (slots >= m contribute zeros and are not stored).
-template <bool GATED, int TG, bool FP4, int R>
+// Bias, activation and bf16 store of a pass's outputs after the reduction.
+// Value index ((g S + s) TG + t): tensor g (gate 0, up 1), row slot s, token
+// slot t.  Row slot s of the wavefront covers rows nw + s RPS + (0 .. RPS-1),
+// one per group of LPR lanes (lane / LPR picks the row; RPS = 64 / LPR).
+template <bool GATED, int TG, int S, int LPR>
+__device__ __forceinline__ void store_pass(const DecodeArgs& a, float* v, int e, bool shared, int N, int nw, int m0,
+                                           int m, int t0, int lane) {
+  constexpr int G = GATED ? 2 : 1;
+  constexpr int V = G * S * TG;
+  constexpr int JN = ilog2(LPR);
+  constexpr int RPS = 64 / LPR;
+  reduce_scatter<0, V, JN>(v, lane);
+
+  constexpr int C = V >= LPR ? V / LPR : 1;
+  const int lb = lane_bits<V, JN>(lane);
+  const bool own = lane_owns<V, JN>(lane);
+  const int sub = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    // the gate/up index bit is the most significant, taken from lane bit 3:
+    // the up value of a gate lane sits in lane ^ 8 (row rotate by 8)
+    float up = 0.f;
+    if constexpr (GATED)
+      up = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0x128, 0xF, 0xF, true));
+    const int idx = lb * C + i;
+    const int g = idx / (S * TG), s = (idx / TG) % S, t = idx % TG;
+    const int n = nw + s * RPS + sub;
+    if (!own || g != 0 || t0 + t >= m || n >= N) continue;
+    float val = v[i];
+    if (!shared && a.bias0) val += bf16_to_f32(a.bias0[(size_t)e * N + n]);
+    if constexpr (GATED) {
+      if (!shared && a.bias1) up += bf16_to_f32(a.bias1[(size_t)e * N + n]);
+      val = expert_act(shared ? 1 : a.act, val, up, a.alpha, a.limit);
+    }
+    a.out[(size_t)(m0 + t0 + t) * a.ldo + n] = f32_to_bf16(val);
+  }
+}
+
+// Token rows t0 .. t0+TG-1 of the expert (slots >= m repeat slot m - 1; they
+// contribute zeros and are not stored).
+template <int TG>
+__device__ __forceinline__ void token_rows(const DecodeArgs& a, int m0, int m, int t0, const uint16_t* (&X)[TG]) {
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const int slot = min(t0 + t, m - 1);
+    const int brow = a.row_token ? a.row_token[m0 + slot] : m0 + slot;
+    X[t] = a.a + (size_t)brow * a.lda;
+  }
+}
+
+// One pass over the wavefront's R bf16 weight rows for token slots
+// t0 .. t0+TG-1 of the expert.
+template <bool GATED, int TG, int R>
 __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool shared, int N, int K, int nw, int m0,
                                             int m, int t0, int lane) {
   constexpr int G = GATED ? 2 : 1;
@@ -207,73 +261,13 @@ __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool sha
     if constexpr (GATED) Wr[1][r] = Wb1 + row;
   }
   const uint16_t* X[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    const int slot = min(t0 + t, m - 1);
-    const int brow = a.row_token ? a.row_token[m0 + slot] : m0 + slot;
-    X[t] = a.a + (size_t)brow * a.lda;
-  }
+  token_rows<TG>(a, m0, m, t0, X);
 
   float v[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) v[i] = 0.f;
 
-  if constexpr (FP4) {
-    // codes and scales of the wavefront's rows (rows past N read row N - 1)
-    const uint8_t* Cr[G][R];
-    const uint8_t* Sr[G][R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const size_t row = (size_t)e * N + min(nw + r, N - 1);
-      Cr[0][r] = a.c0 + row * (K / 2);
-      Sr[0][r] = a.s0 + row * (K / 32);
-      if constexpr (GATED) {
-        Cr[1][r] = a.c1 + row * (K / 2);
-        Sr[1][r] = a.s1 + row * (K / 32);
-      }
-    }
-    constexpr int kChunk4 = 2048;  // elements of a row per wavefront load (64 lanes x 32)
-    const int chunks = (K + kChunk4 - 1) / kChunk4;
-    for (int c = 0; c < chunks; ++c) {
-      const int k = c * kChunk4 + 32 * lane;
-      if (k < K) {  // K % 32 == 0: a lane's 32 elements are all in range or all out
-        u32x4_t wc[G][R];
-        float sf[G][R];
-        bool nan[G][R];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            wc[g][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Cr[g][r] + k / 2));
-            const uint32_t sb = Sr[g][r][k / 32];
-            sf[g][r] = e8m0_factor(sb);
-            nan[g][r] = sb == 255u;
-          }
-        // the four 8-element pieces, unrolled: each piece's code word is then
-        // picked at compile time (a rolled loop selects it with three
-        // v_cndmask per word and row), at the price of every token's 32
-        // elements held at once
-#pragma unroll MOE_DECODE_FP4_UNROLL
-        for (int q = 0; q < 4; ++q) {
-          u32x4_t x[TG];
-#pragma unroll
-          for (int t = 0; t < TG; ++t) x[t] = (t0 + t < m) ? ld16(X[t] + k + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              const uint32_t word = q == 0 ? wc[g][r].x : q == 1 ? wc[g][r].y : q == 2 ? wc[g][r].z : wc[g][r].w;
-              u32x4_t w8 = fp4_word_bf16(word, sf[g][r]);
-              // a NaN block: one NaN weight makes the row's sums NaN, as the oracle's would be
-              if (q == 0 && nan[g][r]) w8.x = 0x7fc07fc0u;
-#pragma unroll
-              for (int t = 0; t < TG; ++t) v[(g * R + r) * TG + t] = dot8(w8, x[t], v[(g * R + r) * TG + t]);
-            }
-        }
-      }
-    }
-  }
-  const int chunks = FP4 ? 0 : (K + kChunk - 1) / kChunk;
+  const int chunks = (K + kChunk - 1) / kChunk;
   for (int c = 0; c < chunks; ++c) {
     const int k = c * kChunk + 8 * lane;
     if (k < K) {  // K % 8 == 0: a lane's 8 elements are all in range or all out
@@ -292,46 +286,118 @@ __device__ __forceinline__ void decode_pass(const DecodeArgs& a, int e, bool sha
           for (int t = 0; t < TG; ++t) v[(g * R + r) * TG + t] = dot8(w[g][r], x[t], v[(g * R + r) * TG + t]);
     }
   }
+  store_pass<GATED, TG, R, 64>(a, v, e, shared, N, nw, m0, m, t0, lane);
+}
 
-  reduce_scatter<0, V>(v, lane);
+// One pass over the wavefront's R MXFP4 weight rows.  A row of K elements is
+// KB = K / 32 blocks, each 16 bytes of codes under one scale byte.  LPR lanes
+// share a row: lane l takes blocks l % LPR + LPR j (j = 0, 1, ...) of row
+// l / LPR of each slot of RPS = 64 / LPR consecutive rows.  A 64-lane row
+// step wastes the lanes past KB in its last step (K = 2880: 90 blocks in two
+// steps of 64, 26 lanes busy in the second); 32 lanes per row cover two rows
+// in three steps of 32 blocks each, i.e. 1.5 full-wavefront steps per row
+// instead of 2, and a load instruction covers 512 contiguous bytes of each of
+// the two rows.  Measured on the 8-token layer (K = 2880): gate|up 57.0 ->
+// 50.4 us, and with 8 down rows per wavefront the step 0.1003 -> 0.0915 ms.
+template <bool GATED, int TG, int R, int LPR>
+__device__ __forceinline__ void decode_pass_fp4(const DecodeArgs& a, int e, bool shared, int N, int K, int nw, int m0,
+                                                int m, int t0, int lane) {
+  constexpr int G = GATED ? 2 : 1;
+  constexpr int RPS = 64 / LPR;
+  static_assert(R % RPS == 0, "rows per wavefront must fill its row slots");
+  constexpr int S = R / RPS;
+  constexpr int V = G * S * TG;  // value index ((g S + s) TG + t)
+  static_assert((V & (V - 1)) == 0, "value count must be a power of two");
 
-  constexpr int C = V >= 64 ? V / 64 : 1;
-  const int lb = lane_bits<V>(lane);
-  const bool own = lane_owns<V>(lane);
+  const uint16_t* X[TG];
+  token_rows<TG>(a, m0, m, t0, X);
+  const int sub = lane / LPR, pos = lane % LPR;
+  // codes and scales of the lane's row in each slot (rows past N read row N - 1)
+  const uint8_t* Cr[G][S];
+  const uint8_t* Sr[G][S];
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    // the gate/up index bit is the most significant, taken from lane bit 3:
-    // the up value of a gate lane sits in lane ^ 8 (row rotate by 8)
-    float up = 0.f;
-    if constexpr (GATED)
-      up = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0x128, 0xF, 0xF, true));
-    const int idx = lb * C + i;
-    const int g = idx / (R * TG), r = (idx / TG) % R, t = idx % TG;
-    const int n = nw + r;
-    if (!own || g != 0 || t0 + t >= m || n >= N) continue;
-    float val = v[i];
-    if (!shared && a.bias0) val += bf16_to_f32(a.bias0[(size_t)e * N + n]);
+  for (int s = 0; s < S; ++s) {
+    const size_t row = (size_t)e * N + min(nw + s * RPS + sub, N - 1);
+    Cr[0][s] = a.c0 + row * (K / 2);
+    Sr[0][s] = a.s0 + row * (K / 32);
     if constexpr (GATED) {
-      if (!shared && a.bias1) up += bf16_to_f32(a.bias1[(size_t)e * N + n]);
-      val = expert_act(shared ? 1 : a.act, val, up, a.alpha, a.limit);
+      Cr[1][s] = a.c1 + row * (K / 2);
+      Sr[1][s] = a.s1 + row * (K / 32);
     }
-    a.out[(size_t)(m0 + t0 + t) * a.ldo + n] = f32_to_bf16(val);
   }
+
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = 0.f;
+
+  const int KB = K / 32;
+  const int steps = (KB + LPR - 1) / LPR;
+  for (int j = 0; j < steps; ++j) {
+    const int kb = pos + LPR * j;
+    if (kb < KB) {
+      const int k = 32 * kb;
+      u32x4_t wc[G][S];
+      float sf[G][S];
+      bool nan[G][S];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          wc[g][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Cr[g][s] + 16 * kb));
+          const uint32_t sb = Sr[g][s][kb];
+          sf[g][s] = e8m0_factor(sb);
+          nan[g][s] = sb == 255u;
+        }
+      // the four 8-element pieces, unrolled: each piece's code word is then
+      // picked at compile time (a rolled loop selects it with three
+      // v_cndmask per word and row), at the price of every token's 32
+      // elements held at once
+#pragma unroll MOE_DECODE_FP4_UNROLL
+      for (int q = 0; q < 4; ++q) {
+        u32x4_t x[TG];
+#pragma unroll
+        for (int t = 0; t < TG; ++t) x[t] = (t0 + t < m) ? ld16(X[t] + k + 8 * q) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            const uint32_t word = q == 0 ? wc[g][s].x : q == 1 ? wc[g][s].y : q == 2 ? wc[g][s].z : wc[g][s].w;
+            u32x4_t w8 = fp4_word_bf16(word, sf[g][s]);
+            // a NaN block: one NaN weight makes the row's sums NaN, as the oracle's would be
+            if (q == 0 && nan[g][s]) w8.x = 0x7fc07fc0u;
+#pragma unroll
+            for (int t = 0; t < TG; ++t) v[(g * S + s) * TG + t] = dot8(w8, x[t], v[(g * S + s) * TG + t]);
+          }
+      }
+    }
+  }
+  store_pass<GATED, TG, S, LPR>(a, v, e, shared, N, nw, m0, m, t0, lane);
 }
 
 // MXFP4 shapes.  The conversions and dot products of 4.25-bit weights cost
 // more issue slots per byte than the loads, so the shapes minimise vector
 // instructions per weight: a pass takes at most 2 tokens (the widest token
-// group sets the register budget of the whole kernel; with the pieces
-// unrolled, 2 keeps it at three wavefronts per SIMD, and an expert with more
-// rows makes more passes over its weights), and a wavefront takes 4 rows of
-// each tensor (gate and up, or down).  Measured on the 8-token layer against
-// 4 tokens, rolled pieces and 8 down rows: gate|up 69.2 -> 57.7 us.
+// group sets the register budget of the whole kernel, and an expert with more
+// rows makes more passes over its weights), a wavefront takes 4 rows of gate
+// and up or 8 rows of down, and the lanes per row are chosen per launch from
+// K.  Measured on the 8-token layer (64 lanes per row then) against 4 tokens,
+// rolled pieces and 8 down rows: gate|up 69.2 -> 57.7 us.  With 32 lanes per
+// row: 8 gate|up rows 54.3 us against 50.4 for 4; 16 down rows 0.0947 ms per
+// step against 0.0915 for 8; passes of 4 tokens 51.4 us.
 #ifndef MOE_DECODE_FP4_RG
 #define MOE_DECODE_FP4_RG 4
 #endif
 #ifndef MOE_DECODE_FP4_RD
-#define MOE_DECODE_FP4_RD 4
+#define MOE_DECODE_FP4_RD 8
+#endif
+// Narrowest row share considered.  16 lanes per row (a load covering 256
+// bytes of each of 4 rows) measured 18% slower on the gate|up rows of 2880
+// than 32 lanes at the same lane count per row, so 16 is not taken by default.
+#ifndef MOE_DECODE_FP4_MIN_LPR
+#define MOE_DECODE_FP4_MIN_LPR 32
+#endif
+#ifndef MOE_DECODE_FP4_TIE_NARROW
+#define MOE_DECODE_FP4_TIE_NARROW 0
 #endif
 constexpr int kFp4RowsGated = MOE_DECODE_FP4_RG, kFp4RowsDown = MOE_DECODE_FP4_RD, kFp4MaxTg = MOE_DECODE_FP4_TG;
 template <bool GATED, bool FP4> constexpr int rows_per_wave() {
@@ -339,7 +405,15 @@ template <bool GATED, bool FP4> constexpr int rows_per_wave() {
 }
 template <bool GATED, bool FP4> constexpr int max_token_group() { return FP4 ? kFp4MaxTg : kMaxTg; }
 
-template <bool GATED, bool FP4>
+template <bool GATED, int TG, bool FP4, int R, int LPR>
+__device__ __forceinline__ void run_pass(const DecodeArgs& a, int e, bool shared, int N, int K, int nw, int m0, int m,
+                                         int t0, int lane) {
+  if constexpr (FP4) decode_pass_fp4<GATED, TG, R, LPR>(a, e, shared, N, K, nw, m0, m, t0, lane);
+  else decode_pass<GATED, TG, R>(a, e, shared, N, K, nw, m0, m, t0, lane);
+}
+
+// LPR: lanes per MXFP4 row (64 for bf16 weights)
+template <bool GATED, bool FP4, int LPR = 64>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int RW = rows_per_wave<GATED, FP4>();
   const int e = blockIdx.y;
@@ -357,17 +431,47 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // token group: the smallest power of two covering m, up to MT per pass
   constexpr int MT = max_token_group<GATED, FP4>();
   if (m <= 1) {
-    decode_pass<GATED, 1, FP4, RW>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    run_pass<GATED, 1, FP4, RW, LPR>(a, e, shared, N, K, nw, m0, m, 0, lane);
   } else if (m <= 2) {
-    decode_pass<GATED, 2, FP4, RW>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    run_pass<GATED, 2, FP4, RW, LPR>(a, e, shared, N, K, nw, m0, m, 0, lane);
   } else if (m <= 4 || MT < 8) {
     for (int t0 = 0; t0 < m; t0 += 4 < MT ? 4 : MT)
-      decode_pass<GATED, (4 < MT ? 4 : MT), FP4, RW>(a, e, shared, N, K, nw, m0, m, t0, lane);
+      run_pass<GATED, (4 < MT ? 4 : MT), FP4, RW, LPR>(a, e, shared, N, K, nw, m0, m, t0, lane);
   } else if (m <= 8 || MT < 16) {
-    for (int t0 = 0; t0 < m; t0 += 8) decode_pass<GATED, 8, FP4, RW>(a, e, shared, N, K, nw, m0, m, t0, lane);
+    for (int t0 = 0; t0 < m; t0 += 8) run_pass<GATED, 8, FP4, RW, LPR>(a, e, shared, N, K, nw, m0, m, t0, lane);
   } else {
-    decode_pass<GATED, (MT < 16 ? 8 : 16), FP4, RW>(a, e, shared, N, K, nw, m0, m, 0, lane);
+    run_pass<GATED, (MT < 16 ? 8 : 16), FP4, RW, LPR>(a, e, shared, N, K, nw, m0, m, 0, lane);
   }
+}
+
+// Lanes per MXFP4 row of K elements: the choice with the fewest lane-blocks
+// per row, ceil(KB / LPR) LPR with KB = K / 32, the widest on a tie (longer
+// contiguous loads, fewer token loads).  K = 2880: 32; K = 2048: 64.
+int fp4_lanes_per_row(int K) {
+  const int kb = K / 32;
+  int best = 64, cost = (kb + 63) / 64 * 64;
+  for (int lpr = 32; lpr >= MOE_DECODE_FP4_MIN_LPR; lpr /= 2) {
+    const int c = (kb + lpr - 1) / lpr * lpr;
+    if (c < cost || (MOE_DECODE_FP4_TIE_NARROW && c == cost)) {
+      best = lpr;
+      cost = c;
+    }
+  }
+  return best;
+}
+
+template <bool GATED>
+void launch_fp4(const DecodeArgs& d, int rows, int K, int n_experts, hipStream_t s) {
+  constexpr int rb = rows_per_wave<GATED, true>() * kWaves;
+  const dim3 grid((rows + rb - 1) / rb, n_experts);
+  const int lpr = fp4_lanes_per_row(K);
+  if constexpr (MOE_DECODE_FP4_MIN_LPR <= 16) {
+    if (lpr == 16) return (void)decode_kernel<GATED, true, 16><<<grid, 64 * kWaves, 0, s>>>(d);
+  }
+  if constexpr (MOE_DECODE_FP4_MIN_LPR <= 32) {
+    if (lpr == 32) return (void)decode_kernel<GATED, true, 32><<<grid, 64 * kWaves, 0, s>>>(d);
+  }
+  decode_kernel<GATED, true, 64><<<grid, 64 * kWaves, 0, s>>>(d);
 }
 
 DecodeArgs base_args(const Layer& L, const Work& W) {
@@ -398,8 +502,7 @@ hipError_t launch_gate_up_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.out = static_cast<uint16_t*>(W.h);
   d.ldo = L.F_max();
   if (L.wfmt == WF_MXFP4) {
-    constexpr int rb = rows_per_wave<true, true>() * kWaves;
-    decode_kernel<true, true><<<dim3((L.F_max() + rb - 1) / rb, L.n_experts_all()), 64 * kWaves, 0, s>>>(d);
+    launch_fp4<true>(d, L.F_max(), L.d, L.n_experts_all(), s);
   } else {
     const dim3 grid((L.F_max() + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
     decode_kernel<true, false><<<grid, 64 * kWaves, 0, s>>>(d);
@@ -420,8 +523,7 @@ hipError_t launch_down_decode(const Layer& L, const Work& W, hipStream_t s) {
   d.out = static_cast<uint16_t*>(W.y);
   d.ldo = L.d;
   if (L.wfmt == WF_MXFP4) {
-    constexpr int rb = rows_per_wave<false, true>() * kWaves;
-    decode_kernel<false, true><<<dim3((L.d + rb - 1) / rb, L.n_experts_all()), 64 * kWaves, 0, s>>>(d);
+    launch_fp4<false>(d, L.d, L.F, L.n_experts_all(), s);
   } else {
     const dim3 grid((L.d + kRowsPerBlock - 1) / kRowsPerBlock, L.n_experts_all());
     decode_kernel<false, false><<<grid, 64 * kWaves, 0, s>>>(d);

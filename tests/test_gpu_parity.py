@@ -494,8 +494,12 @@ MXD_CASES = [
     W.GPTOSS_MXFP4_DECODE.scaled(T=16, d=512, d_ff=256, E=4, k=4, name="mxfp4_decode_T16_multi_pass"),
     # 7 tokens over 2 experts: an odd row count ends on a half-filled pass of 2
     W.GPTOSS_MXFP4_DECODE.scaled(T=7, d=320, d_ff=224, E=2, k=1, name="mxfp4_decode_T7_two_experts"),
-    # K ragged against the 2048-element chunks of a wave load, 1..5 rows per expert
+    # K = 2112 (66 blocks of 32): 32 lanes per row, the last of 3 steps with 2 lanes busy; 1..5 rows per expert
     W.GPTOSS_MXFP4_DECODE.scaled(T=5, d=2112, d_ff=160, E=6, k=3, name="mxfp4_decode_T5_ragged_k"),
+    # gate|up rows of 2048 (64 lanes per row), down rows of 3072 (96 blocks: 32 lanes per row, two rows a step)
+    W.GPTOSS_MXFP4_DECODE.scaled(T=6, d=2048, d_ff=3072, E=4, k=2, name="mxfp4_decode_lanes_64_32"),
+    # the full-size rows (32 lanes per row) with ~7 rows per expert: four passes of 2 tokens
+    W.GPTOSS_MXFP4_DECODE.scaled(T=9, E=4, k=3, name="mxfp4_decode_T9_E4"),
     W.GPTOSS_MXFP4_DECODE.scaled(T=1, d=256, d_ff=96, E=32, k=4, name="mxfp4_decode_T1"),
     # as a MoE block
     W.GPTOSS_MXFP4_DECODE.scaled(T=8, d=256, d_ff=192, E=8, k=2, block=True, name="mxfp4_decode_block"),
