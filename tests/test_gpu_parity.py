@@ -377,6 +377,8 @@ MX_CASES = [
     W.GPTOSS_MXFP4_MX8.scaled(T=70, d=64, d_ff=320, E=6, k=6, name="mx8_k_equals_E"),
     # few tokens, long K (8 stages), N ragged against the 256-column tiles
     W.GPTOSS_MXFP4_MX8.scaled(T=9, d=1024, d_ff=320, E=8, k=3, name="mx8_T9_long_k"),
+    # long K: gate|up 25 stages, down 16.5 (a half stage after 8 steady pairs)
+    W.GPTOSS_MXFP4_MX8.scaled(T=40, d=3200, d_ff=2112, E=4, k=2, name="mx8_long_k_d3200"),
     # MXFP8 (E4M3) weights: the full layer, 1.5 / 4.5 stages, a single half stage
     W.GPTOSS_MXFP8_MX8,
     W.GPTOSS_MXFP8_MX8.scaled(T=150, d=256, d_ff=192, E=8, k=2, name="mx8w_small"),
