@@ -80,6 +80,12 @@ constexpr bool kBoundaryReadsInterleaved = MOE_GEMM_BOUNDARY_READS != 0;
 // Wavefronts along N: 2 (4 wavefronts of 128 x 128, one per SIMD) or 4 (8
 // wavefronts of 128 x 64, two per SIMD).
 constexpr int kWavesN = MOE_GEMM_WAVES_N;
+// A rows past a tile's last row copy a row of zeros (1) or the tile's first
+// row (0).
+#ifndef MOE_GEMM_ZERO_ROWS
+#define MOE_GEMM_ZERO_ROWS 1
+#endif
+constexpr bool kZeroRows = MOE_GEMM_ZERO_ROWS != 0;
 
 
 
@@ -147,16 +153,19 @@ __device__ __forceinline__ void mfma_gemm_tile(const MfmaArgs& a, int e, int r0,
   // segment NW i + wv: lane l writes 16-byte slot l, i.e. row
   // SEG_ROWS (NW i + wv) + l / CPR, stored chunk l % CPR, which holds the
   // logical chunk that swz() maps there.  Rows past the expert's last row (A)
-  // or past N (B) copy a valid row instead: they only feed outputs that the
-  // epilogue drops.
+  // copy the zero row a.zrow (a_row -1), else the tile's first row; rows past
+  // N (B) copy a valid row.  They only feed outputs that the epilogue drops
+  // (zeros keep the matrix cores' operands quiet: measured 0.5% faster on the
+  // 8192-token layer).
   const int ld_sub = lane / CPR;
   const int ld_phys = lane % CPR;
   int a_row[RA];
 #pragma unroll
   for (int i = 0; i < RA; ++i) {
     const int r = SEG_ROWS * (NW * i + wv) + ld_sub;
-    const int gr = r0 + r < r_end ? r0 + r : r0;
-    a_row[i] = a.row_token ? a.row_token[gr] : gr - a.a_row0;
+    const bool dead = r0 + r >= r_end;
+    const int gr = dead ? r0 : r0 + r;
+    a_row[i] = dead && a.zrow ? -1 : a.row_token ? a.row_token[gr] : gr - a.a_row0;
   }
   int b_row[RB];
 #pragma unroll
@@ -190,7 +199,8 @@ __device__ __forceinline__ void mfma_gemm_tile(const MfmaArgs& a, int e, int r0,
   // stubs without a diagnostic.)
   auto copy_a = [&](int kt, uint16_t* As, int i) __attribute__((always_inline)) {
     const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
-    __builtin_amdgcn_global_load_lds(a.a + (size_t)a_row[i] * a.lda + k, As + (NW * i + wv) * 512, 16, 0, 0);
+    const uint16_t* row = a_row[i] >= 0 ? a.a + (size_t)a_row[i] * a.lda : a.zrow;
+    __builtin_amdgcn_global_load_lds(row + k, As + (NW * i + wv) * 512, 16, 0, 0);
   };
   auto copy_b = [&](int kt, uint16_t* Bs, int i) __attribute__((always_inline)) {
     const int k = min(kt * BK + 8 * ld_chunk_of(i), K - 8);
@@ -461,6 +471,7 @@ MfmaArgs gate_up_args(const Layer& L, const Work& W, int e_first, int e_end) {
   m.out = static_cast<uint16_t*>(W.h);
   m.ldo = L.F_max();
   m.n_tiles = (L.F_max() + 127) / 128;
+  m.zrow = kZeroRows ? static_cast<const uint16_t*>(W.zrow) : nullptr;
   return m;
 }
 
@@ -487,6 +498,7 @@ MfmaArgs down_args(const Layer& L, const Work& W, int e_first, int e_end) {
   m.out = static_cast<uint16_t*>(W.y);
   m.ldo = L.d;
   m.n_tiles = down_narrow(L) ? (L.d + 191) / 192 : (L.d + 255) / 256;
+  m.zrow = kZeroRows ? static_cast<const uint16_t*>(W.zrow) : nullptr;
   return m;
 }
 
@@ -528,6 +540,7 @@ hipError_t launch_route_shared_gate_up(const Layer& L, const Work& W, hipStream_
   const int P = L.T * L.k;
   m.row_token = nullptr;  // shared row P + t is token t
   m.a_row0 = P;
+  m.zrow = nullptr;  // the permutation writes the zero row later
   const dim3 grid(n_route + (L.T + BM - 1) / BM * m.n_tiles);
   if (L.E <= 16) route_shared_gate_up_kernel<1><<<grid, 256, 0, s>>>(ra, n_route, m, P, L.T);
   else if (L.E <= 32) route_shared_gate_up_kernel<2><<<grid, 256, 0, s>>>(ra, n_route, m, P, L.T);
@@ -539,7 +552,8 @@ hipError_t launch_route_shared_gate_up(const Layer& L, const Work& W, hipStream_
 hipError_t launch_permute_shared_down(const Layer& L, const Work& W, hipStream_t s) {
   const PermuteArgs pa = permute_args(L, W);
   const int n_perm = (L.T + kPermuteTokens - 1) / kPermuteTokens;
-  const MfmaArgs m = down_args(L, W, L.E, L.E + 1);
+  MfmaArgs m = down_args(L, W, L.E, L.E + 1);
+  m.zrow = nullptr;  // written by this launch's permutation blocks
   const int P = L.T * L.k;
   const dim3 grid(n_perm + (L.T + BM - 1) / BM * m.n_tiles);
   if (down_narrow(L)) permute_shared_down_kernel<3><<<grid, 256, 0, s>>>(pa, n_perm, m, P, L.T);

@@ -27,6 +27,8 @@ struct MfmaArgs {
   int lda;
   const int32_t* row_token;   // gate|up: token of each sorted row; down: nullptr
   int a_row0;                 // without row_token: A row of sorted row r is r - a_row0
+  const uint16_t* zrow;       // zeros (at least K of them) for the A rows past a tile's last row, or
+                              // nullptr (those rows then copy the tile's first row)
   const uint16_t* w0;         // dense [E, N, K] (down, or gate)
   const uint16_t* w1;         // dense up
   const uint8_t* c0;          // low-bit codes [E, N, K * bits / 8]; scales: MXFP4 e8m0 bytes
@@ -250,6 +252,7 @@ inline MfmaArgs base_args(const Layer& L, const Work& W) {
   m.act = L.act;
   m.alpha = L.alpha;
   m.limit = L.limit;
+  m.zrow = nullptr;
   return m;
 }
 

@@ -115,6 +115,7 @@ struct Work {
   uint8_t* xs = nullptr;           //   and e8m0 scales [T, mx_row_bytes(d) / 32]
   uint8_t* hq = nullptr;           //   h as codes [rows, mx_row_bytes(d_ff)]
   uint8_t* hs = nullptr;           //   and scales [rows, mx_row_bytes(d_ff) / 32]
+  void* zrow = nullptr;            // bf16: max(d, F_max) zeros, written by the permutation
 };
 
 // Byte size of the workspace and the layout of its buffers (ws == nullptr:

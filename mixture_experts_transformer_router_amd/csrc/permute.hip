@@ -42,6 +42,8 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(RouteArgs ra
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = ra.E, T = ra.T, k = ra.k, P = T * k;
   for (int e = tid; e < EP; e += 1024) cnt[e] = 0;
+  if (a.zrow)
+    for (int i = tid; i < a.zrow_words; i += 1024) a.zrow[i] = 0u;
   for (int i = tid; i < T * E; i += 1024) {
     const int t = i / E, e = i % E;
     float pv[kRouteSplitK];  // all slices loaded first, then added in order

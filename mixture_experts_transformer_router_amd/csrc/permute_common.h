@@ -29,6 +29,8 @@ struct PermuteArgs {
   int32_t* pos;
   int32_t* user_offsets;
   int32_t* user_sorted;
+  uint32_t* zrow;  // block 0 writes zrow_words zeros (the GEMMs' zero row), or nullptr
+  int zrow_words;
 };
 
 __device__ __forceinline__ void permute_block(const PermuteArgs& a, int b) {
@@ -41,6 +43,8 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, int b) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E;
+  if (b == 0 && a.zrow)
+    for (int i = tid; i < a.zrow_words; i += kPermuteThreads) a.zrow[i] = 0u;
 
   // Column sums of the count table, split over all threads: thread
   // (part, e) adds rows part, part + parts, ... of expert e.
@@ -199,6 +203,8 @@ inline PermuteArgs permute_args(const Layer& L, const Work& W) {
   a.tile_desc = W.tile_desc;
   a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
   a.user_offsets = L.routing.expert_offsets; a.user_sorted = L.routing.sorted_pair;
+  a.zrow = static_cast<uint32_t*>(W.zrow);
+  a.zrow_words = W.zrow ? ((L.d > L.F_max() ? L.d : L.F_max()) + 1) / 2 : 0;
   return a;
 }
 
