@@ -34,6 +34,12 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroupM = 4;               // row tiles walked together within an XCD
+// A rows past a tile's last row copy the workspace's zero row (1) or the
+// tile's first row (0).
+#ifndef MOE_MX_ZERO_ROWS
+#define MOE_MX_ZERO_ROWS 1
+#endif
+constexpr bool kMxZeroRows = MOE_MX_ZERO_ROWS != 0;
 constexpr int NJ = 4;                    // 32-column results per wavefront
 constexpr int BN = 64 * NJ;              // 256 block columns
 constexpr int BKX = 128;                 // K elements per stage
@@ -117,12 +123,15 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
   // 8 (4 i + wv) + l / 8, which holds the logical chunk swz() maps there.
   // B round i: 1024 / BRB rows of BRB bytes, slot l % BCPR of row
   // (1024 / BRB) (4 i + wv) + l / BCPR.
+  // Rows past the tile's last row copy the zero row (zoff: its byte offset
+  // from the codes, both in the workspace), else the tile's first row.
+  const uint32_t zoff = a.zrow ? (uint32_t)(reinterpret_cast<const uint8_t*>(a.zrow) - aq) : 0u;
   uint32_t a_off[RA];  // byte offset of the copied chunk in stage 0
 #pragma unroll
   for (int i = 0; i < RA; ++i) {
     const int row = 8 * (4 * i + wv) + (lane >> 3);
     const int chunk = (swz<64>(row, lane & 7) - row * 64) >> 3;
-    a_off[i] = (uint32_t)a_token(row) * lda + 16u * (uint32_t)chunk;
+    a_off[i] = (r0 + row >= r_end && a.zrow ? zoff : (uint32_t)a_token(row) * lda) + 16u * (uint32_t)chunk;
   }
   const uint32_t sa_off = (uint32_t)a_token(tid) * (lda / 32);  // A scales: thread tid copies row tid
   const int kb = K * WB / 8;  // code bytes of a weight row
@@ -347,12 +356,21 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(MfmaArgs a) {
   store_tile<GATED, NJ>(a, acc, e, false, N, n0, r0, r_end, wm, wn, lane);
 }
 
+// The zero row, if its byte offset from the codes fits the kernel's 32-bit
+// row offsets (the codes' own offsets are checked below 2^32 by the library).
+const uint16_t* zero_row_for(const Work& W, const uint8_t* codes) {
+  if (!kMxZeroRows || !W.zrow) return nullptr;
+  const uintptr_t z = reinterpret_cast<uintptr_t>(W.zrow), c = reinterpret_cast<uintptr_t>(codes);
+  return z > c && z - c < (1ull << 32) - (1u << 16) ? static_cast<const uint16_t*>(W.zrow) : nullptr;
+}
+
 }  // namespace
 
 hipError_t launch_gate_up_mx(const Layer& L, const Work& W, hipStream_t s) {
   MfmaArgs m = base_args(L, W);
   m.a = reinterpret_cast<const uint16_t*>(W.xq);
   m.as = W.xs;
+  m.zrow = zero_row_for(W, W.xq);
   m.lda = mx_row_bytes(L.d);
   m.row_token = W.row_token;
   m.c0 = L.wg_codes; m.s0 = L.wg_scales;
@@ -373,6 +391,7 @@ hipError_t launch_down_mx(const Layer& L, const Work& W, hipStream_t s) {
   MfmaArgs m = base_args(L, W);
   m.a = reinterpret_cast<const uint16_t*>(W.hq);
   m.as = W.hs;
+  m.zrow = zero_row_for(W, W.hq);
   m.lda = mx_row_bytes(L.F);
   m.row_token = nullptr;
   m.c0 = L.wd_codes; m.s0 = L.wd_scales;

@@ -295,7 +295,7 @@ size_t carve_workspace(const Layer& L, void* ws, Work* W) {
   W->xs = static_cast<uint8_t*>(take((size_t)L.T * xrow / 32));
   W->hq = static_cast<uint8_t*>(take(rows * hrow));
   W->hs = static_cast<uint8_t*>(take(rows * hrow / 32));
-  W->zrow = L.dt == MOE_BF16 ? take((size_t)(L.d > L.F_max() ? L.d : L.F_max()) * 2 + 2) : nullptr;
+  W->zrow = L.dt == MOE_BF16 ? take(zero_row_bytes(L)) : nullptr;
   return off;
 }
 

@@ -115,8 +115,15 @@ struct Work {
   uint8_t* xs = nullptr;           //   and e8m0 scales [T, mx_row_bytes(d) / 32]
   uint8_t* hq = nullptr;           //   h as codes [rows, mx_row_bytes(d_ff)]
   uint8_t* hs = nullptr;           //   and scales [rows, mx_row_bytes(d_ff) / 32]
-  void* zrow = nullptr;            // bf16: max(d, F_max) zeros, written by the permutation
+  void* zrow = nullptr;            // bf16: zero_row_bytes() of zeros, written by the permutation
 };
+
+// Bytes of the zero row: at least a bf16 row of max(d, F_max) elements and an
+// MXFP8 code row (mx_row_bytes) of either.
+inline size_t zero_row_bytes(const Layer& L) {
+  const int m = L.d > L.F_max() ? L.d : L.F_max();
+  return 2 * (size_t)m + 256;
+}
 
 // Byte size of the workspace and the layout of its buffers (ws == nullptr:
 // size only).  Returns (size_t)-1 for sizes it cannot represent.

@@ -204,7 +204,7 @@ inline PermuteArgs permute_args(const Layer& L, const Work& W) {
   a.sorted_pair = W.sorted_pair; a.row_token = W.row_token; a.pos = W.pos;
   a.user_offsets = L.routing.expert_offsets; a.user_sorted = L.routing.sorted_pair;
   a.zrow = static_cast<uint32_t*>(W.zrow);
-  a.zrow_words = W.zrow ? ((L.d > L.F_max() ? L.d : L.F_max()) + 1) / 2 : 0;
+  a.zrow_words = W.zrow ? (int)(zero_row_bytes(L) / 4) : 0;
   return a;
 }
 
