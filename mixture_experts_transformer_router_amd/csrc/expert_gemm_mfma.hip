@@ -13,8 +13,9 @@
 // rows: a few tens of megabytes, mostly cache hits) has NS buffers and runs
 // NS - 1 tiles ahead of the multiply; the B operand (expert weights, streamed
 // from HBM) may have NSB = NS + 1 buffers to run one tile further ahead.  On
-// MI355X the copies are bound by the L2 requests a CU keeps in flight, not by
-// how far ahead they are issued, so the default is NSB = NS = 2.
+// MI355X the copies are bound by the L2 requests a CU keeps in flight more
+// than by how far ahead they are issued: NSB = NS = 2 by default, NSB = 3 for
+// launches whose experts average two or more row tiles (1% faster there).
 // 4 wavefronts, each owning a 128 x (32 NJ) sub-tile as 4 x NJ results of
 // v_mfma_f32_32x32x16_bf16 (fp32 accumulators).  An LDS row holds BK bf16;
 // its 16-byte chunks are stored XOR-swizzled by the row's position within a
@@ -502,10 +503,21 @@ MfmaArgs down_args(const Layer& L, const Work& W, int e_first, int e_end) {
   return m;
 }
 
+// Weight copies a tile further ahead (a third LDS stage for B, all 160 KB of
+// LDS) where the routed experts average at least two 256-row tiles, so
+// that an expert's weight panels serve several row tiles: on the 8192-token
+// layer (32 experts, 1024 rows each on average) gate|up 1119-1126 against
+// 1134-1139 us; on GLM-sized layers (192 rows per expert, one row tile each)
+// it measured slower (0.476-0.487 against 0.473-0.477 ms per step).
+bool deep_weight_stages(const Layer& L, int e_first, int e_end) {
+  return kStagesB == 2 && e_first < L.E && e_end >= L.E && (long long)L.T * L.k >= 2LL * BM * L.E;
+}
+
 hipError_t gate_up_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, int e_end) {
   const MfmaArgs m = gate_up_args(L, W, e_first, e_end);
   const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
   if (kWavesN == 4) mfma_gemm_kernel<true, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
+  else if (deep_weight_stages(L, e_first, e_end)) mfma_gemm_kernel<true, 4, kBK, kStages, 3, 2><<<grid, 256, 0, s>>>(m);
   else mfma_gemm_kernel<true, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   return hipGetLastError();
 }
@@ -515,6 +527,7 @@ hipError_t down_mfma(const Layer& L, const Work& W, hipStream_t s, int e_first, 
   const dim3 grid(grid_for(max_row_tiles(L, e_first, e_end) * m.n_tiles));
   if (down_narrow(L)) mfma_gemm_kernel<false, 3, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   else if (kWavesN == 4) mfma_gemm_kernel<false, 2, kBK, kStages, kStagesB, 4><<<grid, 512, 0, s>>>(m);
+  else if (deep_weight_stages(L, e_first, e_end)) mfma_gemm_kernel<false, 4, kBK, kStages, 3, 2><<<grid, 256, 0, s>>>(m);
   else mfma_gemm_kernel<false, 4, kBK, kStages, kStagesB, 2><<<grid, 256, 0, s>>>(m);
   return hipGetLastError();
 }

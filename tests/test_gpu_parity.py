@@ -68,6 +68,11 @@ SMALL = [
     # grouped-GEMM path with K ragged against the 64-wide stages and many K
     # tiles (steady, unrolled and tail tiles): d = 1000, d_ff = 712
     W.GPTOSS_PREFILL.scaled(T=300, d=1000, d_ff=712, E=8, k=2, name="prefill_ragged_k"),
+    # experts averaging two or more row tiles take the third weight stage:
+    # steady, unrolled and tail K tiles; and K of one or two tiles (fewer
+    # tiles than stages)
+    W.GPTOSS_PREFILL.scaled(T=1100, d=1000, d_ff=712, E=4, k=2, name="prefill_deep_stages_ragged_k"),
+    W.GPTOSS_PREFILL.scaled(T=1100, d=64, d_ff=96, E=4, k=2, name="prefill_deep_stages_short_k"),
     W.GPTOSS_MXFP4.scaled(T=150, d=256, d_ff=160, E=8, k=2, name="mxfp4_small"),
     W.TINY_F32.scaled(T=300, d=96, d_ff=80, E=16, k=3, name="f32_T300"),
     W.GLM4_MOE_LITE.scaled(T=300, d=256, d_ff=192, E=64, k=6, d_ff_shared=128, name="glm_small"),
